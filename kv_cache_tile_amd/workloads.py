@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs shaped like the workloads the pages quantize.
+
+The pages evaluate on Llama-3.1-8B-Instruct weights and KV caches and on the
+LTX-2-19B DiT (gist.science explainer of HyperQuant, "Experimental
+Results"); neither the weights nor the data are available, so these seeded
+tensors stand in for them, with the shapes and value distributions of the
+five benchmark configurations.  This module holds random-number generation
+only — none of the codec's arithmetic — so that both the HIP path and the CPU
+oracle are fed from it.
+
+All generators draw in fp64 from numpy's PCG64 (SeedSequence(key)), round to
+fp32, and (for bf16 tensors) round to bf16 by round-to-nearest-even.  The
+largest tensors (KV cache, DiT stack) are drawn per slice so memory stays
+bounded; each slice has its own key, so any slice can be regenerated alone.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def to_bf16(a: np.ndarray) -> torch.Tensor:
+    """fp32/fp64 numpy -> torch bfloat16 (RNE)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """torch bfloat16 tensor (any device) -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def student_t_outlier_cols(rows: int, cols: int, key: int, nu: float = 4.0, n_out: int = 8,
+                           scale: float = 20.0) -> np.ndarray:
+    """Weight matrix, i.i.d. standard Student-t(nu) entries, n_out random columns
+    scaled by `scale` (column set drawn before the values).  fp32."""
+    rng = _rng(key)
+    out_cols = rng.choice(cols, n_out, replace=False)
+    w = rng.standard_t(nu, size=(rows, cols))
+    w[:, out_cols] *= scale
+    return w.astype(np.float32)
+
+
+def gaussian_outlier_channels(rows: int, cols: int, key: int, std: float = 0.02,
+                              frac: float = 0.01, scale: float = 10.0) -> np.ndarray:
+    """Llama-style projection weight: N(0, std^2) entries with round(frac*cols)
+    input channels (columns) scaled by `scale`.  fp32."""
+    rng = _rng(key)
+    k = int(round(frac * cols))
+    out_cols = rng.choice(cols, k, replace=False)
+    w = std * rng.standard_normal((rows, cols))
+    w[:, out_cols] *= scale
+    return w.astype(np.float32)
+
+
+def kv_cache(batch: int, heads: int, seq: int, head_dim: int, key: int, which: str) -> np.ndarray:
+    """KV cache [B, H, S, D]: V ~ N(0,1); K ~ N(0,1) * scale[h, d] with a
+    per-channel outlier scale ~ LogNormal(0, 1).  Drawn per batch entry.  fp32."""
+    sub = 0 if which == "K" else 1
+    out = np.empty((batch, heads, seq, head_dim), np.float32)
+    scale = None
+    if which == "K":
+        scale = _rng(key, 0, 99).lognormal(0.0, 1.0, size=(heads, head_dim))
+    for b in range(batch):
+        v = _rng(key, sub, b).standard_normal((heads, seq, head_dim))
+        if scale is not None:
+            v *= scale[:, None, :]
+        out[b] = v
+    return out
+
+
+def dit_layer(rows: int, cols: int, key: int, layer: int, std: float = 0.02,
+              p_out: float = 0.005, nu: float = 3.0) -> np.ndarray:
+    """One DiT linear weight: N(0, std^2) entries, each replaced with
+    probability p_out by a standard (unit-scale) Student-t(nu) draw.  fp32."""
+    rng = _rng(key, layer)
+    w = std * rng.standard_normal((rows, cols))
+    mask = rng.random((rows, cols)) < p_out
+    w[mask] = rng.standard_t(nu, size=int(mask.sum()))
+    return w.astype(np.float32)
+
+
+def gaussian(rows: int, cols: int, key: int) -> np.ndarray:
+    return _rng(key).standard_normal((rows, cols)).astype(np.float32)
+
+
+# The five benchmark configurations (0-indexed; configuration i uses key/seed i).
+CONFIGS = {
+    0: dict(name="weight-1024x1024-f32-studentt", rows=1024, cols=1024, dtype="f32", tile=128,
+            lattices=["E8"], bps=[4.0], seed=0),
+    1: dict(name="llama7b-proj-4096x4096-bf16", rows=4096, cols=4096, dtype="bf16", tile=128,
+            lattices=["E8"], bps=[4.0], seed=1),
+    2: dict(name="llama-mlp-11008x4096-bf16", rows=11008, cols=4096, dtype="bf16", tile=128,
+            lattices=["Z", "A2", "D4", "E8"], bps=[3.0, 4.0, 5.0], seed=2),
+    3: dict(name="kv-cache-8x32x8192x128-bf16", batch=8, heads=32, seq=8192, head_dim=128,
+            dtype="bf16", tile=128, lattices=["E8"], bps=[2.0], seed=3, dither=1),
+    4: dict(name="dit-stack-48x4096x16384-bf16", layers=48, rows=4096, cols=16384, dtype="bf16",
+            tile=256, lattices=["E8"], bps=[4.0], seed=4),
+}
+
+
+def config_tensor(cfg: int, layer: int = 0, which: str = "K") -> np.ndarray:
+    """fp32 numpy array of configuration `cfg` (layer of the DiT stack; K or V of
+    the KV cache).  bf16 configurations are rounded by the caller (to_bf16)."""
+    c = CONFIGS[cfg]
+    if cfg == 0:
+        return student_t_outlier_cols(c["rows"], c["cols"], key=0)
+    if cfg in (1, 2):
+        return gaussian_outlier_channels(c["rows"], c["cols"], key=cfg)
+    if cfg == 3:
+        return kv_cache(c["batch"], c["heads"], c["seq"], c["head_dim"], key=3, which=which)
+    if cfg == 4:
+        return dit_layer(c["rows"], c["cols"], key=4, layer=layer)
+    raise KeyError(cfg)
+
+
+def codec_seed(cfg: int, layer: int = 0, which: str = "K") -> int:
+    """Codec seed: the config's seed; per DiT layer (4 << 32) | layer; V of the
+    KV cache 3 + 2^32 (a different per-layer sign diagonal and dither)."""
+    if cfg == 4:
+        return (4 << 32) | layer
+    if cfg == 3:
+        return 3 if which == "K" else 3 + (1 << 32)
+    return cfg

@@ -1,0 +1,629 @@
+/*
+ * hq_oracle.c — plain, slow, single-threaded CPU oracle of the HyperQuant
+ * encode/decode path.  TEST INFRASTRUCTURE ONLY (see hq_oracle.h).
+ *
+ * Every floating-point step is one IEEE binary32 operation, round to
+ * nearest even, written out one at a time; the file must be compiled with
+ * -ffp-contract=off and without fast-math so that the compiler neither
+ * fuses nor reorders them.  No SIMD, no threads, no lookup tables.
+ *
+ * Citations name the source page and its section:
+ *   [Abs]  paperdance.org card of the paper, English abstract.
+ *   [M1]   gist.science explainer (English), "Methodology: The HyperQuant
+ *          Pipeline", 1. Per-Tile Randomized Hadamard Transform.
+ *   [M2]   same section, 2. Lattice Quantization.
+ *   [M3]   same section, 3. Bit-Stripping and Rice Coding.
+ *   [M4]   same section, 4. Bias Correction for KV Cache.
+ * Where the pages leave a step open the reading taken is stated at the step.
+ */
+#include "hq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Counter-based generator: the "pcg" hash of Jarzynski & Olano, "Hash      */
+/* Functions for GPU Rendering", JCGT 9(3), 2020 — one LCG step of PCG      */
+/* followed by PCG's RXS-M-XS output permutation (O'Neill 2014).            */
+/* The pages name no generator; this one is a bijection on 32-bit words and */
+/* needs no state, so encoder and decoder regenerate the same numbers.      */
+/* ------------------------------------------------------------------------ */
+uint32_t hqo_pcg_hash(uint32_t v)
+{
+    uint32_t state = v * 747796405u + 2891336453u;
+    uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+    return (word >> 22u) ^ word;
+}
+
+#define DOMAIN_SIGN   0x5349474Eu   /* "SIGN" */
+#define DOMAIN_DITHER 0x44495448u   /* "DITH" */
+
+uint32_t hqo_key(uint64_t seed, uint32_t domain)
+{
+    uint32_t lo = (uint32_t)(seed & 0xFFFFFFFFu);
+    uint32_t hi = (uint32_t)(seed >> 32);
+    return hqo_pcg_hash(hqo_pcg_hash(lo ^ domain) ^ hi);
+}
+
+/* [M1]: D is a random sign diagonal.  Reading: one D per call (per layer for
+ * the KV cache, [M4] "per-layer rotation ... +-1 sign diagonal"), entry i
+ * negative iff the top bit of hash(key + i) is set. */
+uint32_t hqo_sign_bit(uint64_t seed, uint32_t i)
+{
+    return hqo_pcg_hash(hqo_key(seed, DOMAIN_SIGN) + i) >> 31;
+}
+
+/* [M4]: the dither is fresh per vector; coordinate g of the call (row-major
+ * flat index) draws 24 uniform bits. */
+uint32_t hqo_dither_bits(uint64_t seed, uint32_t g)
+{
+    return hqo_pcg_hash(hqo_key(seed, DOMAIN_DITHER) + g) >> 8;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalar helpers                                                           */
+/* ------------------------------------------------------------------------ */
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 round-to-nearest-even of a finite fp32 value, returned as bits */
+static uint16_t bf16_rne(float f)
+{
+    uint32_t u = f32_to_bits(f);
+    u = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+static float bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+static uint32_t log2u(uint32_t n) { uint32_t l = 0; while ((1u << l) < n) l++; return l; }
+
+static float inv_sqrt_n(uint32_t n) { return (float)(1.0 / sqrt((double)n)); }
+static float sqrt3_f(void) { return (float)sqrt(3.0); }
+static float inv_sqrt3_f(void) { return (float)(1.0 / sqrt(3.0)); }
+
+uint32_t hqo_zigzag(int32_t v) { return v >= 0 ? 2u * (uint32_t)v : 2u * (uint32_t)(-(int64_t)v) - 1u; }
+int32_t hqo_unzigzag(uint32_t u) { return (u & 1u) ? -(int32_t)((u >> 1) + 1u) : (int32_t)(u >> 1); }
+
+/* floor(v / 2) for a 32-bit integer, without relying on signed shifts */
+static int32_t floor_half(int32_t v) { return (v - (v & 1)) / 2; }
+
+static uint32_t lattice_dim(uint32_t lat)
+{
+    switch (lat) { case HQO_Z: return 1; case HQO_A2: return 2; case HQO_D4: return 4; case HQO_E8: return 8; }
+    return 0;
+}
+/* coset bits per block: E8 = D8 u (D8 + 1/2), A2 = R u (R + (1/2, sqrt3/2)) */
+static uint32_t coset_bits_per_block(uint32_t lat) { return (lat == HQO_E8 || lat == HQO_A2) ? 1u : 0u; }
+
+/* ------------------------------------------------------------------------ */
+/* [M1] RHT_n(x) = H_n D x, scaled by 1/sqrt(n) so that it is orthogonal     */
+/* ("The transform is orthogonal").  H_n is the Sylvester-ordered           */
+/* Walsh-Hadamard matrix, H_ij = (-1)^popcount(i & j), applied by the fast   */
+/* butterfly with strides h = 1, 2, 4, ..., n/2 in that order.              */
+/* ------------------------------------------------------------------------ */
+static void fwht(float *a, uint32_t n)
+{
+    for (uint32_t h = 1; h < n; h <<= 1) {
+        for (uint32_t j = 0; j < n; j++) {
+            if (j & h) continue;
+            float lo = a[j], hi = a[j + h];
+            a[j]     = lo + hi;
+            a[j + h] = lo - hi;
+        }
+    }
+}
+
+void hqo_rht_forward(const float *x, uint32_t n, uint64_t seed, float *y)
+{
+    float a[256];
+    float s = inv_sqrt_n(n);
+    for (uint32_t i = 0; i < n; i++) a[i] = hqo_sign_bit(seed, i) ? -x[i] : x[i];
+    fwht(a, n);
+    for (uint32_t i = 0; i < n; i++) y[i] = a[i] * s;
+}
+
+/* inverse: x = D H y / sqrt(n)  (H symmetric, H H = n I, D D = I) */
+void hqo_rht_inverse(const float *y, uint32_t n, uint64_t seed, float *x)
+{
+    float a[256];
+    float s = inv_sqrt_n(n);
+    for (uint32_t i = 0; i < n; i++) a[i] = y[i];
+    fwht(a, n);
+    for (uint32_t i = 0; i < n; i++) {
+        float v = a[i] * s;
+        x[i] = hqo_sign_bit(seed, i) ? -v : v;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [M2] per-tile scale alpha.  Reading: step = bf16_rne(RMS(y) * c), where   */
+/* c is the rate constant for the target bps; the sum of squares is the     */
+/* pairwise tree ((y0^2 + y1^2) + (y2^2 + y3^2)) + ...  A step that rounds   */
+/* to zero or to a bf16 subnormal is stored as 0 (the tile decodes to 0).   */
+/* ------------------------------------------------------------------------ */
+float hqo_tile_step(const float *y, uint32_t n, float c, int *nonfinite)
+{
+    float sq[256];
+    for (uint32_t i = 0; i < n; i++) sq[i] = y[i] * y[i];
+    for (uint32_t m = n; m > 1; m >>= 1)
+        for (uint32_t i = 0; i < m / 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+    float ss = sq[0];
+    *nonfinite = 0;
+    if (!isfinite(ss)) { *nonfinite = 1; return 0.0f; }
+    float mean = ss * ldexpf(1.0f, -(int)log2u(n));     /* exact power-of-two scale */
+    float rms = sqrtf(mean);
+    float r = rms * c;
+    uint16_t sb = bf16_rne(r);
+    if ((sb & 0x7F80u) == 0x7F80u) { *nonfinite = 1; return 0.0f; }
+    if ((sb & 0x7F80u) == 0) return 0.0f;                 /* zero or subnormal */
+    return bf16_to_f32(sb);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [M2] nearest lattice points.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Z: coordinate-wise round half to even */
+static void nearest_Z(const float *t, int32_t *code, float *pt)
+{
+    float f = rintf(t[0]);
+    code[0] = 0; code[1] = (int32_t)f; pt[0] = f;
+}
+
+/* D4 = {x in Z^4 : sum x even} (Conway & Sloane's decoder): round every
+ * coordinate; if the sum is odd, move the coordinate with the largest
+ * rounding error (smallest index on ties) to its second-nearest integer. */
+static void nearest_D4(const float *t, int32_t *code, float *pt)
+{
+    float f[4], dl[4];
+    int32_t s = 0;
+    for (int i = 0; i < 4; i++) { f[i] = rintf(t[i]); dl[i] = t[i] - f[i]; s += (int32_t)f[i]; }
+    if (s & 1) {
+        int j = 0;
+        for (int i = 1; i < 4; i++) if (fabsf(dl[i]) > fabsf(dl[j])) j = i;
+        f[j] = (t[j] >= f[j]) ? f[j] + 1.0f : f[j] - 1.0f;
+    }
+    code[0] = 0;
+    for (int i = 0; i < 4; i++) { code[1 + i] = (int32_t)f[i]; pt[i] = f[i]; }
+}
+
+/* E8 = D8 u (D8 + 1/2) ([M2]: "E8 ... constant-time closed-form decoder").
+ * Candidate A: nearest point of D8 (as for D4).  Candidate B: nearest point
+ * of D8 + 1/2: start from floor(t) + 1/2 and, if sum floor(t) is odd, move
+ * the coordinate with the largest |t - (floor t + 1/2)| one step towards t.
+ *
+ * Choice between A and B.  With delta = t - rint(t) (|delta| <= 1/2) every
+ * coordinate's distance to floor(t) + 1/2 is 1/2 - |delta|, and in exact
+ * arithmetic
+ *   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|)
+ *                                       - [B moved](2 min|delta|);
+ * B's moved coordinate is the one of smallest |delta|.  B is taken iff this
+ * difference, evaluated in fp32 in the order written below, is > 0 (ties
+ * go to A).  Reading: the pages fix no decision arithmetic; this form is the
+ * exact identity evaluated with one rounding per operation. */
+static void nearest_E8(const float *t, int32_t *code, float *pt)
+{
+    float f[8], dl[8], ad[8];
+    int32_t fi[8], gi[8], sf = 0, sg = 0;
+    for (int i = 0; i < 8; i++) {
+        f[i] = rintf(t[i]);
+        dl[i] = t[i] - f[i];
+        ad[i] = fabsf(dl[i]);
+        fi[i] = (int32_t)f[i];
+        gi[i] = (int32_t)floorf(t[i]);
+        sf += fi[i];
+        sg += gi[i];
+    }
+    int oddA = sf & 1, oddB = sg & 1;
+    int jA = 0, jB = 0;
+    for (int i = 1; i < 8; i++) {
+        if (ad[i] > ad[jA]) jA = i;
+        if (ad[i] < ad[jB]) jB = i;
+    }
+    float mx = ad[jA], mn = ad[jB];
+    float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
+    float diff = sabs - 2.0f;
+    if (oddA) diff = diff + (1.0f - 2.0f * mx);
+    if (oddB) diff = diff - 2.0f * mn;
+    int useB = diff > 0.0f;
+
+    int32_t d[8];
+    if (!useB) {
+        for (int i = 0; i < 8; i++) d[i] = fi[i];
+        if (oddA) d[jA] += (t[jA] >= f[jA]) ? 1 : -1;
+    } else {
+        for (int i = 0; i < 8; i++) d[i] = gi[i];
+        if (oddB) d[jB] += (t[jB] >= (float)gi[jB] + 0.5f) ? 1 : -1;
+    }
+    code[0] = useB;
+    for (int i = 0; i < 8; i++) {
+        code[1 + i] = d[i];
+        pt[i] = useB ? (float)d[i] + 0.5f : (float)d[i];
+    }
+}
+
+/* A2 (hexagonal, minimal distance 1) = R u (R + (1/2, sqrt3/2)) with
+ * R = Z x sqrt3 Z: the nearer of the two rectangular-coset roundings,
+ * squared distances in fp32, ties to R.  Code: p, m, n' with point
+ * (m + p/2, sqrt3 (n' + p/2)). */
+static void nearest_A2(const float *t, int32_t *code, float *pt)
+{
+    const float S3 = sqrt3_f(), IS3 = inv_sqrt3_f();
+    float s1 = t[1] * IS3;
+    float am = rintf(t[0]), an = rintf(s1);
+    float bm = floorf(t[0]), bn = floorf(s1);
+    float a0 = am, a1 = S3 * an;
+    float b0 = bm + 0.5f, b1 = S3 * (bn + 0.5f);
+    float ea0 = t[0] - a0, ea1 = t[1] - a1;
+    float eb0 = t[0] - b0, eb1 = t[1] - b1;
+    float da = ea0 * ea0 + ea1 * ea1;
+    float db = eb0 * eb0 + eb1 * eb1;
+    if (db < da) { code[0] = 1; code[1] = (int32_t)bm; code[2] = (int32_t)bn; pt[0] = b0; pt[1] = b1; }
+    else         { code[0] = 0; code[1] = (int32_t)am; code[2] = (int32_t)an; pt[0] = a0; pt[1] = a1; }
+}
+
+void hqo_nearest(uint32_t lattice, const float *t, int32_t *code, float *point)
+{
+    switch (lattice) {
+    case HQO_Z:  nearest_Z(t, code, point); break;
+    case HQO_A2: nearest_A2(t, code, point); break;
+    case HQO_D4: nearest_D4(t, code, point); break;
+    case HQO_E8: nearest_E8(t, code, point); break;
+    }
+}
+
+void hqo_nearest_batch(uint32_t lattice, const float *t, uint64_t nblocks, int32_t *codes, float *points)
+{
+    uint32_t d = lattice_dim(lattice);
+    for (uint64_t b = 0; b < nblocks; b++)
+        hqo_nearest(lattice, t + b * d, codes + b * (d + 1), points + b * d);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [M4] subtractive dither U ~ Uniform(V(Lambda)).  Draw v uniformly on a    */
+/* box that is a fundamental region of a sublattice of Lambda (E8, D4:       */
+/* [-1,1)^d of 2Z^d; Z: [-1/2,1/2); A2: [-1/2,1/2) x sqrt3[-1/2,1/2) of R),  */
+/* then reduce into the Voronoi cell: u = v - Q(v).                          */
+/* ------------------------------------------------------------------------ */
+void hqo_dither_block(uint32_t lattice, uint64_t seed, uint32_t g0, float *u)
+{
+    uint32_t d = lattice_dim(lattice);
+    float v[8] = {0}, pt[8];
+    int32_t code[9];
+    for (uint32_t i = 0; i < d; i++) {
+        float a = (float)hqo_dither_bits(seed, g0 + i);       /* exact: 24 bits */
+        if (lattice == HQO_E8 || lattice == HQO_D4) v[i] = a * 0x1p-23f - 1.0f;
+        else v[i] = a * 0x1p-24f - 0.5f;
+    }
+    if (lattice == HQO_A2) v[1] = sqrt3_f() * v[1];
+    hqo_nearest(lattice, v, code, pt);
+    for (uint32_t i = 0; i < d; i++) u[i] = v[i] - pt[i];
+}
+
+/* ------------------------------------------------------------------------ */
+/* [M3] bit-stripping and Rice coding.                                      */
+/* ------------------------------------------------------------------------ */
+uint64_t hqo_rice_cost(const uint32_t *u, uint32_t n, uint32_t k)
+{
+    uint64_t c = 0;
+    for (uint32_t i = 0; i < n; i++) c += (uint64_t)(u[i] >> k) + 1u + k;
+    return c;
+}
+
+/* Reading: "k chosen per tile" = the k in 0..7 of smallest coded length,
+ * the smallest such k on ties. */
+uint32_t hqo_rice_k(const uint32_t *u, uint32_t n)
+{
+    uint32_t best = 0;
+    uint64_t bc = hqo_rice_cost(u, n, 0);
+    for (uint32_t k = 1; k < 8; k++) {
+        uint64_t c = hqo_rice_cost(u, n, k);
+        if (c < bc) { bc = c; best = k; }
+    }
+    return best;
+}
+
+/* Bit-stripping ([M3]: membership constraints fix some bits of the integer
+ * code): E8 keeps its coset bit raw and drops the parity of d7, which equals
+ * the parity of d0+...+d6 (D8 has even coordinate sum); D4 likewise drops the
+ * parity of w3.  Every other integer is zigzag-mapped to a non-negative
+ * symbol.  Symbols are in block order, coordinate order inside a block. */
+static void block_symbols(uint32_t lattice, const int32_t *code, uint32_t *sym)
+{
+    switch (lattice) {
+    case HQO_Z:  sym[0] = hqo_zigzag(code[1]); break;
+    case HQO_A2: sym[0] = hqo_zigzag(code[1]); sym[1] = hqo_zigzag(code[2]); break;
+    case HQO_D4:
+        for (int i = 0; i < 3; i++) sym[i] = hqo_zigzag(code[1 + i]);
+        sym[3] = hqo_zigzag(floor_half(code[4]));
+        break;
+    case HQO_E8:
+        for (int i = 0; i < 7; i++) sym[i] = hqo_zigzag(code[1 + i]);
+        sym[7] = hqo_zigzag(floor_half(code[8]));
+        break;
+    }
+}
+
+/* inverse of block_symbols + point reconstruction (decode) */
+static void block_point(uint32_t lattice, uint32_t p, const uint32_t *sym, float *pt)
+{
+    switch (lattice) {
+    case HQO_Z: pt[0] = (float)hqo_unzigzag(sym[0]); break;
+    case HQO_A2: {
+        float h = p ? 0.5f : 0.0f;
+        pt[0] = (float)hqo_unzigzag(sym[0]) + h;
+        pt[1] = sqrt3_f() * ((float)hqo_unzigzag(sym[1]) + h);
+        break;
+    }
+    case HQO_D4: {
+        int32_t w[4], s = 0;
+        for (int i = 0; i < 3; i++) { w[i] = hqo_unzigzag(sym[i]); s += w[i]; }
+        w[3] = 2 * hqo_unzigzag(sym[3]) + (s & 1);
+        for (int i = 0; i < 4; i++) pt[i] = (float)w[i];
+        break;
+    }
+    case HQO_E8: {
+        int32_t d[8], s = 0;
+        for (int i = 0; i < 7; i++) { d[i] = hqo_unzigzag(sym[i]); s += d[i]; }
+        d[7] = 2 * hqo_unzigzag(sym[7]) + (s & 1);
+        for (int i = 0; i < 8; i++) pt[i] = p ? (float)d[i] + 0.5f : (float)d[i];
+        break;
+    }
+    }
+}
+
+/* ---- bit I/O: bit b of a stream is bit (b & 31) of 32-bit word b >> 5 ---- */
+static void put_bit(uint32_t *w, uint64_t b, uint32_t v) { if (v) w[b >> 5] |= 1u << (b & 31); }
+static uint32_t get_bit(const uint32_t *w, uint64_t b) { return (w[b >> 5] >> (b & 31)) & 1u; }
+
+/* Rice_k(u): (u >> k) zero bits, a one bit, then the k low bits of u, least
+ * significant first.  Reading: the pages fix neither polarity nor bit order. */
+static uint64_t put_rice(uint32_t *w, uint64_t b, uint32_t u, uint32_t k)
+{
+    uint32_t q = u >> k;
+    b += q;                       /* zeros: buffer is zero-initialised */
+    put_bit(w, b++, 1);
+    for (uint32_t i = 0; i < k; i++) put_bit(w, b++, (u >> i) & 1u);
+    return b;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Capacity: a bound on any tile's length from the per-tile scale.          */
+/* |t|_2 <= sqrt(n)/c' (c' = c with bf16 rounding margin), so               */
+/* sum|t_i| <= n/c'; every code integer is within 3/2 of t_i (covering      */
+/* radius <= 1, plus the coset half), so sum of symbols <= 2n/c' + 3n       */
+/* (+2n with the dither, |u_i| <= 1); C(k*) <= C(k) for every k.             */
+/* ------------------------------------------------------------------------ */
+uint32_t hqo_tile_bound_bits(const hqo_params *p)
+{
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    if (!d || !(p->c > 0.0f) || !isfinite(p->c)) return 0;
+    double cp = (double)p->c * (1.0 - 1.0 / 128.0);
+    double S = 2.0 * n / cp + 3.0 * n + (p->dither ? 2.0 * n : 0.0);
+    double best = 1e300;
+    for (int k = 0; k < 8; k++) {
+        double L = floor(S / (double)(1u << k)) + (double)n * (1 + k);
+        if (L < best) best = L;
+    }
+    double B = (double)(n / d) * coset_bits_per_block(p->lattice);
+    double bound = B + best;
+    if (bound > 8191.0) return 0;
+    return (uint32_t)bound;
+}
+
+static int check_params(const hqo_params *p)
+{
+    if (p->dtype != HQO_F32 && p->dtype != HQO_BF16) return HQO_EINVAL;
+    if (p->tile != 64 && p->tile != 128 && p->tile != 256) return HQO_EINVAL;
+    if (!lattice_dim(p->lattice)) return HQO_EINVAL;
+    if (p->dither > 1) return HQO_EINVAL;
+    if (p->rows == 0 || p->cols == 0 || p->cols % p->tile) return HQO_EINVAL;
+    if (p->rows * p->cols >= (1ull << 32)) return HQO_EINVAL;
+    if (!hqo_tile_bound_bits(p)) return HQO_EINVAL;
+    return HQO_OK;
+}
+
+uint64_t hqo_payload_cap_words(const hqo_params *p)
+{
+    if (check_params(p) != HQO_OK) return 0;
+    uint64_t T = p->rows * p->cols / p->tile;
+    uint64_t C = (T + HQO_CHUNK_TILES - 1) / HQO_CHUNK_TILES;
+    return (T * hqo_tile_bound_bits(p) + 31) / 32 + C;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encode one tile: symbols, coset bits, k, length.                         */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint16_t step;
+    uint32_t k, len, nonfinite;
+    uint32_t nb;            /* number of coset bits */
+    uint32_t cos[256];      /* coset bits in block order */
+    uint32_t sym[256];
+} tile_code;
+
+static void load_tile(const void *x, const hqo_params *p, uint64_t t, float *xt)
+{
+    uint64_t base = t * p->tile;
+    for (uint32_t i = 0; i < p->tile; i++) {
+        if (p->dtype == HQO_F32) xt[i] = ((const float *)x)[base + i];
+        else xt[i] = bf16_to_f32(((const uint16_t *)x)[base + i]);
+    }
+}
+
+static void encode_tile(const void *x, const hqo_params *p, uint64_t t, tile_code *tc)
+{
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    float xt[256], y[256], tt[256];
+    load_tile(x, p, t, xt);
+    hqo_rht_forward(xt, n, p->seed, y);                       /* [M1] */
+    int nf;
+    float s = hqo_tile_step(y, n, p->c, &nf);                 /* [M2] alpha */
+    tc->nonfinite = nf;
+    tc->step = bf16_rne(s);
+    float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    /* a tile with a non-finite energy is reported and coded as a zero tile */
+    for (uint32_t i = 0; i < n; i++) tt[i] = nf ? 0.0f : y[i] * inv;
+    if (p->dither) {                                          /* [M4] t + U */
+        for (uint32_t b = 0; b < n; b += d) {
+            float u[8];
+            hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + b), u);
+            for (uint32_t i = 0; i < d; i++) tt[b + i] = tt[b + i] + u[i];
+        }
+    }
+    tc->nb = 0;
+    for (uint32_t b = 0; b < n; b += d) {                     /* [M2] nearest point */
+        int32_t code[9];
+        float pt[8];
+        hqo_nearest(p->lattice, tt + b, code, pt);
+        if (coset_bits_per_block(p->lattice)) tc->cos[tc->nb++] = (uint32_t)code[0];
+        block_symbols(p->lattice, code, tc->sym + b);         /* [M3] strip */
+    }
+    tc->k = hqo_rice_k(tc->sym, n);                           /* [M3] Rice */
+    tc->len = tc->nb + (uint32_t)hqo_rice_cost(tc->sym, n, tc->k);
+}
+
+static uint64_t write_tile(uint32_t *w, uint64_t b, const tile_code *tc, uint32_t n)
+{
+    for (uint32_t i = 0; i < tc->nb; i++) put_bit(w, b++, tc->cos[i]);
+    for (uint32_t i = 0; i < n; i++) b = put_rice(w, b, tc->sym[i], tc->k);
+    return b;
+}
+
+/* Stream layout (reading; the pages give none): tiles in row-major order,
+ * each tile = its coset bits then its n Rice codewords; tiles are
+ * bit-contiguous inside a chunk of 64 tiles; every chunk starts on a 32-bit
+ * word (chunk_off[c] = its first word, chunk_off[C] = total words) and its
+ * tail is zero-padded.  meta[t] = len << 3 | k; step[t] = bf16 bits. */
+int hqo_encode(const void *x, const hqo_params *p,
+               uint16_t *step, uint16_t *meta, uint32_t *chunk_off,
+               uint32_t *payload, uint64_t payload_cap_words)
+{
+    int rc = check_params(p);
+    if (rc) return rc;
+    uint64_t T = p->rows * p->cols / p->tile;
+    uint64_t C = (T + HQO_CHUNK_TILES - 1) / HQO_CHUNK_TILES;
+    tile_code *tc = (tile_code *)malloc(sizeof(tile_code));
+    if (!tc) return HQO_ENOSPC;
+    int status = HQO_OK;
+    uint64_t word = 0;
+    for (uint64_t c = 0; c < C; c++) {
+        chunk_off[c] = (uint32_t)word;
+        uint64_t t0 = c * HQO_CHUNK_TILES, t1 = t0 + HQO_CHUNK_TILES;
+        if (t1 > T) t1 = T;
+        uint64_t bit = word * 32;
+        for (uint64_t t = t0; t < t1; t++) {
+            encode_tile(x, p, t, tc);
+            if (tc->nonfinite) status = HQO_ENONFINITE;
+            step[t] = tc->step;
+            meta[t] = (uint16_t)((tc->len << 3) | tc->k);
+            uint64_t need = (bit + tc->len + 31) / 32;
+            if (need > payload_cap_words) { free(tc); return HQO_ENOSPC; }
+            for (uint64_t w = bit / 32 + 1; w < need; w++) payload[w] = 0;
+            if (bit % 32 == 0) payload[bit / 32] = 0;
+            bit = write_tile(payload, bit, tc, p->tile);
+        }
+        word = (bit + 31) / 32;
+    }
+    chunk_off[C] = (uint32_t)word;
+    free(tc);
+    return status;
+}
+
+int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t1,
+                     uint16_t *step, uint16_t *meta, uint32_t *bits, uint64_t bits_cap_words)
+{
+    int rc = check_params(p);
+    if (rc) return rc;
+    uint64_t T = p->rows * p->cols / p->tile;
+    if (t0 > t1 || t1 > T) return HQO_EINVAL;
+    tile_code *tc = (tile_code *)malloc(sizeof(tile_code));
+    if (!tc) return HQO_ENOSPC;
+    memset(bits, 0, bits_cap_words * 4);
+    int status = HQO_OK;
+    uint64_t bit = 0;
+    for (uint64_t t = t0; t < t1; t++) {
+        encode_tile(x, p, t, tc);
+        if (tc->nonfinite) status = HQO_ENONFINITE;
+        step[t - t0] = tc->step;
+        meta[t - t0] = (uint16_t)((tc->len << 3) | tc->k);
+        if ((bit + tc->len + 31) / 32 > bits_cap_words) { free(tc); return HQO_ENOSPC; }
+        bit = write_tile(bits, bit, tc, p->tile);
+    }
+    free(tc);
+    return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode: parse, rebuild lattice points, undo dither, scale, inverse RHT.  */
+/* ------------------------------------------------------------------------ */
+int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk_off,
+               const uint32_t *payload, uint64_t payload_words,
+               const hqo_params *p, void *x_out)
+{
+    int rc = check_params(p);
+    if (rc) return rc;
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    uint32_t nb = (n / d) * coset_bits_per_block(p->lattice);
+    uint64_t T = p->rows * p->cols / n;
+    uint64_t C = (T + HQO_CHUNK_TILES - 1) / HQO_CHUNK_TILES;
+    int status = HQO_OK;
+    if (chunk_off[0] != 0 || chunk_off[C] > payload_words) return HQO_ECORRUPT;
+    for (uint64_t c = 0; c < C; c++) {
+        uint64_t w0 = chunk_off[c], w1 = chunk_off[c + 1];
+        if (w1 < w0 || w1 > payload_words) return HQO_ECORRUPT;
+        uint64_t b = w0 * 32, bend = w1 * 32;
+        uint64_t t0 = c * HQO_CHUNK_TILES, t1 = t0 + HQO_CHUNK_TILES;
+        if (t1 > T) t1 = T;
+        for (uint64_t t = t0; t < t1; t++) {
+            uint32_t len = meta[t] >> 3, k = meta[t] & 7u;
+            uint64_t tb = b;
+            int bad = 0;
+            uint32_t cos[256], sym[256];
+            for (uint32_t i = 0; i < nb; i++) {
+                if (b >= bend) { bad = 1; break; }
+                cos[i] = get_bit(payload, b++);
+            }
+            for (uint32_t i = 0; i < n && !bad; i++) {
+                uint32_t q = 0;
+                while (b < bend && !get_bit(payload, b)) { q++; b++; }
+                if (b >= bend || q > (1u << 20)) { bad = 1; break; }
+                b++;                                  /* the terminating one */
+                uint32_t r = 0;
+                for (uint32_t j = 0; j < k; j++) {
+                    if (b >= bend) { bad = 1; break; }
+                    r |= get_bit(payload, b++) << j;
+                }
+                sym[i] = (q << k) | r;
+            }
+            if (bad || b - tb != len) {
+                status = HQO_ECORRUPT;
+                memset(sym, 0, sizeof sym);
+                memset(cos, 0, sizeof cos);
+                b = tb + len;
+                if (b > bend) return HQO_ECORRUPT;
+            }
+            float s = bf16_to_f32(step[t]);
+            float v[256], xo[256];
+            for (uint32_t blk = 0; blk < n / d; blk++) {
+                float pt[8];
+                uint32_t pc = coset_bits_per_block(p->lattice) ? cos[blk] : 0;
+                block_point(p->lattice, pc, sym + blk * d, pt);
+                if (p->dither) {
+                    float u[8];
+                    hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + blk * d), u);
+                    for (uint32_t i = 0; i < d; i++) pt[i] = pt[i] - u[i];
+                }
+                for (uint32_t i = 0; i < d; i++) v[blk * d + i] = pt[i] * s;
+            }
+            hqo_rht_inverse(v, n, p->seed, xo);
+            for (uint32_t i = 0; i < n; i++) {
+                if (p->dtype == HQO_F32) ((float *)x_out)[t * n + i] = xo[i];
+                else ((uint16_t *)x_out)[t * n + i] = bf16_rne(xo[i]);
+            }
+        }
+        if ((b + 31) / 32 != w1) status = HQO_ECORRUPT;
+    }
+    return status;
+}

@@ -1,0 +1,132 @@
+"""Pins of the oracle's transform steps against facts fixed by the pages and
+by mathematics: the RHT is H_n D x scaled to be orthogonal (gist.science
+explainer of HyperQuant, Methodology section 1), the generator's outputs are
+balanced, and the per-tile scale is the RMS times the rate constant."""
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from hq_testutil import golden_hadamard
+from kv_cache_tile_amd import workloads
+
+
+# ---------------------------------------------------------------- generator
+def test_pcg_hash_is_a_bijection_on_a_large_sample():
+    # a random function would collide ~2^39/2^32 = 128 times on 2^20 inputs
+    L = oracle.lib()
+    vals = np.array([L.hqo_pcg_hash(i * 2654435761 & 0xFFFFFFFF) for i in range(1 << 16)], np.uint64)
+    assert len(np.unique(vals)) == vals.size
+
+
+def test_sign_bits_balanced_and_seed_dependent():
+    s0 = oracle.sign_bits(0, 4096)
+    s1 = oracle.sign_bits(1, 4096)
+    assert abs(s0.mean() - 0.5) < 0.03 and abs(s1.mean() - 0.5) < 0.03
+    assert 0.4 < (s0 != s1).mean() < 0.6            # independent-looking diagonals
+
+
+def test_dither_bits_uniform_24bit():
+    a = np.array([oracle.dither_bits(3, g) for g in range(1 << 15)], np.int64)
+    assert a.min() >= 0 and a.max() < (1 << 24)
+    h = np.bincount(a >> 20, minlength=16)          # top 4 bits: chi-square, 15 dof
+    chi2 = ((h - a.size / 16) ** 2 / (a.size / 16)).sum()
+    assert chi2 < 40.0
+    assert abs((a & 1).mean() - 0.5) < 0.02
+
+
+# ---------------------------------------------------------------- RHT
+@pytest.mark.parametrize("n", [2, 4])
+def test_rht_matches_textbook_sylvester_matrix(n):
+    H = golden_hadamard()[n]
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n).astype(np.float32)
+    seed = 11
+    sig = oracle.sign_bits(seed, n)
+    D = np.diag(np.where(sig == 1, -1.0, 1.0))
+    want = H @ D @ x.astype(np.float64) / np.sqrt(n)
+    got = oracle.rht_forward(x, seed)
+    np.testing.assert_allclose(got, want, rtol=0, atol=4e-7 * np.abs(x).sum())
+
+
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_rht_closed_form_within_fp32_error_bound(n):
+    # y_i = (1/sqrt n) sum_j (-1)^popcount(i&j) sigma_j x_j; a butterfly of depth
+    # log2 n in fp32 errs by at most about (log2 n + 1) 2^-24 |x|_1 / sqrt(n) per entry
+    H = scipy.linalg.hadamard(n).astype(np.float64)
+    rng = np.random.default_rng(n)
+    for seed in (0, 5, (4 << 32) | 7):
+        x = workloads.student_t_outlier_cols(4, n, key=seed & 0xFF, n_out=2)[0]
+        sig = oracle.sign_bits(seed, n)
+        want = H @ (np.where(sig == 1, -1.0, 1.0) * x.astype(np.float64)) / np.sqrt(n)
+        got = oracle.rht_forward(x, seed).astype(np.float64)
+        bound = (np.log2(n) + 2) * 2.0 ** -24 * np.abs(x).sum() / np.sqrt(n) + 1e-30
+        assert np.max(np.abs(got - want)) <= bound
+    del rng
+
+
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_rht_is_orthogonal(n):
+    # build the matrix column by column from basis vectors: M M^T = I
+    M = np.stack([oracle.rht_forward(np.eye(n, dtype=np.float32)[j], 9) for j in range(n)], axis=1)
+    M = M.astype(np.float64)
+    np.testing.assert_allclose(M @ M.T, np.eye(n), atol=2e-6)
+
+
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_rht_preserves_norm_and_inverts(n):
+    rng = np.random.default_rng(100 + n)
+    for _ in range(20):
+        x = (rng.standard_normal(n) * rng.uniform(1e-3, 1e3)).astype(np.float32)
+        y = oracle.rht_forward(x, 21)
+        assert abs(np.linalg.norm(y.astype(np.float64)) / np.linalg.norm(x.astype(np.float64)) - 1) < 1e-6
+        xr = oracle.rht_inverse(y, 21)
+        np.testing.assert_allclose(xr, x, rtol=0, atol=2e-6 * np.abs(x).max())
+
+
+def test_rht_gaussianizes_heavy_tailed_tiles():
+    # Methodology section 1: per-coordinate distribution becomes ~N(0, s^2).
+    # Student-t(4) entries: kurtosis >> 3 before, ~3 after (CLT over the tile).
+    # (A tile dominated by one spike maps to a +-constant vector instead, which
+    # is why the outlier columns are left out of this check.)
+    x = workloads.student_t_outlier_cols(256, 1024, key=0, n_out=0)
+    tiles = x.reshape(-1, 128)
+    y = np.concatenate([oracle.rht_forward(t, 0) for t in tiles])
+    xs = tiles.reshape(-1).astype(np.float64)
+    yn = np.concatenate([(t / np.sqrt(np.mean(t.astype(np.float64) ** 2)))
+                         for t in y.reshape(-1, 128)])
+    kx = np.mean((xs - xs.mean()) ** 4) / np.var(xs) ** 2
+    ky = np.mean(yn ** 4) / np.mean(yn ** 2) ** 2
+    assert kx > 6
+    assert abs(ky - 3.0) < 0.25
+
+
+# ---------------------------------------------------------------- scale
+@pytest.mark.parametrize("n", [64, 128, 256])
+def test_tile_step_is_bf16_rne_of_rms_times_c(n):
+    rng = np.random.default_rng(7 + n)
+    for _ in range(50):
+        y = (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        c = np.float32(rng.uniform(0.01, 3.0))
+        s, nf = oracle.tile_step(y, c)
+        assert not nf
+        rms64 = np.sqrt(np.mean(y.astype(np.float64) ** 2))
+        r32 = np.float32(rms64 * np.float64(c))
+        # before bf16 rounding the fp32 product agrees with fp64 to ~1e-6
+        ref_bf16 = torch.tensor([float(r32)], dtype=torch.float32).to(torch.bfloat16).float().item()
+        assert abs(float(s) - ref_bf16) <= 2.0 ** -7 * ref_bf16   # at most one bf16 ulp apart
+        assert abs(float(s) - rms64 * c) <= 2.0 ** -8 * rms64 * c * 1.0001
+
+
+def test_tile_step_special_values():
+    n = 128
+    s, nf = oracle.tile_step(np.zeros(n, np.float32), 0.3)
+    assert s == 0 and not nf
+    y = np.zeros(n, np.float32); y[3] = np.nan
+    assert oracle.tile_step(y, 0.3)[1]
+    y[3] = np.inf
+    assert oracle.tile_step(y, 0.3)[1]
+    y = np.full(n, 1e-40, np.float32)                      # bf16-subnormal step -> 0
+    s, nf = oracle.tile_step(y, 0.3)
+    assert s == 0 and not nf
