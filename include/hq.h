@@ -1,0 +1,147 @@
+/*
+ * hq.h — C ABI of the HyperQuant encode/decode library (libhq.so, HIP, gfx950).
+ *
+ * The library compresses a row-major 2-D tensor (LLM weights, or KV-cache
+ * vectors) with the HyperQuant pipeline as described in "HyperQuant: A
+ * Rate-Distortion-Optimal Quantization Pipeline for Large Language and
+ * Diffusion Models" (gist.science explainer, section "Methodology: The
+ * HyperQuant Pipeline"):
+ *   1. per-tile Randomized Hadamard Transform  y = H_n D x / sqrt(n)  (tile n
+ *      contiguous elements of a row, seeded sign diagonal D)        [Methodology 1]
+ *   2. per-tile scale (step = bf16(RMS(y) * c(bps))) and nearest point of the
+ *      E8 (D8 u D8+1/2), D4, A2 or Z lattice, block by block           [Methodology 2]
+ *   3. lossless bit-stripping of the lattice code and Rice coding with one
+ *      parameter k in 0..7 per tile (the shortest)                   [Methodology 3]
+ *   4. KV variant: a subtractive dither U ~ Uniform(Voronoi cell), added
+ *      before quantization and subtracted after, regenerated from the seed
+ *      at decode; the sign diagonal is the per-layer rotation         [Methodology 4]
+ * and the inverse (decode).
+ *
+ * Conventions
+ *  - All tensor/buffer pointers are DEVICE pointers (hipMalloc'd or
+ *    torch-owned); descriptors and sizes are host values.  `stream` is a
+ *    hipStream_t passed as void* (NULL = default stream).  Every compute call
+ *    is asynchronous on `stream`; buffers must stay alive until it is
+ *    synchronised.  The library allocates no device memory and keeps no
+ *    pointer after returning.
+ *  - Return value: 0 (HQ_OK) or a negative hq_status for argument errors
+ *    (synchronous, nothing launched) and HIP launch errors.  Data-dependent
+ *    conditions found while the kernels run are OR-ed as HQ_FLAG_* bits into
+ *    the device word *status (the caller zeroes it before the call and reads
+ *    it after synchronising).
+ *  - Input is never modified.
+ *
+ * Compressed layout (all produced by hq_encode, consumed by hq_decode):
+ *  - T = rows*cols/tile tiles in row-major order; C = ceil(T/64) chunks.
+ *  - step[T]      uint16 bf16 bits of the per-tile step (0 = zero tile)
+ *  - meta[T]      uint16 (len << 3) | k : tile bit length and Rice parameter
+ *  - chunk_off[C+1] uint32 word offset of each chunk in payload; last = total
+ *  - payload[]    uint32 words; bit b of a chunk = bit (b & 31) of its word
+ *                 b >> 5.  A tile is its coset bits (E8: n/8, A2: n/2) then n
+ *                 Rice codewords (q zeros, a one, k remainder bits LSB first);
+ *                 tiles are bit-contiguous within a chunk; each chunk starts
+ *                 on a word and its tail bits are zero.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HQ_OK = 0,
+    HQ_EINVAL = -1,      /* bad shape, tile, lattice, dtype, or bps not on the rate grid */
+    HQ_EHIP = -2,        /* HIP runtime / launch error */
+    HQ_ENOSPC = -3,      /* a capacity argument is below what hq_plan reported */
+    HQ_ENONFINITE = -4,  /* (status flag) non-finite input tile */
+    HQ_ECORRUPT = -5     /* (status flag) inconsistent compressed stream */
+} hq_status;
+
+/* bits OR-ed into *status by the kernels */
+#define HQ_FLAG_NONFINITE 1u   /* encode: a tile had a non-finite energy; it was coded as zero */
+#define HQ_FLAG_CORRUPT   2u   /* decode: a tile's parsed length disagreed with meta (tile -> 0) */
+#define HQ_FLAG_NOSPACE   4u   /* encode: payload capacity exceeded (nothing written past it) */
+
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+typedef enum { HQ_Z = 1, HQ_A2 = 2, HQ_D4 = 4, HQ_E8 = 8 } hq_lattice;
+
+/*
+ * hq_plan — host-only, synchronous.  Validates a configuration and returns
+ * the sizes of the buffers the caller must allocate.
+ *   dtype    HQ_F32 or HQ_BF16 (encode input and decode output element type)
+ *   rows, cols  tensor shape, cols % tile == 0, rows*cols < 2^32
+ *   tile     64, 128 or 256 (the RHT size n; "tiles (e.g. size 128)",
+ *            Methodology 1)
+ *   lattice  HQ_Z, HQ_A2, HQ_D4, HQ_E8 (Methodology 2)
+ *   bps      target payload bits per scalar on the grid 1.5, 1.75, ..., 8
+ *            ("within ~0.01 bps of any target", Methodology 3)
+ *   kv       0 for weights (hq_encode), 1 for the dithered KV variant
+ * Outputs (any may be NULL): tiles T, chunks C, payload capacity in words
+ * (worst case over all inputs), workspace bytes for hq_encode / hq_kv_encode,
+ * the worst-case tile length in bits, and the rate constant c used.
+ */
+int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+            float bps, uint32_t kv,
+            uint64_t *tiles, uint64_t *chunks, uint64_t *payload_cap_words,
+            uint64_t *workspace_bytes, uint32_t *tile_bound_bits, float *rate_constant);
+
+/*
+ * hq_encode — weights.  Methodology 1-3.
+ *   x          device, [rows][cols] of dtype, row-major, read only
+ *   seed       selects the sign diagonal D
+ *   payload    device, payload_cap_words uint32 (>= hq_plan's capacity)
+ *   step, meta device, T uint16 each
+ *   chunk_off  device, C+1 uint32
+ *   status     device, one uint32 (flags OR-ed in)
+ *   workspace  device, workspace_bytes (>= hq_plan's) zero-filled ONCE
+ *              before its first use; the kernels leave it ready for the next
+ *              call.  Calls that overlap in time must not share a workspace.
+ * The bit stream is a pure function of (x, shape, tile, lattice, bps, seed).
+ */
+int hq_encode(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+              uint32_t lattice, float bps, uint64_t seed,
+              uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,
+              uint32_t *chunk_off, uint32_t *status, void *workspace, uint64_t workspace_bytes,
+              void *stream);
+
+/*
+ * hq_decode — inverse of hq_encode: Rice parse, lattice point, step, inverse
+ * RHT.  Same shape arguments and seed as the encode; writes x_out
+ * ([rows][cols] of dtype, device).  payload_words = chunk_off[C] of the
+ * stream (the number of valid words); reads never go beyond it.
+ */
+int hq_decode(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
+              const uint16_t *meta, const uint32_t *chunk_off,
+              uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+              float bps, uint64_t seed, void *x_out, uint32_t *status, void *stream);
+
+/*
+ * hq_kv_encode / hq_kv_decode — KV cache (Methodology 4).  x is [tokens][head_dim]
+ * (e.g. a [B, H, S, D] cache viewed as B*H*S rows), one tile per (token, head)
+ * vector: tile = head_dim.  seed selects the per-layer sign diagonal and the
+ * dither; the dither of coordinate g (row-major index in the call) is
+ * regenerated at decode, so decode must use the same seed and shape.
+ * Other arguments as hq_encode / hq_decode.
+ */
+int hq_kv_encode(const void *x, uint32_t dtype, uint64_t tokens, uint32_t head_dim,
+                 uint32_t lattice, float bps, uint64_t seed,
+                 uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,
+                 uint32_t *chunk_off, uint32_t *status, void *workspace, uint64_t workspace_bytes,
+                 void *stream);
+int hq_kv_decode(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
+                 const uint16_t *meta, const uint32_t *chunk_off,
+                 uint32_t dtype, uint64_t tokens, uint32_t head_dim, uint32_t lattice,
+                 float bps, uint64_t seed, void *x_out, uint32_t *status, void *stream);
+
+/* message for a hq_status code (static storage) */
+const char *hq_strerror(int code);
+/* (major << 16) | minor of the library; the stream layout above is version 1 */
+uint32_t hq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

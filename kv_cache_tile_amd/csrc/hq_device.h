@@ -1,0 +1,263 @@
+// hq_device.h — device building blocks of the HyperQuant HIP kernels (gfx950).
+//
+// Source of the method: "HyperQuant: A Rate-Distortion-Optimal Quantization
+// Pipeline for Large Language and Diffusion Models", gist.science explainer,
+// section "Methodology: The HyperQuant Pipeline" (cited below as Methodology
+// 1-4).  Every floating-point step is one IEEE binary32 operation in a fixed
+// order (the library is built with -ffp-contract=off and without fast-math),
+// so that the output is a pure function of the input.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+constexpr int kChunkTiles = 64;   // tiles per chunk of the stream
+constexpr int kLaneElems = 32;    // tile elements held by one lane
+
+// --------------------------------------------------------------------------
+// Counter-based generator: the "pcg" hash of Jarzynski & Olano (JCGT 9(3),
+// 2020): one PCG LCG step followed by PCG's RXS-M-XS output permutation.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pcg_hash(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// bf16 round-to-nearest-even of a finite value (bit arithmetic)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = as_u(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t zigzag(int32_t v) {
+  return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
+}
+__device__ __forceinline__ int32_t unzigzag(uint32_t u) {
+  return (int32_t)(u >> 1) ^ -(int32_t)(u & 1u);
+}
+
+template <int LAT> struct LatticeTraits;
+template <> struct LatticeTraits<1> { static constexpr int dim = 1, coset = 0; };
+template <> struct LatticeTraits<2> { static constexpr int dim = 2, coset = 1; };
+template <> struct LatticeTraits<4> { static constexpr int dim = 4, coset = 0; };
+template <> struct LatticeTraits<8> { static constexpr int dim = 8, coset = 1; };
+
+struct A2Consts { float sqrt3, inv_sqrt3; };
+
+// --------------------------------------------------------------------------
+// Nearest lattice points (Methodology 2).  t: d coordinates; writes the
+// integer code d[] and coset bit p.  Tie rules: round half to even; the
+// moved coordinate of a D_n candidate is the one with the largest |t - rint t|
+// (smallest index on ties), moved towards t; E8 picks the half-integer coset
+// only when it is strictly nearer.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ void nearest_z(const float* t, int32_t* d, uint32_t& p) {
+  d[0] = (int32_t)__builtin_rintf(t[0]);
+  p = 0;
+}
+
+__device__ __forceinline__ void nearest_d4(const float* t, int32_t* d, uint32_t& p) {
+  float f[4], ad[4];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[i] = __builtin_rintf(t[i]);
+    ad[i] = __builtin_fabsf(t[i] - f[i]);
+    s += (int32_t)f[i];
+  }
+  int j = 0;
+  float mx = ad[0];
+#pragma unroll
+  for (int i = 1; i < 4; i++)
+    if (ad[i] > mx) { mx = ad[i]; j = i; }
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    int32_t a = (int32_t)f[i];
+    if ((s & 1) && i == j) a += (t[i] >= f[i]) ? 1 : -1;
+    d[i] = a;
+  }
+  p = 0;
+}
+
+// E8 = D8 u (D8 + 1/2).  With delta = t - rint(t):
+//   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|) - [B moved](2 min|delta|)
+// (exact identity; B's moved coordinate is the one of smallest |delta|),
+// evaluated in fp32 in this order; B iff > 0.
+__device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t& p) {
+  float f[8], ad[8];
+  int32_t g[8], sf = 0, sg = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    f[i] = __builtin_rintf(t[i]);
+    ad[i] = __builtin_fabsf(t[i] - f[i]);
+    g[i] = (int32_t)__builtin_floorf(t[i]);
+    sf += (int32_t)f[i];
+    sg += g[i];
+  }
+  int jA = 0, jB = 0;
+  float mx = ad[0], mn = ad[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) {
+    if (ad[i] > mx) { mx = ad[i]; jA = i; }
+    if (ad[i] < mn) { mn = ad[i]; jB = i; }
+  }
+  float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
+  float diff = sabs - 2.0f;
+  if (sf & 1) diff = diff + (1.0f - 2.0f * mx);
+  if (sg & 1) diff = diff - 2.0f * mn;
+  const bool useB = diff > 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    int32_t a = (int32_t)f[i];
+    if ((sf & 1) && i == jA) a += (t[i] >= f[i]) ? 1 : -1;
+    int32_t b = g[i];
+    if ((sg & 1) && i == jB) b += (t[i] >= (float)g[i] + 0.5f) ? 1 : -1;
+    d[i] = useB ? b : a;
+  }
+  p = useB ? 1u : 0u;
+}
+
+// A2 = R u (R + (1/2, sqrt3/2)), R = Z x sqrt3 Z; code (p, m, n') with point
+// (m + p/2, sqrt3 (n' + p/2)).
+__device__ __forceinline__ void nearest_a2(const float* t, int32_t* d, uint32_t& p, A2Consts k) {
+  float s1 = t[1] * k.inv_sqrt3;
+  float am = __builtin_rintf(t[0]), an = __builtin_rintf(s1);
+  float bm = __builtin_floorf(t[0]), bn = __builtin_floorf(s1);
+  float a1 = k.sqrt3 * an;
+  float b0 = bm + 0.5f, b1 = k.sqrt3 * (bn + 0.5f);
+  float ea0 = t[0] - am, ea1 = t[1] - a1;
+  float eb0 = t[0] - b0, eb1 = t[1] - b1;
+  float da = ea0 * ea0 + ea1 * ea1;
+  float db = eb0 * eb0 + eb1 * eb1;
+  const bool useB = db < da;
+  d[0] = (int32_t)(useB ? bm : am);
+  d[1] = (int32_t)(useB ? bn : an);
+  p = useB ? 1u : 0u;
+}
+
+template <int LAT>
+__device__ __forceinline__ void nearest(const float* t, int32_t* d, uint32_t& p, A2Consts k) {
+  if constexpr (LAT == 1) nearest_z(t, d, p);
+  else if constexpr (LAT == 2) nearest_a2(t, d, p, k);
+  else if constexpr (LAT == 4) nearest_d4(t, d, p);
+  else nearest_e8(t, d, p);
+}
+
+// lattice point (as floats) of a code (used for the dither reduction)
+template <int LAT>
+__device__ __forceinline__ void code_point(const int32_t* d, uint32_t p, float* pt, A2Consts k) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+  if constexpr (LAT == 2) {
+    float h = p ? 0.5f : 0.0f;
+    pt[0] = (float)d[0] + h;
+    pt[1] = k.sqrt3 * ((float)d[1] + h);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; i++) pt[i] = (LAT == 8 && p) ? (float)d[i] + 0.5f : (float)d[i];
+  }
+}
+
+// Bit-stripping + zigzag (Methodology 3): the last coordinate of a D4/E8
+// block is stored halved (its parity equals that of the other coordinates'
+// sum); everything else is zigzag-mapped.
+template <int LAT>
+__device__ __forceinline__ void block_symbols(const int32_t* d, uint32_t* u) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    int32_t v = d[i];
+    if ((LAT == 4 || LAT == 8) && i == D - 1) v = v >> 1;   // arithmetic shift: floor(v / 2)
+    u[i] = zigzag(v);
+  }
+}
+
+// inverse: symbols + coset bit -> lattice point (floats)
+template <int LAT>
+__device__ __forceinline__ void block_point(const uint32_t* u, uint32_t p, float* pt, A2Consts k) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+  int32_t d[D];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    d[i] = unzigzag(u[i]);
+    if (i < D - 1) s += d[i];
+  }
+  if constexpr (LAT == 4 || LAT == 8) d[D - 1] = 2 * d[D - 1] + (s & 1);
+  code_point<LAT>(d, p, pt, k);
+}
+
+// Subtractive dither (Methodology 4): v uniform on a box that is a
+// fundamental region of a sublattice (E8, D4: [-1,1)^d of 2Z^d; Z: [-1/2,1/2);
+// A2: [-1/2,1/2) x sqrt3 [-1/2,1/2) of Z x sqrt3 Z), reduced into the Voronoi
+// cell: u = v - Q(v).  24 uniform bits per coordinate g.
+template <int LAT>
+__device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, float* u, A2Consts k) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+  float v[D];
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    float a = (float)(pcg_hash(key_dither + g0 + (uint32_t)i) >> 8);
+    if constexpr (LAT == 8 || LAT == 4) v[i] = a * 0x1p-23f - 1.0f;
+    else v[i] = a * 0x1p-24f - 0.5f;
+  }
+  if constexpr (LAT == 2) v[1] = k.sqrt3 * v[1];
+  int32_t d[D];
+  uint32_t p;
+  nearest<LAT>(v, d, p, k);
+  float pt[D];
+  code_point<LAT>(d, p, pt, k);
+#pragma unroll
+  for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
+}
+
+// --------------------------------------------------------------------------
+// Fast Walsh-Hadamard butterfly on a tile held as 32 consecutive elements per
+// lane in LPT lanes (lane q of the tile holds elements 32q .. 32q+31).
+// Strides h = 1..16 are in registers, h = 32, 64, 128 pair lane q with
+// q ^ (h/32).  Each output is exactly the oracle's a_j + a_{j+h} or
+// a_j - a_{j+h} (Methodology 1).
+// --------------------------------------------------------------------------
+template <int LPT>
+__device__ __forceinline__ void fwht_tile(float (&a)[kLaneElems], int q) {
+#pragma unroll
+  for (int h = 1; h < kLaneElems; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < kLaneElems; j++) {
+      if (j & h) continue;
+      float lo = a[j], hi = a[j + h];
+      a[j] = lo + hi;
+      a[j + h] = lo - hi;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPT; m <<= 1) {
+    const bool upper = (q & m) != 0;
+#pragma unroll
+    for (int j = 0; j < kLaneElems; j++) {
+      float other = __shfl_xor(a[j], m);
+      a[j] = upper ? (other - a[j]) : (a[j] + other);
+    }
+  }
+}
+
+// read 32 bits starting at bit `pos` of an LDS word array (needs one guard word)
+__device__ __forceinline__ uint32_t lds_read32(const uint32_t* w, uint32_t pos) {
+  uint32_t i = pos >> 5, s = pos & 31u;
+  uint64_t v = ((uint64_t)w[i + 1] << 32) | w[i];
+  return (uint32_t)(v >> s);
+}
+
+// OR an nbits-wide field (nbits <= 32) into an LDS bit array at bit `pos`
+__device__ __forceinline__ void lds_or_bits(uint32_t* w, uint32_t pos, uint32_t field, uint32_t nbits) {
+  uint32_t i = pos >> 5, s = pos & 31u;
+  atomicOr(&w[i], field << s);
+  if (s + nbits > 32u) atomicOr(&w[i + 1], field >> (32u - s));
+}
+
+}  // namespace hq

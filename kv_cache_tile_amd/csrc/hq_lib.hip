@@ -1,0 +1,706 @@
+// hq_lib.hip — HyperQuant encode/decode kernels for gfx950 and the C ABI of
+// libhq.so (declared in include/hq.h).
+//
+// Method: "HyperQuant: A Rate-Distortion-Optimal Quantization Pipeline for
+// Large Language and Diffusion Models", gist.science explainer, section
+// "Methodology: The HyperQuant Pipeline", components 1-4 (RHT, lattice,
+// bit-stripping + Rice, KV dither).
+//
+// Encode: one workgroup = one chunk of 64 tiles at a time (persistent
+// workgroups take chunks from an atomic ticket).  Lane q of a tile holds its
+// elements 32q..32q+31: load, sign flip, butterfly, scale, lattice search,
+// symbols and the Rice parameter are all in registers; tile lengths are
+// scanned within the chunk, the chunk's word offset in the stream comes from
+// a decoupled look-back over earlier chunks' published sizes, and the bits
+// are packed into LDS and written out with coalesced stores.
+// Decode: one workgroup per chunk (grid-strided): payload staged in LDS, one
+// lane per tile parses its Rice codewords into LDS, then every lane rebuilds
+// its 32 elements, runs the butterfly and stores.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "hq.h"
+#include "hq_device.h"
+
+using namespace hq;
+
+namespace {
+
+struct RateEntry { uint8_t lattice, dither; uint16_t tile; uint16_t bps_q; uint32_t c_bits; };
+#include "hq_rate_table.inc"   // kRateTable[], generated from rate_table.json
+
+constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
+constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+
+// --------------------------------------------------------------------------
+// Encode kernel
+// --------------------------------------------------------------------------
+template <int LAT, int N, bool BF16, bool DITHER>
+__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems))
+encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
+              uint32_t key_sign, uint32_t key_dither, A2Consts a2,
+              uint32_t* __restrict__ payload, uint64_t cap_words,
+              uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
+              uint32_t* __restrict__ chunk_off, uint32_t* __restrict__ status,
+              uint32_t* __restrict__ ws, uint32_t stage_words) {
+  constexpr int LPT = N / kLaneElems;                       // lanes per tile
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
+  constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;   // coset bits per lane
+  constexpr uint32_t B = CB_LANE * LPT;                     // coset bits per tile
+
+  extern __shared__ uint32_t smem[];
+  uint32_t* stage = smem;                                   // [stage_words]
+  uint32_t* tile_len = smem + stage_words;                  // [64]
+  uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
+  uint32_t* misc = tile_off + kChunkTiles;                  // [4]
+
+  const int tid = threadIdx.x;
+  const int tau = tid / LPT;
+  const int q = tid % LPT;
+  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);
+
+  // sign diagonal entries of this lane's 32 positions (Methodology 1)
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+
+  if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t epoch = misc[2] & kEpochMask;
+
+  for (;;) {
+    if (tid == 0) {
+      uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      misc[0] = tk;
+      if ((uint64_t)tk == C + gridDim.x - 1) {               // last ticket: all taken, reset for next call
+        __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    const uint64_t chunk = misc[0];
+    if (chunk >= C) break;
+
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const bool active = t < T;
+
+    // ---- load + sign (bf16 -> fp32 is exact) ----
+    float a[kLaneElems];
+    if (active) {
+      const uint64_t base = t * N + (uint64_t)q * kLaneElems;
+      if constexpr (BF16) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          uint4 w = p[v];
+          uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int h = 0; h < 4; h++) {
+            a[v * 8 + 2 * h] = as_f(ww[h] << 16);
+            a[v * 8 + 2 * h + 1] = as_f(ww[h] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
+#pragma unroll
+        for (int v = 0; v < 8; v++) {
+          float4 w = p[v];
+          a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ (((sgn >> i) & 1u) << 31));
+
+    // ---- RHT: butterfly, then 1/sqrt(n) ----
+    fwht_tile<LPT>(a, q);
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
+
+    // ---- tile energy: pairwise tree over the tile, step = bf16(rms * c) ----
+    float sq[kLaneElems];
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) sq[i] = a[i] * a[i];
+#pragma unroll
+    for (int m = kLaneElems; m > 1; m >>= 1) {
+#pragma unroll
+      for (int i = 0; i < m / 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+    }
+    float ss = sq[0];
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) ss = ss + __shfl_xor(ss, m);
+    bool nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
+    float s = 0.0f;
+    uint32_t sbits = 0;
+    if (!nonfinite) {
+      float rms = sqrtf(ss * inv_n);
+      float r = rms * c;
+      sbits = bf16_rne_bits(r);
+      if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
+      else if ((sbits & 0x7F80u) == 0) sbits = 0;
+      s = as_f(sbits << 16);
+    }
+    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = nonfinite ? 0.0f : a[i] * inv;
+
+    // ---- KV: add the dither (Methodology 4) ----
+    if constexpr (DITHER) {
+      const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
+#pragma unroll
+      for (int b = 0; b < BPL; b++) {
+        float u[D];
+        dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), u, a2);
+#pragma unroll
+        for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + u[i];
+      }
+    }
+
+    // ---- nearest lattice point, strip, zigzag ----
+    uint32_t sym[kLaneElems];
+    uint32_t cb = 0;
+#pragma unroll
+    for (int b = 0; b < BPL; b++) {
+      int32_t d[D];
+      uint32_t p;
+      nearest<LAT>(&a[b * D], d, p, a2);
+      block_symbols<LAT>(d, &sym[b * D]);
+      cb |= p << b;
+    }
+
+    // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
+    uint32_t S[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> k;
+      S[k] = acc;
+    }
+    uint32_t best_k = 0, best_c = 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t tot = S[k];
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+      uint32_t cost = tot + (uint32_t)N * (1u + k);
+      if (cost < best_c) { best_c = cost; best_k = k; }
+    }
+    const uint32_t k = best_k;
+    uint32_t lane_bits = 0;
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++) if (kk == (int)k) lane_bits = S[kk];
+    lane_bits += (uint32_t)kLaneElems * (1u + k);
+    // exclusive prefix of lane lengths inside the tile
+    uint32_t incl = lane_bits;
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) {
+      uint32_t v = __shfl_up(incl, m, LPT);
+      if (q >= m) incl += v;
+    }
+    const uint32_t lane_excl = incl - lane_bits;
+    const uint32_t tlen = B + best_c;
+    if (q == 0) tile_len[tau] = active ? tlen : 0u;
+    __syncthreads();
+
+    // ---- chunk scan: bit offset of every tile inside the chunk ----
+    if (tid < kChunkTiles) {
+      uint32_t v = tile_len[tid], inc = v;
+#pragma unroll
+      for (int m = 1; m < kChunkTiles; m <<= 1) {
+        uint32_t o = __shfl_up(inc, m, kChunkTiles);
+        if (tid >= m) inc += o;
+      }
+      tile_off[tid] = inc - v;
+      if (tid == kChunkTiles - 1) misc[1] = inc;
+    }
+    __syncthreads();
+    const uint32_t total_bits = misc[1];
+    uint32_t W = (total_bits + 31u) >> 5;
+    const bool fits = W <= stage_words - 2;
+
+    // publish this chunk's size early so later chunks can look back past it
+    if (tid == 0) {
+      uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
+      __hip_atomic_store(&look[chunk], (tag << 32) | W, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (uint32_t i = tid; i < W + 2 && i < stage_words; i += blockDim.x) stage[i] = 0u;
+    __syncthreads();
+
+    // ---- pack: coset bits, then Rice codewords (q zeros, one, k bits LSB first) ----
+    if (active && fits) {
+      uint32_t pos = tile_off[tau];
+      if constexpr (CB_LANE > 0) lds_or_bits(stage, pos + (uint32_t)q * CB_LANE, cb, CB_LANE);
+      pos += B + lane_excl;
+      const uint32_t rmask = (1u << k) - 1u;
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) {
+        const uint32_t qv = sym[i] >> k;
+        const uint32_t field = ((sym[i] & rmask) << 1) | 1u;
+        pos += qv;
+        lds_or_bits(stage, pos, field, k + 1u);
+        pos += 1u + k;
+      }
+    }
+    __syncthreads();
+
+    // ---- decoupled look-back for the chunk's word offset ----
+    if (tid == 0) {
+      uint32_t excl = 0;
+      if (chunk > 0) {
+        uint64_t j = chunk - 1;
+        for (;;) {
+          uint64_t v = __hip_atomic_load(&look[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+          uint32_t hi = (uint32_t)(v >> 32);
+          if ((hi >> 2) != epoch || (hi & 3u) == 0) { __builtin_amdgcn_s_sleep(1); continue; }
+          excl += (uint32_t)v;
+          if ((hi & 3u) == kFlagIncl) break;
+          j--;
+        }
+        uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
+        __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      misc[3] = excl;
+      chunk_off[chunk] = excl;
+      if (chunk == C - 1) chunk_off[C] = excl + W;
+      if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+    }
+    __syncthreads();
+    const uint32_t excl = misc[3];
+    if (fits && (uint64_t)excl + W <= cap_words) {
+      for (uint32_t i = tid; i < W; i += blockDim.x) payload[excl + i] = stage[i];
+    }
+    if (active && q == 0) {
+      step_out[t] = (uint16_t)sbits;
+      meta_out[t] = (uint16_t)((tlen << 3) | k);
+      if (nonfinite) atomicOr(status, HQ_FLAG_NONFINITE);
+    }
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------------------
+// Decode kernel
+// --------------------------------------------------------------------------
+template <int LAT, int N, bool BF16, bool DITHER>
+__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems))
+decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
+              const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
+              const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
+              uint32_t key_sign, uint32_t key_dither, A2Consts a2, void* __restrict__ out,
+              uint32_t* __restrict__ status, uint32_t stage_words) {
+  constexpr int LPT = N / kLaneElems;
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr int BPL = kLaneElems / D;
+  constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
+  constexpr uint32_t B = CB_LANE * LPT;
+  constexpr uint32_t CBW = (B + 31) / 32 + 1;              // coset words per tile (+1 guard)
+  constexpr uint32_t SYMW = N / 2 + 1;                      // u16 symbols, padded row (words)
+
+  extern __shared__ uint32_t smem[];
+  uint32_t* stage = smem;                                   // [stage_words]
+  uint32_t* symw = stage + stage_words;                     // [64][SYMW]
+  uint32_t* cosw = symw + kChunkTiles * SYMW;               // [64][CBW]
+  uint32_t* tile_off = cosw + kChunkTiles * CBW;            // [64]
+  uint32_t* tile_bad = tile_off + kChunkTiles;              // [64]
+  uint16_t* sym16 = reinterpret_cast<uint16_t*>(symw);
+
+  const int tid = threadIdx.x;
+  const int tau = tid / LPT;
+  const int q = tid % LPT;
+
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+
+  for (uint64_t chunk = blockIdx.x; chunk < C; chunk += gridDim.x) {
+    const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
+    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) + 2 <= stage_words;
+    const uint32_t W = range_ok ? (uint32_t)(w1 - w0) : 0u;
+    for (uint32_t i = tid; i < W; i += blockDim.x) stage[i] = payload[w0 + i];
+    if (tid < 2) stage[W + tid] = 0u;
+
+    // tile offsets inside the chunk
+    if (tid < kChunkTiles) {
+      const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
+      const uint32_t len = tt < T ? (uint32_t)(meta[tt] >> 3) : 0u;
+      uint32_t inc = len;
+#pragma unroll
+      for (int m = 1; m < kChunkTiles; m <<= 1) {
+        uint32_t o = __shfl_up(inc, m, kChunkTiles);
+        if (tid >= m) inc += o;
+      }
+      tile_off[tid] = inc - len;
+      const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
+      const bool chunk_ok = range_ok && ((total + 31u) >> 5) == W;
+      tile_bad[tid] = chunk_ok ? 0u : 1u;
+    }
+    __syncthreads();
+
+    // ---- parse: one lane per tile ----
+    if (tid < kChunkTiles) {
+      const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
+      if (tt < T && !tile_bad[tid]) {
+        const uint32_t m = meta[tt];
+        const uint32_t len = m >> 3, k = m & 7u;
+        const uint32_t start = tile_off[tid], end = start + len;
+        uint32_t pos = start;
+        bool bad = len < B + (uint32_t)N;                  // every codeword has at least one bit
+        uint32_t* cw = cosw + tid * CBW;
+        if (!bad && B > 0) {
+#pragma unroll
+          for (uint32_t w = 0; w < (B + 31) / 32; w++) {
+            const uint32_t nb = (B - 32 * w) < 32 ? (B - 32 * w) : 32;
+            uint32_t v = lds_read32(stage, pos);
+            cw[w] = nb == 32 ? v : (v & ((1u << nb) - 1u));
+            pos += nb;
+          }
+        }
+        uint16_t* srow = sym16 + tid * (2 * SYMW);
+        const uint32_t rmask = (1u << k) - 1u;
+        for (int i = 0; i < N && !bad; i++) {
+          uint32_t qv = 0;
+          for (;;) {
+            if (pos >= end) { bad = true; break; }
+            const uint32_t w = lds_read32(stage, pos);
+            if (w != 0u) {
+              const uint32_t z = __builtin_ctz(w);
+              qv += z;
+              pos += z + 1u;
+              break;
+            }
+            qv += 32u;
+            pos += 32u;
+          }
+          if (bad || pos > end) { bad = true; break; }
+          const uint32_t r = lds_read32(stage, pos) & rmask;
+          pos += k;
+          const uint32_t u = (qv << k) | r;
+          if (u > 0xFFFFu) { bad = true; break; }
+          srow[i] = (uint16_t)u;
+        }
+        if (bad || pos != end) tile_bad[tid] = 1u;
+      }
+    }
+    __syncthreads();
+
+    // ---- rebuild: points, (dither), step, inverse RHT, store ----
+    {
+      const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+      if (t < T) {
+        const bool bad = tile_bad[tau] != 0u;
+        if (bad && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
+        const float s = bad ? 0.0f : as_f((uint32_t)step[t] << 16);
+        const uint16_t* srow = sym16 + tau * (2 * SYMW) + q * kLaneElems;
+        const uint32_t* cw = cosw + tau * CBW;
+        float a[kLaneElems];
+#pragma unroll
+        for (int b = 0; b < BPL; b++) {
+          uint32_t u[D];
+#pragma unroll
+          for (int i = 0; i < D; i++) u[i] = bad ? 0u : (uint32_t)srow[b * D + i];
+          uint32_t p = 0;
+          if constexpr (LatticeTraits<LAT>::coset) {
+            const uint32_t bit = (uint32_t)q * CB_LANE + (uint32_t)b;
+            p = bad ? 0u : (cw[bit >> 5] >> (bit & 31u)) & 1u;
+          }
+          float pt[D];
+          block_point<LAT>(u, p, pt, a2);
+          if constexpr (DITHER) {
+            float du[D];
+            dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
+#pragma unroll
+            for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
+          }
+#pragma unroll
+          for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
+        }
+        fwht_tile<LPT>(a, q);
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i] * inv_sqrtn) ^ (((sgn >> i) & 1u) << 31));
+        const uint64_t base = t * N + (uint64_t)q * kLaneElems;
+        if constexpr (BF16) {
+          uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; h++)
+              w[h] = bf16_rne_bits(a[v * 8 + 2 * h]) | (bf16_rne_bits(a[v * 8 + 2 * h + 1]) << 16);
+            p[v] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        } else {
+          float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base);
+#pragma unroll
+          for (int v = 0; v < 8; v++) p[v] = make_float4(a[v * 4], a[v * 4 + 1], a[v * 4 + 2], a[v * 4 + 3]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------------------
+// Host side
+// --------------------------------------------------------------------------
+uint32_t lattice_dim(uint32_t lat) {
+  switch (lat) { case HQ_Z: return 1; case HQ_A2: return 2; case HQ_D4: return 4; case HQ_E8: return 8; }
+  return 0;
+}
+
+uint32_t host_pcg(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+// stream keys of the sign diagonal ("SIGN") and of the dither ("DITH")
+uint32_t derive_key(uint64_t seed, uint32_t domain) {
+  return host_pcg(host_pcg((uint32_t)(seed & 0xFFFFFFFFu) ^ domain) ^ (uint32_t)(seed >> 32));
+}
+
+bool rate_constant(uint32_t lat, uint32_t tile, uint32_t dither, float bps, float* c) {
+  float q4 = bps * 4.0f;
+  if (!(q4 == floorf(q4))) return false;
+  uint32_t bq = (uint32_t)q4;
+  for (const RateEntry& e : kRateTable) {
+    if (e.lattice == lat && e.tile == tile && e.dither == dither && e.bps_q == bq) {
+      memcpy(c, &e.c_bits, 4);
+      return true;
+    }
+  }
+  return false;
+}
+
+// Worst-case tile length: |t|_2 <= sqrt(n)/c' (c' = c less the bf16 rounding
+// margin), so sum|t_i| <= n/c'; every code integer is within 3/2 of its t_i,
+// so the symbols sum to at most 2n/c' + 3n (+2n with the dither); the chosen
+// k codes at most as long as any fixed k.
+uint32_t tile_bound_bits(uint32_t n, uint32_t lat, uint32_t dither, float c) {
+  double cp = (double)c * (1.0 - 1.0 / 128.0);
+  double S = 2.0 * n / cp + 3.0 * n + (dither ? 2.0 * n : 0.0);
+  double best = 1e300;
+  for (int k = 0; k < 8; k++) {
+    double L = floor(S / (double)(1u << k)) + (double)n * (1 + k);
+    if (L < best) best = L;
+  }
+  uint32_t d = lattice_dim(lat);
+  double B = (lat == HQ_E8 || lat == HQ_A2) ? (double)(n / d) : 0.0;
+  double bound = B + best;
+  return bound > 8191.0 ? 0u : (uint32_t)bound;
+}
+
+struct Plan {
+  uint64_t T, C, cap_words, ws_bytes;
+  uint32_t bound, stage_words;
+  float c;
+};
+
+int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat, float bps,
+              uint32_t kv, Plan* P) {
+  if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_EINVAL;
+  if (tile != 64 && tile != 128 && tile != 256) return HQ_EINVAL;
+  if (!lattice_dim(lat) || kv > 1) return HQ_EINVAL;
+  if (rows == 0 || cols == 0 || cols % tile) return HQ_EINVAL;
+  if (rows > (1ull << 32) || cols > (1ull << 32) || rows * cols >= (1ull << 32)) return HQ_EINVAL;
+  float c;
+  if (!rate_constant(lat, tile, kv, bps, &c)) return HQ_EINVAL;
+  uint32_t bound = tile_bound_bits(tile, lat, kv, c);
+  if (!bound) return HQ_EINVAL;
+  P->T = rows * cols / tile;
+  P->C = (P->T + kChunkTiles - 1) / kChunkTiles;
+  P->bound = bound;
+  P->c = c;
+  P->stage_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 2;
+  P->cap_words = (P->T * bound + 31) / 32 + P->C;
+  P->ws_bytes = 8 + 8 * P->C;
+  return HQ_OK;
+}
+
+// ---- dispatch tables -------------------------------------------------------
+using EncFn = void (*)(const void*, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t, A2Consts,
+                       uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*, uint32_t);
+using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
+                       uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t*, uint32_t);
+
+template <int LAT, int N>
+EncFn enc_pick(bool bf16, bool dither) {
+  if (bf16) return dither ? encode_kernel<LAT, N, true, true> : encode_kernel<LAT, N, true, false>;
+  return dither ? encode_kernel<LAT, N, false, true> : encode_kernel<LAT, N, false, false>;
+}
+template <int LAT, int N>
+DecFn dec_pick(bool bf16, bool dither) {
+  if (bf16) return dither ? decode_kernel<LAT, N, true, true> : decode_kernel<LAT, N, true, false>;
+  return dither ? decode_kernel<LAT, N, false, true> : decode_kernel<LAT, N, false, false>;
+}
+template <int LAT>
+EncFn enc_by_tile(uint32_t n, bool bf16, bool dither) {
+  if (n == 64) return enc_pick<LAT, 64>(bf16, dither);
+  if (n == 128) return enc_pick<LAT, 128>(bf16, dither);
+  return enc_pick<LAT, 256>(bf16, dither);
+}
+template <int LAT>
+DecFn dec_by_tile(uint32_t n, bool bf16, bool dither) {
+  if (n == 64) return dec_pick<LAT, 64>(bf16, dither);
+  if (n == 128) return dec_pick<LAT, 128>(bf16, dither);
+  return dec_pick<LAT, 256>(bf16, dither);
+}
+EncFn enc_fn(uint32_t lat, uint32_t n, bool bf16, bool dither) {
+  switch (lat) {
+    case HQ_Z: return enc_by_tile<1>(n, bf16, dither);
+    case HQ_A2: return enc_by_tile<2>(n, bf16, dither);
+    case HQ_D4: return enc_by_tile<4>(n, bf16, dither);
+    default: return enc_by_tile<8>(n, bf16, dither);
+  }
+}
+DecFn dec_fn(uint32_t lat, uint32_t n, bool bf16, bool dither) {
+  switch (lat) {
+    case HQ_Z: return dec_by_tile<1>(n, bf16, dither);
+    case HQ_A2: return dec_by_tile<2>(n, bf16, dither);
+    case HQ_D4: return dec_by_tile<4>(n, bf16, dither);
+    default: return dec_by_tile<8>(n, bf16, dither);
+  }
+}
+
+uint32_t decode_lds_words(uint32_t n, uint32_t lat, uint32_t stage_words) {
+  uint32_t d = lattice_dim(lat);
+  uint32_t B = (lat == HQ_E8 || lat == HQ_A2) ? n / d : 0;
+  uint32_t cbw = (B + 31) / 32 + 1;
+  return stage_words + kChunkTiles * (n / 2 + 1) + kChunkTiles * cbw + 2 * kChunkTiles;
+}
+
+int grid_for(const void* fn, int block, size_t lds, uint64_t chunks, int* grid) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HQ_EHIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return HQ_EHIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, block, lds) != hipSuccess) return HQ_EHIP;
+  if (per < 1) return HQ_EINVAL;
+  uint64_t g = (uint64_t)cus * (uint64_t)per;
+  if (g > chunks) g = chunks;
+  *grid = (int)(g < 1 ? 1 : g);
+  return HQ_OK;
+}
+
+int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat,
+              float bps, uint64_t seed, uint32_t kv, uint32_t* payload, uint64_t cap, uint16_t* step,
+              uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* ws, uint64_t ws_bytes,
+              void* stream) {
+  Plan P;
+  int rc = make_plan(dtype, rows, cols, tile, lat, bps, kv, &P);
+  if (rc) return rc;
+  if (!x || !payload || !step || !meta || !chunk_off || !status || !ws) return HQ_EINVAL;
+  if (cap < P.cap_words || ws_bytes < P.ws_bytes) return HQ_ENOSPC;
+  if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
+  EncFn fn = enc_fn(lat, tile, dtype == HQ_BF16, kv != 0);
+  const int block = kChunkTiles * (int)(tile / kLaneElems);
+  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4) * 4;
+  int grid;
+  rc = grid_for((const void*)fn, block, lds, P.C, &grid);
+  if (rc) return rc;
+  A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
+  const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
+  const float inv_n = 1.0f / (float)tile;   // exact: tile is a power of two
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, x, P.T, P.C, P.c, inv_sqrtn, inv_n,
+                     derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, payload, cap, step, meta,
+                     chunk_off, status, (uint32_t*)ws, P.stage_words);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
+              const uint32_t* chunk_off, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+              uint32_t lat, float bps, uint64_t seed, uint32_t kv, void* out, uint32_t* status, void* stream) {
+  Plan P;
+  int rc = make_plan(dtype, rows, cols, tile, lat, bps, kv, &P);
+  if (rc) return rc;
+  if (!payload || !step || !meta || !chunk_off || !status || !out) return HQ_EINVAL;
+  if ((uintptr_t)out & 15) return HQ_EINVAL;
+  DecFn fn = dec_fn(lat, tile, dtype == HQ_BF16, kv != 0);
+  const int block = kChunkTiles * (int)(tile / kLaneElems);
+  const size_t lds = (size_t)decode_lds_words(tile, lat, P.stage_words) * 4;
+  int grid;
+  rc = grid_for((const void*)fn, block, lds, P.C, &grid);
+  if (rc) return rc;
+  A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
+  const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, payload, payload_words, step, meta,
+                     chunk_off, P.T, P.C, inv_sqrtn, derive_key(seed, 0x5349474Eu),
+                     derive_key(seed, 0x44495448u), a2, out, status, P.stage_words);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+extern "C" {
+
+int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice, float bps,
+            uint32_t kv, uint64_t* tiles, uint64_t* chunks, uint64_t* payload_cap_words,
+            uint64_t* workspace_bytes, uint32_t* tile_bound, float* rate_c) {
+  Plan P;
+  int rc = make_plan(dtype, rows, cols, tile, lattice, bps, kv, &P);
+  if (rc) return rc;
+  if (tiles) *tiles = P.T;
+  if (chunks) *chunks = P.C;
+  if (payload_cap_words) *payload_cap_words = P.cap_words;
+  if (workspace_bytes) *workspace_bytes = P.ws_bytes;
+  if (tile_bound) *tile_bound = P.bound;
+  if (rate_c) *rate_c = P.c;
+  return HQ_OK;
+}
+
+int hq_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+              float bps, uint64_t seed, uint32_t* payload, uint64_t payload_cap_words, uint16_t* step,
+              uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* workspace,
+              uint64_t workspace_bytes, void* stream) {
+  return do_encode(x, dtype, rows, cols, tile, lattice, bps, seed, 0, payload, payload_cap_words, step, meta,
+                   chunk_off, status, workspace, workspace_bytes, stream);
+}
+
+int hq_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
+              const uint32_t* chunk_off, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+              uint32_t lattice, float bps, uint64_t seed, void* x_out, uint32_t* status, void* stream) {
+  return do_decode(payload, payload_words, step, meta, chunk_off, dtype, rows, cols, tile, lattice, bps, seed,
+                   0, x_out, status, stream);
+}
+
+int hq_kv_encode(const void* x, uint32_t dtype, uint64_t tokens, uint32_t head_dim, uint32_t lattice,
+                 float bps, uint64_t seed, uint32_t* payload, uint64_t payload_cap_words, uint16_t* step,
+                 uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* workspace,
+                 uint64_t workspace_bytes, void* stream) {
+  return do_encode(x, dtype, tokens, head_dim, head_dim, lattice, bps, seed, 1, payload, payload_cap_words,
+                   step, meta, chunk_off, status, workspace, workspace_bytes, stream);
+}
+
+int hq_kv_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
+                 const uint32_t* chunk_off, uint32_t dtype, uint64_t tokens, uint32_t head_dim,
+                 uint32_t lattice, float bps, uint64_t seed, void* x_out, uint32_t* status, void* stream) {
+  return do_decode(payload, payload_words, step, meta, chunk_off, dtype, tokens, head_dim, head_dim, lattice,
+                   bps, seed, 1, x_out, status, stream);
+}
+
+const char* hq_strerror(int code) {
+  switch (code) {
+    case HQ_OK: return "ok";
+    case HQ_EINVAL: return "invalid argument (shape, tile, lattice, dtype, bps or alignment)";
+    case HQ_EHIP: return "HIP runtime or launch error";
+    case HQ_ENOSPC: return "buffer capacity below the planned size";
+    case HQ_ENONFINITE: return "non-finite input";
+    case HQ_ECORRUPT: return "corrupt compressed stream";
+  }
+  return "unknown error";
+}
+
+uint32_t hq_version(void) { return (1u << 16) | 0u; }
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+"""Thin Python binding of libhq.so (argument marshalling only).
+
+Every step of the codec runs in the library's HIP kernels; torch provides the
+device memory and the stream.  Function names follow the C ABI (include/hq.h):
+``encode`` / ``decode`` (weights) and ``kv_encode`` / ``kv_decode`` (KV cache).
+Importing this module on a machine without the built library or without a GPU
+raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhq.so")
+
+LATTICES = {"Z": 1, "A2": 2, "D4": 4, "E8": 8}
+F32, BF16 = 0, 1
+FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE = 1, 2, 4
+CHUNK_TILES = 64
+
+EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
+           "hq_version")
+
+
+class HQError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise HQError(f"{LIB_PATH} is missing: run `python -m kv_cache_tile_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        u32, u64, vp, f32 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_float
+        P = ctypes.POINTER
+        L.hq_plan.argtypes = [u32, u64, u64, u32, u32, f32, u32, P(u64), P(u64), P(u64), P(u64), P(u32), P(f32)]
+        L.hq_plan.restype = ctypes.c_int
+        enc = [vp, u32, u64, u64, u32, u32, f32, u64, vp, u64, vp, vp, vp, vp, vp, u64, vp]
+        L.hq_encode.argtypes = enc
+        L.hq_encode.restype = ctypes.c_int
+        L.hq_kv_encode.argtypes = [vp, u32, u64, u32, u32, f32, u64, vp, u64, vp, vp, vp, vp, vp, u64, vp]
+        L.hq_kv_encode.restype = ctypes.c_int
+        L.hq_decode.argtypes = [vp, u64, vp, vp, vp, u32, u64, u64, u32, u32, f32, u64, vp, vp, vp]
+        L.hq_decode.restype = ctypes.c_int
+        L.hq_kv_decode.argtypes = [vp, u64, vp, vp, vp, u32, u64, u32, u32, f32, u64, vp, vp, vp]
+        L.hq_kv_decode.restype = ctypes.c_int
+        L.hq_strerror.argtypes = [ctypes.c_int]
+        L.hq_strerror.restype = ctypes.c_char_p
+        L.hq_version.argtypes = []
+        L.hq_version.restype = u32
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise HQError(f"hq error {rc}: {lib().hq_strerror(rc).decode()}")
+
+
+@dataclass
+class Plan:
+    tiles: int
+    chunks: int
+    payload_cap_words: int
+    workspace_bytes: int
+    tile_bound_bits: int
+    rate_constant: float
+
+
+def plan(dtype: int, rows: int, cols: int, tile: int, lattice: str, bps: float, kv: bool = False) -> Plan:
+    vals = [ctypes.c_uint64() for _ in range(4)]
+    tb = ctypes.c_uint32()
+    rc_ = ctypes.c_float()
+    _check(lib().hq_plan(dtype, rows, cols, tile, LATTICES[lattice], float(bps), int(kv),
+                         *[ctypes.byref(v) for v in vals], ctypes.byref(tb), ctypes.byref(rc_)))
+    return Plan(vals[0].value, vals[1].value, vals[2].value, vals[3].value, tb.value, rc_.value)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise HQError(f"unsupported dtype {t}")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_workspaces: dict = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised encode workspace, reused across calls on a device
+    (calls that overlap in time on different streams must not share one)."""
+    device = torch.device(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+@dataclass
+class HQTensor:
+    """Compressed tensor: device buffers plus the parameters needed to decode."""
+    payload: torch.Tensor     # int32 words (capacity; valid prefix = chunk_off[-1])
+    step: torch.Tensor        # int16 bf16 step bits per tile
+    meta: torch.Tensor        # int16 (len << 3 | k) per tile
+    chunk_off: torch.Tensor   # int32 [chunks + 1]
+    status: torch.Tensor      # int32 [1] flags
+    shape: tuple
+    dtype: torch.dtype
+    tile: int
+    lattice: str
+    bps: float
+    seed: int
+    kv: bool = False
+    extra: dict = field(default_factory=dict)
+
+    def payload_words(self) -> int:
+        return int(self.chunk_off[-1].item())
+
+    def flags(self) -> int:
+        return int(self.status.item())
+
+    def bits_payload(self) -> int:
+        """coset + Rice bits (sum of the tile lengths)."""
+        return int((self.meta.to(torch.int32) & 0xFFFF).__rshift__(3).sum().item())
+
+    def bits_total(self) -> int:
+        """everything stored: payload words, step and meta per tile, chunk offsets."""
+        return 32 * self.payload_words() + 32 * self.step.numel() + 32 * self.chunk_off.numel()
+
+
+def _alloc(p: Plan, device) -> tuple:
+    payload = torch.empty(p.payload_cap_words, dtype=torch.int32, device=device)
+    step = torch.empty(p.tiles, dtype=torch.int16, device=device)
+    meta = torch.empty(p.tiles, dtype=torch.int16, device=device)
+    off = torch.empty(p.chunks + 1, dtype=torch.int32, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    return payload, step, meta, off, status
+
+
+def encode(x: torch.Tensor, tile: int = 128, lattice: str = "E8", bps: float = 4.0, seed: int = 0,
+           out: HQTensor | None = None, zero_status: bool = True) -> HQTensor:
+    """Encode a 2-D (or any, viewed as [-1, last]) weight tensor on its GPU.
+    With `out`, its buffers are reused (and its status word is cleared first
+    unless zero_status is False, in which case flags accumulate)."""
+    if not x.is_cuda:
+        raise HQError("encode needs a GPU tensor")
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    dt = _dtype_code(x2.dtype)
+    rows, cols = x2.shape
+    p = plan(dt, rows, cols, tile, lattice, bps, kv=False)
+    bufs = (out.payload, out.step, out.meta, out.chunk_off, out.status) if out is not None else _alloc(p, x.device)
+    payload, step, meta, off, status = bufs
+    if out is not None and zero_status:
+        status.zero_()
+    ws = workspace(x.device, p.workspace_bytes)
+    _check(lib().hq_encode(x2.data_ptr(), dt, rows, cols, tile, LATTICES[lattice], float(bps), seed,
+                           payload.data_ptr(), payload.numel(), step.data_ptr(), meta.data_ptr(),
+                           off.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    if out is not None:
+        return out
+    return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float(bps),
+                    seed, False)
+
+
+def decode(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    rows = 1
+    for s in h.shape[:-1]:
+        rows *= s
+    cols = h.shape[-1]
+    if out is None:
+        out = torch.empty(h.shape, dtype=h.dtype, device=h.payload.device)
+    dt = _dtype_code(h.dtype)
+    fn = lib().hq_kv_decode if h.kv else lib().hq_decode
+    if h.kv:
+        rc = fn(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
+                h.chunk_off.data_ptr(), dt, rows, cols, LATTICES[h.lattice], h.bps, h.seed, out.data_ptr(),
+                h.status.data_ptr(), _stream(out.device))
+    else:
+        rc = fn(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
+                h.chunk_off.data_ptr(), dt, rows, cols, h.tile, LATTICES[h.lattice], h.bps, h.seed,
+                out.data_ptr(), h.status.data_ptr(), _stream(out.device))
+    _check(rc)
+    return out
+
+
+def kv_encode(x: torch.Tensor, lattice: str = "E8", bps: float = 2.0, seed: int = 0,
+              out: HQTensor | None = None) -> HQTensor:
+    """Encode KV vectors: x[..., head_dim], one tile per (token, head) vector, dithered."""
+    if not x.is_cuda:
+        raise HQError("kv_encode needs a GPU tensor")
+    hd = x.shape[-1]
+    x2 = x.reshape(-1, hd).contiguous()
+    dt = _dtype_code(x2.dtype)
+    tokens = x2.shape[0]
+    p = plan(dt, tokens, hd, hd, lattice, bps, kv=True)
+    bufs = (out.payload, out.step, out.meta, out.chunk_off, out.status) if out is not None else _alloc(p, x.device)
+    payload, step, meta, off, status = bufs
+    if out is not None:
+        status.zero_()
+    ws = workspace(x.device, p.workspace_bytes)
+    _check(lib().hq_kv_encode(x2.data_ptr(), dt, tokens, hd, LATTICES[lattice], float(bps), seed,
+                              payload.data_ptr(), payload.numel(), step.data_ptr(), meta.data_ptr(),
+                              off.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    if out is not None:
+        return out
+    return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, hd, lattice, float(bps), seed,
+                    True)
+
+
+def kv_decode(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    if not h.kv:
+        raise HQError("not a KV tensor")
+    return decode(h, out)

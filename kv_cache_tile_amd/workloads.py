@@ -125,3 +125,22 @@ def codec_seed(cfg: int, layer: int = 0, which: str = "K") -> int:
     if cfg == 3:
         return 3 if which == "K" else 3 + (1 << 32)
     return cfg
+
+
+def dit_layer_device(rows: int, cols: int, layer: int, device, std: float = 0.02,
+                     p_out: float = 0.005, nu: int = 3) -> "torch.Tensor":
+    """dit_layer's distribution drawn directly on `device` with torch's
+    generator seeded by (4, layer) — the 6.4 GB stack would take minutes to
+    draw on the host.  Student-t(nu) = N / sqrt(chi2_nu / nu).  Returns bf16."""
+    g = torch.Generator(device=device)
+    g.manual_seed((4 << 32) | layer)
+    w = std * torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32)
+    mask = torch.rand(rows, cols, generator=g, device=device) < p_out
+    z = torch.randn(rows, cols, generator=g, device=device)
+    chi = torch.zeros(rows, cols, device=device)
+    for _ in range(nu):
+        e = torch.randn(rows, cols, generator=g, device=device)
+        chi += e * e
+    t = z / torch.sqrt(chi / nu)
+    w = torch.where(mask, t, w)
+    return w.to(torch.bfloat16)

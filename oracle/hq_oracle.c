@@ -557,7 +557,66 @@ int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t
 
 /* ------------------------------------------------------------------------ */
 /* Decode: parse, rebuild lattice points, undo dither, scale, inverse RHT.  */
+/* Corrupt input (reading; the pages are silent): a tile whose n codewords  */
+/* do not span exactly its meta length, or that holds a symbol above 16     */
+/* bits, and every tile of a chunk whose word count disagrees with its      */
+/* tiles' lengths (or exceeds the capacity bound), decode to zero and are   */
+/* reported.  Valid streams never meet these conditions.                    */
 /* ------------------------------------------------------------------------ */
+
+/* parse one tile starting at bit b (reads never reach bend); 0 = ok */
+static int parse_tile(const uint32_t *w, uint64_t b, uint64_t bend, uint32_t len, uint32_t k,
+                      uint32_t n, uint32_t nb, uint32_t *cos, uint32_t *sym)
+{
+    uint64_t tb = b;
+    if (len < nb + n) return 1;
+    for (uint32_t i = 0; i < nb; i++) {
+        if (b >= bend) return 1;
+        cos[i] = get_bit(w, b++);
+    }
+    for (uint32_t i = 0; i < n; i++) {
+        uint32_t q = 0;
+        while (b < bend && !get_bit(w, b)) { q++; b++; }
+        if (b >= bend) return 1;
+        b++;                                  /* the terminating one */
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < k; j++) {
+            if (b >= bend) return 1;
+            r |= get_bit(w, b++) << j;
+        }
+        uint64_t u = ((uint64_t)q << k) | r;
+        if (u > 0xFFFFu) return 1;
+        sym[i] = (uint32_t)u;
+    }
+    return (b - tb == len) ? 0 : 1;
+}
+
+/* points -> (dither) -> step -> inverse RHT of tile t; stores at out[slot] */
+static void rebuild_tile(const hqo_params *p, uint64_t t, int bad, uint16_t step,
+                         const uint32_t *cos, const uint32_t *sym, void *out, uint64_t slot)
+{
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    float s = bad ? 0.0f : bf16_to_f32(step);
+    float v[256], xo[256];
+    uint32_t zero[8] = {0};
+    for (uint32_t blk = 0; blk < n / d; blk++) {
+        float pt[8];
+        uint32_t pc = (coset_bits_per_block(p->lattice) && !bad) ? cos[blk] : 0;
+        block_point(p->lattice, pc, bad ? zero : sym + blk * d, pt);
+        if (p->dither) {
+            float u[8];
+            hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + blk * d), u);
+            for (uint32_t i = 0; i < d; i++) pt[i] = pt[i] - u[i];
+        }
+        for (uint32_t i = 0; i < d; i++) v[blk * d + i] = pt[i] * s;
+    }
+    hqo_rht_inverse(v, n, p->seed, xo);
+    for (uint32_t i = 0; i < n; i++) {
+        if (p->dtype == HQO_F32) ((float *)out)[slot * n + i] = xo[i];
+        else ((uint16_t *)out)[slot * n + i] = bf16_rne(xo[i]);
+    }
+}
+
 int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk_off,
                const uint32_t *payload, uint64_t payload_words,
                const hqo_params *p, void *x_out)
@@ -568,62 +627,45 @@ int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk
     uint32_t nb = (n / d) * coset_bits_per_block(p->lattice);
     uint64_t T = p->rows * p->cols / n;
     uint64_t C = (T + HQO_CHUNK_TILES - 1) / HQO_CHUNK_TILES;
+    uint64_t chunk_cap = ((uint64_t)HQO_CHUNK_TILES * hqo_tile_bound_bits(p) + 31) / 32;
     int status = HQO_OK;
-    if (chunk_off[0] != 0 || chunk_off[C] > payload_words) return HQO_ECORRUPT;
+    uint32_t cos[256], sym[256];
     for (uint64_t c = 0; c < C; c++) {
         uint64_t w0 = chunk_off[c], w1 = chunk_off[c + 1];
-        if (w1 < w0 || w1 > payload_words) return HQO_ECORRUPT;
-        uint64_t b = w0 * 32, bend = w1 * 32;
         uint64_t t0 = c * HQO_CHUNK_TILES, t1 = t0 + HQO_CHUNK_TILES;
         if (t1 > T) t1 = T;
+        uint64_t total = 0;
+        for (uint64_t t = t0; t < t1; t++) total += meta[t] >> 3;
+        int chunk_bad = !(w1 >= w0 && w1 <= payload_words && w1 - w0 <= chunk_cap)
+                        || (total + 31) / 32 != w1 - w0;
+        uint64_t b = w0 * 32, bend = w1 * 32;
         for (uint64_t t = t0; t < t1; t++) {
             uint32_t len = meta[t] >> 3, k = meta[t] & 7u;
-            uint64_t tb = b;
-            int bad = 0;
-            uint32_t cos[256], sym[256];
-            for (uint32_t i = 0; i < nb; i++) {
-                if (b >= bend) { bad = 1; break; }
-                cos[i] = get_bit(payload, b++);
-            }
-            for (uint32_t i = 0; i < n && !bad; i++) {
-                uint32_t q = 0;
-                while (b < bend && !get_bit(payload, b)) { q++; b++; }
-                if (b >= bend || q > (1u << 20)) { bad = 1; break; }
-                b++;                                  /* the terminating one */
-                uint32_t r = 0;
-                for (uint32_t j = 0; j < k; j++) {
-                    if (b >= bend) { bad = 1; break; }
-                    r |= get_bit(payload, b++) << j;
-                }
-                sym[i] = (q << k) | r;
-            }
-            if (bad || b - tb != len) {
-                status = HQO_ECORRUPT;
-                memset(sym, 0, sizeof sym);
-                memset(cos, 0, sizeof cos);
-                b = tb + len;
-                if (b > bend) return HQO_ECORRUPT;
-            }
-            float s = bf16_to_f32(step[t]);
-            float v[256], xo[256];
-            for (uint32_t blk = 0; blk < n / d; blk++) {
-                float pt[8];
-                uint32_t pc = coset_bits_per_block(p->lattice) ? cos[blk] : 0;
-                block_point(p->lattice, pc, sym + blk * d, pt);
-                if (p->dither) {
-                    float u[8];
-                    hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + blk * d), u);
-                    for (uint32_t i = 0; i < d; i++) pt[i] = pt[i] - u[i];
-                }
-                for (uint32_t i = 0; i < d; i++) v[blk * d + i] = pt[i] * s;
-            }
-            hqo_rht_inverse(v, n, p->seed, xo);
-            for (uint32_t i = 0; i < n; i++) {
-                if (p->dtype == HQO_F32) ((float *)x_out)[t * n + i] = xo[i];
-                else ((uint16_t *)x_out)[t * n + i] = bf16_rne(xo[i]);
-            }
+            int bad = chunk_bad || parse_tile(payload, b, bend, len, k, n, nb, cos, sym);
+            if (bad) status = HQO_ECORRUPT;
+            rebuild_tile(p, t, bad, step[t], cos, sym, x_out, t);
+            b += len;
         }
-        if ((b + 31) / 32 != w1) status = HQO_ECORRUPT;
+    }
+    return status;
+}
+
+int hqo_decode_tiles(const uint16_t *step, const uint16_t *meta, const uint32_t *bits, uint64_t bits_words,
+                     const hqo_params *p, uint64_t t0, uint64_t t1, void *x_out)
+{
+    int rc = check_params(p);
+    if (rc) return rc;
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    uint32_t nb = (n / d) * coset_bits_per_block(p->lattice);
+    int status = HQO_OK;
+    uint32_t cos[256], sym[256];
+    uint64_t b = 0;
+    for (uint64_t t = t0; t < t1; t++) {
+        uint32_t len = meta[t - t0] >> 3, k = meta[t - t0] & 7u;
+        int bad = parse_tile(bits, b, bits_words * 32, len, k, n, nb, cos, sym);
+        if (bad) status = HQO_ECORRUPT;
+        rebuild_tile(p, t, bad, step[t - t0], cos, sym, x_out, t - t0);
+        b += len;
     }
     return status;
 }

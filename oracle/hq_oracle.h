@@ -78,6 +78,10 @@ int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk
 /* encode/decode of a tile range [t0, t1) only (sampled parity at full size):
  * tile-local outputs are the same as the full encode's; bits[] receives the
  * concatenated bitstreams of the tiles, starting at bit 0. */
+/* decode tiles [t0, t1) from their concatenated bitstreams (bit 0 = start of
+ * tile t0); x_out receives the range only ((t1 - t0) * tile elements) */
+int hqo_decode_tiles(const uint16_t *step, const uint16_t *meta, const uint32_t *bits, uint64_t bits_words,
+                     const hqo_params *p, uint64_t t0, uint64_t t1, void *x_out);
 int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t1,
                      uint16_t *step, uint16_t *meta, uint32_t *bits, uint64_t bits_cap_words);
 

@@ -81,6 +81,8 @@ def lib():
         L.hqo_encode_tiles.argtypes = [vp, P(_Params), ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp,
                                        ctypes.c_uint64]
         L.hqo_encode_tiles.restype = ctypes.c_int
+        L.hqo_decode_tiles.argtypes = [vp, vp, vp, ctypes.c_uint64, P(_Params), ctypes.c_uint64, ctypes.c_uint64, vp]
+        L.hqo_decode_tiles.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -252,3 +254,15 @@ def encode_tiles(x: np.ndarray, tile: int, lattice, c: float, seed: int, t0: int
     if st not in (OK, ENONFINITE):
         raise RuntimeError(f"oracle encode_tiles failed: {st}")
     return step, meta, bits
+
+
+def decode_tiles(step, meta, bits, rows, cols, tile, lattice, c, seed, t0, t1, dtype=F32, dither=0):
+    """Decode tiles [t0, t1) of a tensor of shape (rows, cols) from their
+    concatenated bitstreams; returns ([(t1 - t0) * tile] array, status)."""
+    p = params(rows, cols, tile, lattice, c, seed, dtype, dither)
+    out = np.zeros((t1 - t0) * tile, np.float32 if dtype == F32 else np.uint16)
+    bits = np.ascontiguousarray(bits, np.uint32)
+    st = lib().hqo_decode_tiles(_ptr(np.ascontiguousarray(step, np.uint16)),
+                                _ptr(np.ascontiguousarray(meta, np.uint16)), _ptr(bits), bits.size,
+                                ctypes.byref(p), t0, t1, _ptr(out))
+    return out, st

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact on every integer/byte output (step, meta, chunk offsets,
+payload words) and on the reconstruction (fp32 or bf16 bits).  Small cases
+span several chunks and a ragged tail; the benchmark configurations are
+checked in full where the oracle finishes in seconds and on whole sampled
+chunks otherwise (the launch is the full-size one)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hq_testutil import rate_c
+from kv_cache_tile_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from kv_cache_tile_amd import hq
+    hq.lib()                        # no fallback: a missing library fails every test
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return torch.device("cuda:0")
+
+
+def to_device(x_np, dtype):
+    """numpy fp32 -> device tensor of dtype; also returns the oracle's input
+    (fp32 array, or bf16 bit patterns as uint16)."""
+    t = torch.from_numpy(np.ascontiguousarray(x_np, np.float32))
+    if dtype == "bf16":
+        tb = t.to(torch.bfloat16)
+        return tb.to(_dev()), workloads.bf16_bits(tb)
+    return t.to(_dev()), np.ascontiguousarray(x_np, np.float32)
+
+
+def gpu_encode(xd, tile, lat, bps, seed, kv):
+    h = hq.kv_encode(xd, lat, bps, seed) if kv else hq.encode(xd, tile, lat, bps, seed)
+    torch.cuda.synchronize()
+    words = h.payload_words()
+    return h, dict(step=h.step.cpu().numpy().view(np.uint16), meta=h.meta.cpu().numpy().view(np.uint16),
+                   off=h.chunk_off.cpu().numpy().view(np.uint32),
+                   payload=h.payload[:words].cpu().numpy().view(np.uint32), status=h.flags())
+
+
+def out_bits(t):
+    if t.dtype == torch.bfloat16:
+        return workloads.bf16_bits(t)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def oracle_out_bits(a):
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+def check_full(x_np, tile, lat, bps, seed, kv, dtype):
+    xd, xo = to_device(x_np, dtype)
+    xd = xd.reshape(-1, tile) if kv else xd
+    print(f"[case] full parity shape={tuple(x_np.shape)} tile={tile} {lat} bps={bps} kv={kv} {dtype}", flush=True)
+    h, g = gpu_encode(xd, tile, lat, bps, seed, kv)
+    c = rate_c(lat, tile, bps, int(kv))
+    e = oracle.encode(xo.reshape(-1, x_np.shape[-1]) if not kv else xo.reshape(-1, tile), tile, lat, c, seed,
+                      int(kv))
+    np.testing.assert_array_equal(g["step"], e.step)
+    np.testing.assert_array_equal(g["meta"], e.meta)
+    np.testing.assert_array_equal(g["off"], e.chunk_off)
+    np.testing.assert_array_equal(g["payload"], e.payload)
+    assert g["status"] == (hq.FLAG_NONFINITE if e.status == oracle.ENONFINITE else 0)
+    # decode of the GPU stream vs decode of the oracle stream
+    xh = hq.decode(h)
+    torch.cuda.synchronize()
+    rows, cols = (xo.size // tile, tile) if kv else xo.shape
+    ref, st = oracle.decode(e, rows, cols, tile, lat, c, seed,
+                            oracle.BF16 if dtype == "bf16" else oracle.F32, int(kv))
+    assert st == oracle.OK and h.flags() == g["status"]
+    np.testing.assert_array_equal(out_bits(xh).reshape(-1), oracle_out_bits(ref).reshape(-1))
+    return h, e
+
+
+# ---------------------------------------------------------------- small cases
+@pytest.mark.parametrize("kv", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("tile", [64, 128, 256])
+@pytest.mark.parametrize("lat", ["Z", "A2", "D4", "E8"])
+def test_small_parity(lat, tile, dtype, kv):
+    T = 200                                          # 3 full chunks + a ragged 8-tile chunk
+    x = workloads.student_t_outlier_cols(T // 2, 2 * tile, key=tile + len(lat), n_out=2)
+    check_full(x, tile, lat, 2.0 if kv else 4.0, seed=1000 + tile, kv=kv, dtype=dtype)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+def test_tile_counts(T):
+    x = workloads.gaussian(T, 128, key=T)
+    check_full(x, 128, "E8", 4.0, seed=T, kv=False, dtype="bf16")
+
+
+@pytest.mark.parametrize("bps", [1.5, 3.0, 5.0, 8.0])
+@pytest.mark.parametrize("tile", [128, 256])
+def test_rate_extremes(bps, tile):
+    x = workloads.gaussian(96, 2 * tile, key=int(bps * 4))
+    check_full(x, tile, "E8", bps, seed=7, kv=False, dtype="f32")
+
+
+def test_special_values():
+    n = 128
+    x = workloads.gaussian(40, 2 * n, key=9)
+    x[0] = 0.0                                       # zero tiles
+    x[1, :n] = 5.0                                   # constant tile
+    x[2, 3] = np.nan                                 # non-finite tiles -> flagged, coded as zero
+    x[3, 200] = np.inf
+    x[4] = 1e-40                                     # subnormal inputs: step rounds to 0
+    x[5] *= 1e30                                     # huge range
+    x[6, :n] = 0.0; x[6, 7] = 1e3                    # one spike
+    x[7] = np.float32(1.5e-45) * np.arange(2 * n)    # denormal ramp
+    h, e = check_full(x, n, "E8", 4.0, seed=3, kv=False, dtype="f32")
+    assert h.flags() == hq.FLAG_NONFINITE
+
+
+def test_repeatable_and_workspace_reuse():
+    # the ticket counter and look-back tags reset themselves between calls of
+    # different sizes sharing one workspace
+    for T in (320, 64 * 300 + 17, 70, 64 * 40):
+        x = workloads.gaussian(T, 128, key=T)
+        xd, _ = to_device(x, "bf16")
+        outs = [gpu_encode(xd, 128, "E8", 4.0, 5, False)[1] for _ in range(3)]
+        for o in outs[1:]:
+            for k in ("step", "meta", "off", "payload"):
+                np.testing.assert_array_equal(o[k], outs[0][k])
+        check_full(x, 128, "E8", 4.0, seed=5, kv=False, dtype="bf16")
+
+
+def test_decoder_on_oracle_streams_and_corruption():
+    _dev()
+    n, lat = 128, "E8"
+    x = workloads.gaussian(200, n, key=21)
+    c = rate_c(lat, n, 4.0)
+    e = oracle.encode(x, n, lat, c, 4)
+    rng = np.random.default_rng(0)
+    for trial in range(12):
+        pay = e.payload.copy()
+        meta = e.meta.copy()
+        off = e.chunk_off.copy()
+        if trial % 3 == 0:
+            for _ in range(3):
+                w = rng.integers(0, pay.size)
+                pay[w] ^= np.uint32(1) << np.uint32(rng.integers(0, 32))
+        elif trial % 3 == 1:
+            meta[rng.integers(0, meta.size)] += np.uint16(8 * int(rng.integers(1, 4)))
+        else:
+            off[1 + rng.integers(0, off.size - 1)] -= 1
+        ee = oracle.Encoded(e.step, meta, off, pay, 0)
+        ref, st = oracle.decode(ee, 200, n, n, lat, c, 4, oracle.F32)
+        h = hq.HQTensor(torch.from_numpy(pay.view(np.int32)).to(_dev()),
+                        torch.from_numpy(e.step.view(np.int16)).to(_dev()),
+                        torch.from_numpy(meta.view(np.int16)).to(_dev()),
+                        torch.from_numpy(off.view(np.int32)).to(_dev()),
+                        torch.zeros(1, dtype=torch.int32, device=_dev()), (200, n), torch.float32, n, lat, 4.0, 4)
+        out = hq.decode(h)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        assert (h.flags() == hq.FLAG_CORRUPT) == (st == oracle.ECORRUPT)
+
+
+# ---------------------------------------------------------------- benchmark configurations
+def test_config0_full():
+    check_full(workloads.config_tensor(0), 128, "E8", 4.0, seed=0, kv=False, dtype="f32")
+
+
+def test_config1_full():
+    check_full(workloads.config_tensor(1), 128, "E8", 4.0, seed=1, kv=False, dtype="bf16")
+
+
+def sampled_parity(xd, xo2d, tile, lat, bps, seed, kv, chunks):
+    """Full-size GPU encode/decode; oracle on whole sampled chunks."""
+    print(f"[case] sampled parity shape={tuple(xd.shape)} tile={tile} {lat} bps={bps} kv={kv}", flush=True)
+    h, g = gpu_encode(xd, tile, lat, bps, seed, kv)
+    assert g["status"] == 0
+    xh = hq.decode(h)
+    torch.cuda.synchronize()
+    assert h.flags() == 0
+    c = rate_c(lat, tile, bps, int(kv))
+    T = g["step"].size
+    # chunk sizes agree with the tile lengths everywhere
+    lens = (g["meta"] >> 3).astype(np.int64)
+    C = (T + 63) // 64
+    per_chunk = np.add.reduceat(lens, np.arange(0, T, 64))
+    np.testing.assert_array_equal(np.diff(g["off"].astype(np.int64)), (per_chunk + 31) // 32)
+    rows, cols = xo2d.shape
+    xh_bits = out_bits(xh).reshape(-1)
+    for ch in chunks:
+        ch = int(ch) % C
+        t0, t1 = 64 * ch, min(T, 64 * ch + 64)
+        st, mt, bits = oracle.encode_tiles(xo2d, tile, lat, c, seed, t0, t1, int(kv))
+        np.testing.assert_array_equal(g["step"][t0:t1], st)
+        np.testing.assert_array_equal(g["meta"][t0:t1], mt)
+        w0, w1 = int(g["off"][ch]), int(g["off"][ch + 1])
+        np.testing.assert_array_equal(g["payload"][w0:w1], bits[: w1 - w0])
+        assert not bits[w1 - w0:].any()
+        ref, rst = oracle.decode_tiles(st, mt, bits, rows, cols, tile, lat, c, seed, t0, t1,
+                                       oracle.BF16 if xo2d.dtype == np.uint16 else oracle.F32, int(kv))
+        assert rst == oracle.OK
+        np.testing.assert_array_equal(xh_bits[t0 * tile:t1 * tile], oracle_out_bits(ref))
+    return h, g, xh
+
+
+@pytest.mark.parametrize("lat", ["Z", "A2", "D4", "E8"])
+@pytest.mark.parametrize("bps", [3.0, 4.0, 5.0])
+def test_config2_sweep(lat, bps):
+    x = workloads.config_tensor(2)
+    xd, xo = to_device(x, "bf16")
+    if lat == "E8" and bps == 4.0:
+        check_full(x, 128, lat, bps, seed=2, kv=False, dtype="bf16")
+    else:
+        C = (xo.size // 128 + 63) // 64
+        sampled_parity(xd, xo, 128, lat, bps, 2, False, [0, 1, C // 2, C - 1])
+
+
+@pytest.mark.parametrize("which", ["K", "V"])
+def test_config3_kv(which):
+    x = workloads.config_tensor(3, which=which)
+    seed = workloads.codec_seed(3, which=which)
+    xd, xo = to_device(x, "bf16")
+    xo2 = xo.reshape(-1, 128)
+    C = (xo2.shape[0] + 63) // 64
+    del x
+    h, g, xh = sampled_parity(xd, xo2, 128, "E8", 2.0, seed, True, [0, 12345, C // 2, C - 1])
+    bps = float((g["meta"] >> 3).astype(np.int64).sum()) / xo2.size
+    assert abs(bps - 2.0) < 0.05
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_config4_dit_layer(layer):
+    x = workloads.config_tensor(4, layer=layer)
+    seed = workloads.codec_seed(4, layer=layer)
+    xd, xo = to_device(x, "bf16")
+    C = (xo.size // 256 + 63) // 64
+    h, g, xh = sampled_parity(xd, xo, 256, "E8", 4.0, seed, False, [0, 777, C // 2, C - 1])
+    bps = float((g["meta"] >> 3).astype(np.int64).sum()) / xo.size
+    assert abs(bps - 4.0) < 0.05
