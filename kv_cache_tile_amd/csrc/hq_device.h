@@ -246,6 +246,49 @@ __device__ __forceinline__ void fwht_tile(float (&a)[kLaneElems], int q) {
   }
 }
 
+// Sequential reader of an LDS bit array: `buf` holds the next `nb` bits
+// (1 <= nb <= 64 after refill), bit 0 = the bit at position `pos`.
+struct LdsBits {
+  const uint32_t* w;
+  uint32_t fw;      // next word to load
+  uint32_t nb;
+  uint64_t buf;
+  uint32_t pos;
+  __device__ __forceinline__ void init(const uint32_t* words, uint32_t p) {
+    w = words;
+    pos = p;
+    fw = p >> 5;
+    const uint32_t s = p & 31u;
+    buf = (uint64_t)(w[fw] >> s);
+    nb = 32u - s;
+    fw++;
+  }
+  __device__ __forceinline__ void refill() {
+    if (nb <= 32u) {
+      buf |= (uint64_t)w[fw] << nb;
+      fw++;
+      nb += 32u;
+    }
+  }
+  __device__ __forceinline__ void skip(uint32_t n) {   // n <= nb
+    buf = n >= 64u ? 0ull : (buf >> n);
+    nb -= n;
+    pos += n;
+  }
+};
+
+// position (0..31) of the r-th set bit (r counted from 0) of w; w has > r ones
+__device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
+  uint32_t base = 0;
+#pragma unroll
+  for (uint32_t half = 16; half >= 1; half >>= 1) {
+    const uint32_t lo = __builtin_popcount(w & ((1u << half) - 1u));
+    if (r >= lo) { r -= lo; w >>= half; base += half; }
+    else w &= (1u << half) - 1u;
+  }
+  return base;
+}
+
 // read 32 bits starting at bit `pos` of an LDS word array (needs one guard word)
 __device__ __forceinline__ uint32_t lds_read32(const uint32_t* w, uint32_t pos) {
   uint32_t i = pos >> 5, s = pos & 31u;

@@ -196,18 +196,18 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
       if (cost < best_c) { best_c = cost; best_k = k; }
     }
     const uint32_t k = best_k;
-    uint32_t lane_bits = 0;
+    // this lane's unary quotients: sum (q_i + 1) bits; exclusive prefix over the tile's lanes
+    uint32_t lane_unary = 0;
 #pragma unroll
-    for (int kk = 0; kk < 8; kk++) if (kk == (int)k) lane_bits = S[kk];
-    lane_bits += (uint32_t)kLaneElems * (1u + k);
-    // exclusive prefix of lane lengths inside the tile
-    uint32_t incl = lane_bits;
+    for (int kk = 0; kk < 8; kk++) if (kk == (int)k) lane_unary = S[kk];
+    lane_unary += (uint32_t)kLaneElems;
+    uint32_t incl = lane_unary;
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) {
       uint32_t v = __shfl_up(incl, m, LPT);
       if (q >= m) incl += v;
     }
-    const uint32_t lane_excl = incl - lane_bits;
+    const uint32_t lane_excl = incl - lane_unary;
     const uint32_t tlen = B + best_c;
     if (q == 0) tile_len[tau] = active ? tlen : 0u;
     __syncthreads();
@@ -226,7 +226,7 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
     __syncthreads();
     const uint32_t total_bits = misc[1];
     uint32_t W = (total_bits + 31u) >> 5;
-    const bool fits = W <= stage_words - 2;
+    const bool fits = W + 2 <= stage_words;
 
     // publish this chunk's size early so later chunks can look back past it
     if (tid == 0) {
@@ -236,44 +236,70 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
     for (uint32_t i = tid; i < W + 2 && i < stage_words; i += blockDim.x) stage[i] = 0u;
     __syncthreads();
 
-    // ---- pack: coset bits, then Rice codewords (q zeros, one, k bits LSB first) ----
+    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane ----
     if (active && fits) {
-      uint32_t pos = tile_off[tau];
-      if constexpr (CB_LANE > 0) lds_or_bits(stage, pos + (uint32_t)q * CB_LANE, cb, CB_LANE);
-      pos += B + lane_excl;
-      const uint32_t rmask = (1u << k) - 1u;
+      const uint32_t t0 = tile_off[tau];
+      if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
+      if (k > 0) {
+        const uint32_t rmask = (1u << k) - 1u;
+        uint32_t rpos = t0 + B + (uint32_t)q * kLaneElems * k;
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) {
+          lds_or_bits(stage, rpos, sym[i] & rmask, k);
+          rpos += k;
+        }
+      }
+      uint32_t upos = t0 + B + (uint32_t)N * k + lane_excl;
 #pragma unroll
       for (int i = 0; i < kLaneElems; i++) {
-        const uint32_t qv = sym[i] >> k;
-        const uint32_t field = ((sym[i] & rmask) << 1) | 1u;
-        pos += qv;
-        lds_or_bits(stage, pos, field, k + 1u);
-        pos += 1u + k;
+        upos += sym[i] >> k;
+        atomicOr(&stage[upos >> 5], 1u << (upos & 31u));
+        upos += 1u;
       }
     }
     __syncthreads();
 
-    // ---- decoupled look-back for the chunk's word offset ----
-    if (tid == 0) {
+    // ---- decoupled look-back, one predecessor per lane of wave 0 ----
+    if (tid < 64) {
       uint32_t excl = 0;
       if (chunk > 0) {
-        uint64_t j = chunk - 1;
+        int64_t base = (int64_t)chunk - 1;
         for (;;) {
-          uint64_t v = __hip_atomic_load(&look[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-          uint32_t hi = (uint32_t)(v >> 32);
-          if ((hi >> 2) != epoch || (hi & 3u) == 0) { __builtin_amdgcn_s_sleep(1); continue; }
-          excl += (uint32_t)v;
-          if ((hi & 3u) == kFlagIncl) break;
-          j--;
+          const int64_t j = base - tid;
+          uint64_t v;
+          uint32_t flag;
+          if (j < 0) {
+            v = 0;
+            flag = kFlagIncl;                                // before chunk 0: prefix 0
+          } else {
+            for (;;) {
+              v = __hip_atomic_load(&look[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+              const uint32_t hi = (uint32_t)(v >> 32);
+              if ((hi >> 2) == epoch && (hi & 3u) != 0) { flag = hi & 3u; break; }
+              __builtin_amdgcn_s_sleep(1);
+            }
+          }
+          const uint64_t incl_mask = __ballot(flag == kFlagIncl);
+          const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
+          uint32_t part = (tid <= first) ? (uint32_t)v : 0u;
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m);
+          excl += part;
+          if (incl_mask) break;
+          base -= 64;
         }
-        uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
-        __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_AGENT);
       }
-      misc[3] = excl;
-      chunk_off[chunk] = excl;
-      if (chunk == C - 1) chunk_off[C] = excl + W;
-      if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+      if (tid == 0) {
+        if (chunk > 0) {
+          uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
+          __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        misc[3] = excl;
+        chunk_off[chunk] = excl;
+        if (chunk == C - 1) chunk_off[C] = excl + W;
+        if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+      }
     }
     __syncthreads();
     const uint32_t excl = misc[3];
@@ -304,16 +330,12 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   constexpr int BPL = kLaneElems / D;
   constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
   constexpr uint32_t B = CB_LANE * LPT;
-  constexpr uint32_t CBW = (B + 31) / 32 + 1;              // coset words per tile (+1 guard)
-  constexpr uint32_t SYMW = N / 2 + 1;                      // u16 symbols, padded row (words)
 
   extern __shared__ uint32_t smem[];
-  uint32_t* stage = smem;                                   // [stage_words]
-  uint32_t* symw = stage + stage_words;                     // [64][SYMW]
-  uint32_t* cosw = symw + kChunkTiles * SYMW;               // [64][CBW]
-  uint32_t* tile_off = cosw + kChunkTiles * CBW;            // [64]
-  uint32_t* tile_bad = tile_off + kChunkTiles;              // [64]
-  uint16_t* sym16 = reinterpret_cast<uint16_t*>(symw);
+  uint32_t* stage = smem;                                   // [stage_words] chunk payload + guard
+  uint32_t* tile_off = stage + stage_words;                 // [64] bit offset of each tile
+  uint32_t* tile_ok = tile_off + kChunkTiles;               // [64]
+  uint32_t* ustart = tile_ok + kChunkTiles;                 // [64 * LPT] first unary bit per lane
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -325,125 +347,160 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 
   for (uint64_t chunk = blockIdx.x; chunk < C; chunk += gridDim.x) {
     const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
-    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) + 2 <= stage_words;
+    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) + 4 <= stage_words;
     const uint32_t W = range_ok ? (uint32_t)(w1 - w0) : 0u;
     for (uint32_t i = tid; i < W; i += blockDim.x) stage[i] = payload[w0 + i];
-    if (tid < 2) stage[W + tid] = 0u;
+    if (tid < 4) stage[W + tid] = 0u;
 
-    // tile offsets inside the chunk
+    // tile offsets inside the chunk; a chunk whose size disagrees with its tiles is dropped
     if (tid < kChunkTiles) {
       const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
-      const uint32_t len = tt < T ? (uint32_t)(meta[tt] >> 3) : 0u;
+      const uint32_t m = tt < T ? (uint32_t)meta[tt] : 0u;
+      const uint32_t len = m >> 3, kk = m & 7u;
       uint32_t inc = len;
 #pragma unroll
-      for (int m = 1; m < kChunkTiles; m <<= 1) {
-        uint32_t o = __shfl_up(inc, m, kChunkTiles);
-        if (tid >= m) inc += o;
+      for (int s2 = 1; s2 < kChunkTiles; s2 <<= 1) {
+        uint32_t o = __shfl_up(inc, s2, kChunkTiles);
+        if (tid >= s2) inc += o;
       }
       tile_off[tid] = inc - len;
       const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
       const bool chunk_ok = range_ok && ((total + 31u) >> 5) == W;
-      tile_bad[tid] = chunk_ok ? 0u : 1u;
+      tile_ok[tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
     }
     __syncthreads();
 
-    // ---- parse: one lane per tile ----
-    if (tid < kChunkTiles) {
-      const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
-      if (tt < T && !tile_bad[tid]) {
-        const uint32_t m = meta[tt];
-        const uint32_t len = m >> 3, k = m & 7u;
-        const uint32_t start = tile_off[tid], end = start + len;
-        uint32_t pos = start;
-        bool bad = len < B + (uint32_t)N;                  // every codeword has at least one bit
-        uint32_t* cw = cosw + tid * CBW;
-        if (!bad && B > 0) {
-#pragma unroll
-          for (uint32_t w = 0; w < (B + 31) / 32; w++) {
-            const uint32_t nb = (B - 32 * w) < 32 ? (B - 32 * w) : 32;
-            uint32_t v = lds_read32(stage, pos);
-            cw[w] = nb == 32 ? v : (v & ((1u << nb) - 1u));
-            pos += nb;
-          }
-        }
-        uint16_t* srow = sym16 + tid * (2 * SYMW);
-        const uint32_t rmask = (1u << k) - 1u;
-        for (int i = 0; i < N && !bad; i++) {
-          uint32_t qv = 0;
-          for (;;) {
-            if (pos >= end) { bad = true; break; }
-            const uint32_t w = lds_read32(stage, pos);
-            if (w != 0u) {
-              const uint32_t z = __builtin_ctz(w);
-              qv += z;
-              pos += z + 1u;
-              break;
-            }
-            qv += 32u;
-            pos += 32u;
-          }
-          if (bad || pos > end) { bad = true; break; }
-          const uint32_t r = lds_read32(stage, pos) & rmask;
-          pos += k;
-          const uint32_t u = (qv << k) | r;
-          if (u > 0xFFFFu) { bad = true; break; }
-          srow[i] = (uint16_t)u;
-        }
-        if (bad || pos != end) tile_bad[tid] = 1u;
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const bool active = t < T;
+    const uint32_t m = active ? (uint32_t)meta[t] : 0u;
+    const uint32_t len = m >> 3, k = m & 7u;
+    bool ok = active && tile_ok[tau] != 0u;
+    const uint32_t start = tile_off[tau], end = start + len;
+    const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
+
+    // ---- where does each lane's first unary code start?  Every codeword has
+    // exactly one 1 in the unary plane: count ones word by word (lane q takes
+    // words q, q+LPT, ...) and mark the bit after the (32 q)-th one. ----
+    const uint32_t words = ok ? (end - ub + 31u) >> 5 : 0u;
+    uint32_t carry = 0;
+    for (uint32_t r = 0;; r++) {
+      const bool more = r * LPT < words;
+      if (!__any(more)) break;
+      const uint32_t j = r * LPT + (uint32_t)q;
+      uint32_t w = 0;
+      if (j < words) {
+        const uint32_t p = ub + 32u * j;
+        w = lds_read32(stage, p);
+        const uint32_t valid = end - p;
+        if (valid < 32u) w &= (1u << valid) - 1u;
       }
+      const uint32_t c = __builtin_popcount(w);
+      uint32_t inc = c;
+#pragma unroll
+      for (int s2 = 1; s2 < LPT; s2 <<= 1) {
+        uint32_t o = __shfl_up(inc, s2, LPT);
+        if (q >= s2) inc += o;
+      }
+      const uint32_t before = carry + inc - c, after = carry + inc;
+      const uint32_t mm = before / 32u + 1u;
+      if (c != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
+        ustart[tau * LPT + mm] = ub + 32u * j + select_bit(w, 32u * mm - before - 1u) + 1u;
+      carry += __shfl(inc, LPT - 1, LPT);
     }
+    ok = ok && carry == (uint32_t)N;
     __syncthreads();
+
+    // ---- parse this lane's 32 symbols: remainders, then unary quotients ----
+    uint32_t sym[kLaneElems];
+    bool lane_ok = ok;
+    if (ok) {
+      if (k > 0) {
+        LdsBits rd;
+        rd.init(stage, start + B + (uint32_t)q * kLaneElems * k);
+        const uint32_t rmask = (1u << k) - 1u;
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) {
+          rd.refill();
+          sym[i] = (uint32_t)rd.buf & rmask;
+          rd.skip(k);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) sym[i] = 0u;
+      }
+      LdsBits ud;
+      ud.init(stage, q == 0 ? ub : ustart[tau * LPT + q]);
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) {
+        uint32_t qv = 0;
+        ud.refill();
+        while (ud.buf == 0ull && ud.pos < end) {       // a run longer than the buffer
+          qv += ud.nb;
+          ud.pos += ud.nb;
+          ud.nb = 0;
+          ud.refill();
+          ud.refill();
+        }
+        const uint32_t z = (uint32_t)__builtin_ctzll(ud.buf | (1ull << 63));
+        qv += z;
+        ud.skip(z + 1u);
+        const uint32_t u = (qv << k) | sym[i];
+        if (qv > 0xFFFFu || u > 0xFFFFu) lane_ok = false;
+        sym[i] = u;
+      }
+      if (q == LPT - 1 && ud.pos != end) lane_ok = false;   // the last one ends the tile
+    }
+    // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
+    int all_ok = lane_ok ? 1 : 0;
+#pragma unroll
+    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
+    lane_ok = all_ok != 0;
 
     // ---- rebuild: points, (dither), step, inverse RHT, store ----
-    {
-      const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
-      if (t < T) {
-        const bool bad = tile_bad[tau] != 0u;
-        if (bad && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
-        const float s = bad ? 0.0f : as_f((uint32_t)step[t] << 16);
-        const uint16_t* srow = sym16 + tau * (2 * SYMW) + q * kLaneElems;
-        const uint32_t* cw = cosw + tau * CBW;
-        float a[kLaneElems];
+    if (active) {
+      const bool bad = !lane_ok;
+      if (bad && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
+      const float s = bad ? 0.0f : as_f((uint32_t)step[t] << 16);
+      uint32_t cbits = 0;
+      if constexpr (CB_LANE > 0) {
+        if (!bad) cbits = lds_read32(stage, start + (uint32_t)q * CB_LANE);
+      }
+      float a[kLaneElems];
 #pragma unroll
-        for (int b = 0; b < BPL; b++) {
-          uint32_t u[D];
+      for (int b = 0; b < BPL; b++) {
+        uint32_t u[D];
 #pragma unroll
-          for (int i = 0; i < D; i++) u[i] = bad ? 0u : (uint32_t)srow[b * D + i];
-          uint32_t p = 0;
-          if constexpr (LatticeTraits<LAT>::coset) {
-            const uint32_t bit = (uint32_t)q * CB_LANE + (uint32_t)b;
-            p = bad ? 0u : (cw[bit >> 5] >> (bit & 31u)) & 1u;
-          }
-          float pt[D];
-          block_point<LAT>(u, p, pt, a2);
-          if constexpr (DITHER) {
-            float du[D];
-            dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
+        for (int i = 0; i < D; i++) u[i] = bad ? 0u : sym[b * D + i];
+        const uint32_t p = (cbits >> b) & 1u;
+        float pt[D];
+        block_point<LAT>(u, p, pt, a2);
+        if constexpr (DITHER) {
+          float du[D];
+          dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
 #pragma unroll
-            for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
-          }
-#pragma unroll
-          for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
+          for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
         }
-        fwht_tile<LPT>(a, q);
 #pragma unroll
-        for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i] * inv_sqrtn) ^ (((sgn >> i) & 1u) << 31));
-        const uint64_t base = t * N + (uint64_t)q * kLaneElems;
-        if constexpr (BF16) {
-          uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
+        for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
+      }
+      fwht_tile<LPT>(a, q);
 #pragma unroll
-          for (int v = 0; v < 4; v++) {
-            uint32_t w[4];
+      for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i] * inv_sqrtn) ^ (((sgn >> i) & 1u) << 31));
+      const uint64_t base = t * N + (uint64_t)q * kLaneElems;
+      if constexpr (BF16) {
+        uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
 #pragma unroll
-            for (int h = 0; h < 4; h++)
-              w[h] = bf16_rne_bits(a[v * 8 + 2 * h]) | (bf16_rne_bits(a[v * 8 + 2 * h + 1]) << 16);
-            p[v] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        } else {
-          float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base);
+        for (int v = 0; v < 4; v++) {
+          uint32_t w[4];
 #pragma unroll
-          for (int v = 0; v < 8; v++) p[v] = make_float4(a[v * 4], a[v * 4 + 1], a[v * 4 + 2], a[v * 4 + 3]);
+          for (int h = 0; h < 4; h++)
+            w[h] = bf16_rne_bits(a[v * 8 + 2 * h]) | (bf16_rne_bits(a[v * 8 + 2 * h + 1]) << 16);
+          p[v] = make_uint4(w[0], w[1], w[2], w[3]);
         }
+      } else {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base);
+#pragma unroll
+        for (int v = 0; v < 8; v++) p[v] = make_float4(a[v * 4], a[v * 4 + 1], a[v * 4 + 2], a[v * 4 + 3]);
       }
     }
     __syncthreads();
@@ -520,7 +577,7 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
   P->C = (P->T + kChunkTiles - 1) / kChunkTiles;
   P->bound = bound;
   P->c = c;
-  P->stage_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 2;
+  P->stage_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 4;
   P->cap_words = (P->T * bound + 31) / 32 + P->C;
   P->ws_bytes = 8 + 8 * P->C;
   return HQ_OK;
@@ -571,11 +628,8 @@ DecFn dec_fn(uint32_t lat, uint32_t n, bool bf16, bool dither) {
   }
 }
 
-uint32_t decode_lds_words(uint32_t n, uint32_t lat, uint32_t stage_words) {
-  uint32_t d = lattice_dim(lat);
-  uint32_t B = (lat == HQ_E8 || lat == HQ_A2) ? n / d : 0;
-  uint32_t cbw = (B + 31) / 32 + 1;
-  return stage_words + kChunkTiles * (n / 2 + 1) + kChunkTiles * cbw + 2 * kChunkTiles;
+uint32_t decode_lds_words(uint32_t n, uint32_t stage_words) {
+  return stage_words + 2 * kChunkTiles + kChunkTiles * (n / kLaneElems);
 }
 
 int grid_for(const void* fn, int block, size_t lds, uint64_t chunks, int* grid) {
@@ -625,7 +679,7 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   if ((uintptr_t)out & 15) return HQ_EINVAL;
   DecFn fn = dec_fn(lat, tile, dtype == HQ_BF16, kv != 0);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
-  const size_t lds = (size_t)decode_lds_words(tile, lat, P.stage_words) * 4;
+  const size_t lds = (size_t)decode_lds_words(tile, P.stage_words) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C, &grid);
   if (rc) return rc;

@@ -377,14 +377,22 @@ static void block_point(uint32_t lattice, uint32_t p, const uint32_t *sym, float
 static void put_bit(uint32_t *w, uint64_t b, uint32_t v) { if (v) w[b >> 5] |= 1u << (b & 31); }
 static uint32_t get_bit(const uint32_t *w, uint64_t b) { return (w[b >> 5] >> (b & 31)) & 1u; }
 
-/* Rice_k(u): (u >> k) zero bits, a one bit, then the k low bits of u, least
- * significant first.  Reading: the pages fix neither polarity nor bit order. */
-static uint64_t put_rice(uint32_t *w, uint64_t b, uint32_t u, uint32_t k)
+/* Rice_k(u) is the k low bits of u (the remainder) plus the quotient
+ * q = u >> k in unary: q zero bits, then a one bit.  Reading: the pages fix
+ * neither polarity nor bit order nor where the two fields sit; a tile stores
+ * the remainders of all n symbols first (a fixed-width plane, symbol i at
+ * bits i*k .. i*k+k-1, least significant first) and then the n unary
+ * quotients in symbol order.  Each codeword keeps its Rice length q + 1 + k. */
+static uint64_t put_remainder(uint32_t *w, uint64_t b, uint32_t u, uint32_t k)
 {
-    uint32_t q = u >> k;
-    b += q;                       /* zeros: buffer is zero-initialised */
-    put_bit(w, b++, 1);
     for (uint32_t i = 0; i < k; i++) put_bit(w, b++, (u >> i) & 1u);
+    return b;
+}
+
+static uint64_t put_unary(uint32_t *w, uint64_t b, uint32_t u, uint32_t k)
+{
+    b += u >> k;                  /* zeros: buffer is zero-initialised */
+    put_bit(w, b++, 1);
     return b;
 }
 
@@ -484,15 +492,18 @@ static void encode_tile(const void *x, const hqo_params *p, uint64_t t, tile_cod
     tc->len = tc->nb + (uint32_t)hqo_rice_cost(tc->sym, n, tc->k);
 }
 
+/* tile = coset bits (block order), remainder plane, unary plane */
 static uint64_t write_tile(uint32_t *w, uint64_t b, const tile_code *tc, uint32_t n)
 {
     for (uint32_t i = 0; i < tc->nb; i++) put_bit(w, b++, tc->cos[i]);
-    for (uint32_t i = 0; i < n; i++) b = put_rice(w, b, tc->sym[i], tc->k);
+    for (uint32_t i = 0; i < n; i++) b = put_remainder(w, b, tc->sym[i], tc->k);
+    for (uint32_t i = 0; i < n; i++) b = put_unary(w, b, tc->sym[i], tc->k);
     return b;
 }
 
 /* Stream layout (reading; the pages give none): tiles in row-major order,
- * each tile = its coset bits then its n Rice codewords; tiles are
+ * each tile = its coset bits then its n Rice codewords (remainder plane,
+ * then unary plane, see put_remainder/put_unary); tiles are
  * bit-contiguous inside a chunk of 64 tiles; every chunk starts on a 32-bit
  * word (chunk_off[c] = its first word, chunk_off[C] = total words) and its
  * tail is zero-padded.  meta[t] = len << 3 | k; step[t] = bf16 bits. */
@@ -569,22 +580,21 @@ static int parse_tile(const uint32_t *w, uint64_t b, uint64_t bend, uint32_t len
                       uint32_t n, uint32_t nb, uint32_t *cos, uint32_t *sym)
 {
     uint64_t tb = b;
-    if (len < nb + n) return 1;
-    for (uint32_t i = 0; i < nb; i++) {
-        if (b >= bend) return 1;
-        cos[i] = get_bit(w, b++);
+    if (len < nb + n * (k + 1)) return 1;
+    if (tb + len > bend) return 1;
+    bend = tb + len;                  /* a tile's fields never leave the tile */
+    for (uint32_t i = 0; i < nb; i++) cos[i] = get_bit(w, b++);
+    for (uint32_t i = 0; i < n; i++) {
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < k; j++) r |= get_bit(w, b++) << j;
+        sym[i] = r;
     }
     for (uint32_t i = 0; i < n; i++) {
-        uint32_t q = 0;
+        uint64_t q = 0;
         while (b < bend && !get_bit(w, b)) { q++; b++; }
         if (b >= bend) return 1;
         b++;                                  /* the terminating one */
-        uint32_t r = 0;
-        for (uint32_t j = 0; j < k; j++) {
-            if (b >= bend) return 1;
-            r |= get_bit(w, b++) << j;
-        }
-        uint64_t u = ((uint64_t)q << k) | r;
+        uint64_t u = (q << k) | sym[i];
         if (u > 0xFFFFu) return 1;
         sym[i] = (uint32_t)u;
     }

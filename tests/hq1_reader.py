@@ -5,8 +5,9 @@ Format: per tile t (row-major tile order) a bf16 step s_t and a 16-bit meta
 word (len << 3 | k); tiles are grouped 64 to a chunk, chunk c starts at 32-bit
 word chunk_off[c] of the payload; inside a chunk tiles are bit-contiguous
 (bit b = bit b%32 of word b//32).  A tile is its coset bits (E8: one per
-8-block, A2: one per 2-block) followed by n Rice codewords: q zero bits, a one
-bit, then k remainder bits, least significant first; the symbol is (q<<k)|r.
+8-block, A2: one per 2-block), then the n k-bit remainders (least significant
+bit first), then the n unary quotients (q zero bits, then a one bit); the
+symbol is (q<<k)|r.
 Symbols are zigzag codes (v >= 0 -> 2v, v < 0 -> -2v-1).  E8 and D4 store the
 last coordinate of a block halved (floor), its parity being that of the sum
 of the others.  Reconstruction (fp64 here): point = code (+1/2 for coset 1;
@@ -40,17 +41,16 @@ def parse(step, meta, chunk_off, payload, T, n, lattice):
             cos = bits[b:b + nb].astype(np.int64)
             b += nb
             syms = np.empty(n, np.int64)
+            rem = bits[b:b + n * k].reshape(n, k).astype(np.int64) if k else np.zeros((n, 0), np.int64)
+            r = (rem << np.arange(k)).sum(axis=1) if k else np.zeros(n, np.int64)
+            b += n * k
             for i in range(n):
                 q = 0
                 while bits[b] == 0:
                     q += 1
                     b += 1
                 b += 1
-                r = 0
-                for j in range(k):
-                    r |= int(bits[b]) << j
-                    b += 1
-                syms[i] = (q << k) | r
+                syms[i] = (q << k) | int(r[i])
             assert b - b0 == L, "tile length differs from its meta word"
             tiles.append((cos, syms, k))
         end = int(chunk_off[c + 1]) * 32
