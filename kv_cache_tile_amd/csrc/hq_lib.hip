@@ -34,6 +34,10 @@ namespace {
 struct RateEntry { uint8_t lattice, dither; uint16_t tile; uint16_t bps_q; uint32_t c_bits; };
 #include "hq_rate_table.inc"   // kRateTable[], generated from rate_table.json
 
+// Look-back words: (epoch << 34) | (flag << 32) | value.  The value travels
+// inside the atomic word itself, so relaxed agent-scope atomics suffice: no
+// other memory is published through them (release/acquire at agent scope
+// would write back / invalidate the whole L2 of the XCD on every chunk).
 constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 
@@ -70,17 +74,17 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
 #pragma unroll
   for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
 
-  if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t epoch = misc[2] & kEpochMask;
 
   for (;;) {
     if (tid == 0) {
-      uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       misc[0] = tk;
       if ((uint64_t)tk == C + gridDim.x - 1) {               // last ticket: all taken, reset for next call
         __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
@@ -231,7 +235,7 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
     // publish this chunk's size early so later chunks can look back past it
     if (tid == 0) {
       uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
-      __hip_atomic_store(&look[chunk], (tag << 32) | W, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&look[chunk], (tag << 32) | W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     for (uint32_t i = tid; i < W + 2 && i < stage_words; i += blockDim.x) stage[i] = 0u;
     __syncthreads();
@@ -273,7 +277,7 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
             flag = kFlagIncl;                                // before chunk 0: prefix 0
           } else {
             for (;;) {
-              v = __hip_atomic_load(&look[j], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+              v = __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               const uint32_t hi = (uint32_t)(v >> 32);
               if ((hi >> 2) == epoch && (hi & 3u) != 0) { flag = hi & 3u; break; }
               __builtin_amdgcn_s_sleep(1);
@@ -292,7 +296,7 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
       if (tid == 0) {
         if (chunk > 0) {
           uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
-          __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELEASE,
+          __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         }
         misc[3] = excl;
