@@ -289,6 +289,40 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
   return base;
 }
 
+// The same butterfly for the encoder, with the cross-lane stages as one
+// fused multiply-add per element: the lane with the stage bit clear computes
+// own + partner, the other own - partner, which is the exact value
+// a_j - a_{j+h} negated (fma with a +-1 factor rounds once, like an add).
+// Each upper role flips the sign a lane holds, so on return lane q holds
+// (-1)^popcount(q) times the oracle's values; the caller folds that sign
+// into the 1/sqrt(n) scale.  The sign of an exact zero may differ from the
+// oracle's, which no later encode step depends on.
+template <int LPT>
+__device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) {
+#pragma unroll
+  for (int h = 1; h < kLaneElems; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < kLaneElems; j++) {
+      if (j & h) continue;
+      float lo = a[j], hi = a[j + h];
+      a[j] = lo + hi;
+      a[j + h] = lo - hi;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPT; m <<= 1) {
+    const float f = (q & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < kLaneElems; j++) {
+      int other;
+      if (m == 1) other = __builtin_amdgcn_mov_dpp(__float_as_int(a[j]), 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
+      else if (m == 2) other = __builtin_amdgcn_mov_dpp(__float_as_int(a[j]), 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+      else other = __builtin_amdgcn_ds_swizzle(__float_as_int(a[j]), 0x101F);                        // lane ^ 4 (32-lane bit mode)
+      a[j] = __builtin_fmaf(__int_as_float(other), f, a[j]);
+    }
+  }
+}
+
 // read 32 bits starting at bit `pos` of an LDS word array (needs one guard word)
 __device__ __forceinline__ uint32_t lds_read32(const uint32_t* w, uint32_t pos) {
   uint32_t i = pos >> 5, s = pos & 31u;

@@ -45,7 +45,7 @@ constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 // Encode kernel
 // --------------------------------------------------------------------------
 template <int LAT, int N, bool BF16, bool DITHER>
-__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems))
+__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems)) __attribute__((amdgpu_waves_per_eu(4)))
 encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
               uint32_t key_sign, uint32_t key_dither, A2Consts a2,
               uint32_t* __restrict__ payload, uint64_t cap_words,
@@ -73,6 +73,8 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
   uint32_t sgn = 0;
 #pragma unroll
   for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+
+  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
   if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -125,10 +127,10 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
 #pragma unroll
     for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ (((sgn >> i) & 1u) << 31));
 
-    // ---- RHT: butterfly, then 1/sqrt(n) ----
-    fwht_tile<LPT>(a, q);
+    // ---- RHT: butterfly, then 1/sqrt(n) (with the lane's butterfly sign) ----
+    fwht_tile_signed<LPT>(a, q);
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * lane_scale;
 
     // ---- tile energy: pairwise tree over the tile, step = bf16(rms * c) ----
     float sq[kLaneElems];
@@ -182,13 +184,34 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
     }
 
     // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
+    // S[k] = sum of sym >> k over this lane.  When every symbol of the wave
+    // fits a byte, four symbols share a register and one shift, one mask and
+    // one byte-sum (v_sad_u8) add four terms.
     uint32_t S[8];
+    uint32_t mx = 0;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      uint32_t acc = 0;
+    for (int i = 0; i < kLaneElems; i++) mx |= sym[i];
+    if (__all(mx < 256u)) {
+      uint32_t P[kLaneElems / 4];
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> k;
-      S[k] = acc;
+      for (int j = 0; j < kLaneElems / 4; j++)
+        P[j] = sym[4 * j] | (sym[4 * j + 1] << 8) | (sym[4 * j + 2] << 16) | (sym[4 * j + 3] << 24);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const uint32_t bmask = 0x01010101u * (0xFFu >> k);
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> k) & bmask, 0u, acc);
+        S[k] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> k;
+        S[k] = acc;
+      }
     }
     uint32_t best_k = 0, best_c = 0xFFFFFFFFu;
 #pragma unroll
@@ -245,12 +268,15 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
       const uint32_t t0 = tile_off[tau];
       if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
       if (k > 0) {
+        // four k-bit remainders (at most 28 bits) per OR into the staging bits
         const uint32_t rmask = (1u << k) - 1u;
         uint32_t rpos = t0 + B + (uint32_t)q * kLaneElems * k;
 #pragma unroll
-        for (int i = 0; i < kLaneElems; i++) {
-          lds_or_bits(stage, rpos, sym[i] & rmask, k);
-          rpos += k;
+        for (int g = 0; g < kLaneElems / 4; g++) {
+          const uint32_t f = (sym[4 * g] & rmask) | ((sym[4 * g + 1] & rmask) << k) |
+                             ((sym[4 * g + 2] & rmask) << (2u * k)) | ((sym[4 * g + 3] & rmask) << (3u * k));
+          lds_or_bits(stage, rpos, f, 4u * k);
+          rpos += 4u * k;
         }
       }
       uint32_t upos = t0 + B + (uint32_t)N * k + lane_excl;
@@ -322,24 +348,38 @@ encode_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float
 // --------------------------------------------------------------------------
 // Decode kernel
 // --------------------------------------------------------------------------
+// decode work unit: TPW tiles of a chunk (a half chunk at n = 256, so that
+// workgroups stay at 256 threads and several fit on a CU)
+template <int N>
+struct DecodeGeom {
+  static constexpr int LPT = N / kLaneElems;
+  static constexpr int TPW = (256 / LPT) < kChunkTiles ? (256 / LPT) : kChunkTiles;
+  static constexpr int SUB = kChunkTiles / TPW;
+  static constexpr int THREADS = TPW * LPT;
+};
+
 template <int LAT, int N, bool BF16, bool DITHER>
-__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems))
+__global__ void __launch_bounds__(DecodeGeom<N>::THREADS)
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
               const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
               const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
               uint32_t key_sign, uint32_t key_dither, A2Consts a2, void* __restrict__ out,
-              uint32_t* __restrict__ status, uint32_t stage_words) {
+              uint32_t* __restrict__ status, uint32_t stage_words, uint32_t chunk_cap_words,
+              uint32_t tile_bound) {
   constexpr int LPT = N / kLaneElems;
+  constexpr int TPW = DecodeGeom<N>::TPW;
+  constexpr int SUB = DecodeGeom<N>::SUB;
   constexpr int D = LatticeTraits<LAT>::dim;
   constexpr int BPL = kLaneElems / D;
   constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
   constexpr uint32_t B = CB_LANE * LPT;
 
   extern __shared__ uint32_t smem[];
-  uint32_t* stage = smem;                                   // [stage_words] chunk payload + guard
-  uint32_t* tile_off = stage + stage_words;                 // [64] bit offset of each tile
+  uint32_t* stage = smem;                                   // [stage_words] this unit's bits + guard
+  uint32_t* tile_off = stage + stage_words;                 // [64] bit offset of each tile in the chunk
   uint32_t* tile_ok = tile_off + kChunkTiles;               // [64]
-  uint32_t* ustart = tile_ok + kChunkTiles;                 // [64 * LPT] first unary bit per lane
+  uint32_t* ustart = tile_ok + kChunkTiles;                 // [TPW * LPT] first unary bit per lane
+  uint32_t* misc = ustart + TPW * LPT;                      // [4]
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -348,13 +388,14 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   uint32_t sgn = 0;
 #pragma unroll
   for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
-  for (uint64_t chunk = blockIdx.x; chunk < C; chunk += gridDim.x) {
+  const uint64_t units = C * SUB;
+  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const uint64_t chunk = unit / SUB;
+    const int first = (int)(unit % SUB) * TPW;              // first tile of this unit in the chunk
     const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
-    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) + 4 <= stage_words;
-    const uint32_t W = range_ok ? (uint32_t)(w1 - w0) : 0u;
-    for (uint32_t i = tid; i < W; i += blockDim.x) stage[i] = payload[w0 + i];
-    if (tid < 4) stage[W + tid] = 0u;
+    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) <= chunk_cap_words;
 
     // tile offsets inside the chunk; a chunk whose size disagrees with its tiles is dropped
     if (tid < kChunkTiles) {
@@ -369,17 +410,28 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       }
       tile_off[tid] = inc - len;
       const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
-      const bool chunk_ok = range_ok && ((total + 31u) >> 5) == W;
+      const bool too_long = __any(len > tile_bound);        // longer than any valid tile can be
+      const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == w1 - w0;
       tile_ok[tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
+      // this unit's bit range [tile_off[first], tile_off[first + TPW]) in whole words
+      if (tid == first) misc[0] = chunk_ok ? (inc - len) : 0u;
+      if (tid == first + TPW - 1) misc[1] = chunk_ok ? inc : 0u;
     }
     __syncthreads();
+    const uint32_t sw = misc[0] >> 5;                       // first staged word (chunk-relative)
+    const uint32_t WL = ((misc[1] + 31u) >> 5) - sw;        // words staged
+    const uint32_t base_bit = sw * 32u;
+    for (uint32_t i = tid; i < WL; i += blockDim.x) stage[i] = payload[w0 + sw + i];
+    if (tid < 4) stage[WL + tid] = 0u;
+    __syncthreads();
 
-    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const int ct = first + tau;                             // tile index in the chunk
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)ct;
     const bool active = t < T;
     const uint32_t m = active ? (uint32_t)meta[t] : 0u;
     const uint32_t len = m >> 3, k = m & 7u;
-    bool ok = active && tile_ok[tau] != 0u;
-    const uint32_t start = tile_off[tau], end = start + len;
+    bool ok = active && tile_ok[ct] != 0u;
+    const uint32_t start = tile_off[ct] - base_bit, end = start + len;
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
     // ---- where does each lane's first unary code start?  Every codeword has
@@ -414,70 +466,50 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     ok = ok && carry == (uint32_t)N;
     __syncthreads();
 
-    // ---- parse this lane's 32 symbols: remainders, then unary quotients ----
-    uint32_t sym[kLaneElems];
+    // ---- parse and rebuild block by block: remainder and unary readers
+    // advance together; each block becomes lattice point (- dither) * step ----
+    float a[kLaneElems];
     bool lane_ok = ok;
-    if (ok) {
-      if (k > 0) {
-        LdsBits rd;
-        rd.init(stage, start + B + (uint32_t)q * kLaneElems * k);
-        const uint32_t rmask = (1u << k) - 1u;
-#pragma unroll
-        for (int i = 0; i < kLaneElems; i++) {
-          rd.refill();
-          sym[i] = (uint32_t)rd.buf & rmask;
-          rd.skip(k);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kLaneElems; i++) sym[i] = 0u;
-      }
-      LdsBits ud;
-      ud.init(stage, q == 0 ? ub : ustart[tau * LPT + q]);
-#pragma unroll
-      for (int i = 0; i < kLaneElems; i++) {
-        uint32_t qv = 0;
-        ud.refill();
-        while (ud.buf == 0ull && ud.pos < end) {       // a run longer than the buffer
-          qv += ud.nb;
-          ud.pos += ud.nb;
-          ud.nb = 0;
-          ud.refill();
-          ud.refill();
-        }
-        const uint32_t z = (uint32_t)__builtin_ctzll(ud.buf | (1ull << 63));
-        qv += z;
-        ud.skip(z + 1u);
-        const uint32_t u = (qv << k) | sym[i];
-        if (qv > 0xFFFFu || u > 0xFFFFu) lane_ok = false;
-        sym[i] = u;
-      }
-      if (q == LPT - 1 && ud.pos != end) lane_ok = false;   // the last one ends the tile
-    }
-    // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
-    int all_ok = lane_ok ? 1 : 0;
-#pragma unroll
-    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
-    lane_ok = all_ok != 0;
-
-    // ---- rebuild: points, (dither), step, inverse RHT, store ----
-    if (active) {
-      const bool bad = !lane_ok;
-      if (bad && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
-      const float s = bad ? 0.0f : as_f((uint32_t)step[t] << 16);
+    {
+      const float s = active ? as_f((uint32_t)step[t] << 16) : 0.0f;
       uint32_t cbits = 0;
       if constexpr (CB_LANE > 0) {
-        if (!bad) cbits = lds_read32(stage, start + (uint32_t)q * CB_LANE);
+        if (ok) cbits = lds_read32(stage, start + (uint32_t)q * CB_LANE);
       }
-      float a[kLaneElems];
+      const uint32_t rmask = (1u << k) - 1u;
+      LdsBits rd, ud;
+      if (ok) {
+        rd.init(stage, start + B + (uint32_t)q * kLaneElems * k);
+        ud.init(stage, q == 0 ? ub : ustart[tau * LPT + q]);
+      }
 #pragma unroll
       for (int b = 0; b < BPL; b++) {
         uint32_t u[D];
 #pragma unroll
-        for (int i = 0; i < D; i++) u[i] = bad ? 0u : sym[b * D + i];
-        const uint32_t p = (cbits >> b) & 1u;
+        for (int i = 0; i < D; i++) {
+          uint32_t r = 0, qv = 0;
+          if (ok) {
+            rd.refill();
+            r = (uint32_t)rd.buf & rmask;
+            rd.skip(k);
+            ud.refill();
+            while (ud.buf == 0ull && ud.pos < end) {         // a run longer than the buffer
+              qv += ud.nb;
+              ud.pos += ud.nb;
+              ud.nb = 0;
+              ud.refill();
+              ud.refill();
+            }
+            const uint32_t z = (uint32_t)__builtin_ctzll(ud.buf | (1ull << 63));
+            qv += z;
+            ud.skip(z + 1u);
+          }
+          const uint32_t uu = (qv << k) | r;
+          if (qv > 0xFFFFu || uu > 0xFFFFu) lane_ok = false;
+          u[i] = uu;
+        }
         float pt[D];
-        block_point<LAT>(u, p, pt, a2);
+        block_point<LAT>(u, (cbits >> b) & 1u, pt, a2);
         if constexpr (DITHER) {
           float du[D];
           dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
@@ -487,9 +519,30 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 #pragma unroll
         for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
       }
-      fwht_tile<LPT>(a, q);
+      if (ok && q == LPT - 1 && ud.pos != end) lane_ok = false;   // the last one ends the tile
+    }
+    // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
+    int all_ok = lane_ok ? 1 : 0;
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i] * inv_sqrtn) ^ (((sgn >> i) & 1u) << 31));
+    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
+    lane_ok = all_ok != 0;
+
+    // ---- inverse RHT and store (an invalid tile decodes to zeros) ----
+    if (active) {
+      if (!lane_ok) {
+        if (q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+      }
+      fwht_tile_signed<LPT>(a, q);
+      // lane q holds (-1)^popcount(q) times the butterfly output: fold that
+      // sign into the scale; + 0.0f turns a -0 into +0 (every zero of the
+      // exact butterfly is +0), then apply the sign diagonal
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) {
+        const float o = a[i] * lane_scale + 0.0f;
+        a[i] = as_f(as_u(o) ^ (((sgn >> i) & 1u) << 31));
+      }
       const uint64_t base = t * N + (uint64_t)q * kLaneElems;
       if constexpr (BF16) {
         uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
@@ -591,7 +644,7 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
 using EncFn = void (*)(const void*, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t, A2Consts,
                        uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*, uint32_t);
 using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
-                       uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t*, uint32_t);
+                       uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t*, uint32_t, uint32_t, uint32_t);
 
 template <int LAT, int N>
 EncFn enc_pick(bool bf16, bool dither) {
@@ -630,10 +683,6 @@ DecFn dec_fn(uint32_t lat, uint32_t n, bool bf16, bool dither) {
     case HQ_D4: return dec_by_tile<4>(n, bf16, dither);
     default: return dec_by_tile<8>(n, bf16, dither);
   }
-}
-
-uint32_t decode_lds_words(uint32_t n, uint32_t stage_words) {
-  return stage_words + 2 * kChunkTiles + kChunkTiles * (n / kLaneElems);
 }
 
 int grid_for(const void* fn, int block, size_t lds, uint64_t chunks, int* grid) {
@@ -682,16 +731,21 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   if (!payload || !step || !meta || !chunk_off || !status || !out) return HQ_EINVAL;
   if ((uintptr_t)out & 15) return HQ_EINVAL;
   DecFn fn = dec_fn(lat, tile, dtype == HQ_BF16, kv != 0);
-  const int block = kChunkTiles * (int)(tile / kLaneElems);
-  const size_t lds = (size_t)decode_lds_words(tile, P.stage_words) * 4;
+  const uint32_t lpt = tile / kLaneElems;
+  const uint32_t tpw = (256 / lpt) < (uint32_t)kChunkTiles ? 256 / lpt : (uint32_t)kChunkTiles;
+  const int block = (int)(tpw * lpt);
+  const uint32_t chunk_cap = (uint32_t)(((uint64_t)kChunkTiles * P.bound + 31) / 32);
+  // a unit's bits start anywhere in a word: one extra word, plus the readers' guard
+  const uint32_t stage_words = (uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 4;
+  const size_t lds = (size_t)(stage_words + 2 * kChunkTiles + tpw * lpt + 4) * 4;
   int grid;
-  rc = grid_for((const void*)fn, block, lds, P.C, &grid);
+  rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
   if (rc) return rc;
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, payload, payload_words, step, meta,
                      chunk_off, P.T, P.C, inv_sqrtn, derive_key(seed, 0x5349474Eu),
-                     derive_key(seed, 0x44495448u), a2, out, status, P.stage_words);
+                     derive_key(seed, 0x44495448u), a2, out, status, stage_words, chunk_cap, P.bound);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 

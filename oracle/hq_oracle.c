@@ -571,8 +571,10 @@ int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t
 /* Corrupt input (reading; the pages are silent): a tile whose n codewords  */
 /* do not span exactly its meta length, or that holds a symbol above 16     */
 /* bits, and every tile of a chunk whose word count disagrees with its      */
-/* tiles' lengths (or exceeds the capacity bound), decode to zero and are   */
-/* reported.  Valid streams never meet these conditions.                    */
+/* tiles' lengths, exceeds the capacity bound or holds a tile longer than   */
+/* the per-tile bound, decode to zero (+0 with                              */
+/* the sign diagonal applied, no dither) and are reported.  Valid streams   */
+/* never meet these conditions.                                             */
 /* ------------------------------------------------------------------------ */
 
 /* parse one tile starting at bit b (reads never reach bend); 0 = ok */
@@ -613,7 +615,7 @@ static void rebuild_tile(const hqo_params *p, uint64_t t, int bad, uint16_t step
         float pt[8];
         uint32_t pc = (coset_bits_per_block(p->lattice) && !bad) ? cos[blk] : 0;
         block_point(p->lattice, pc, bad ? zero : sym + blk * d, pt);
-        if (p->dither) {
+        if (p->dither && !bad) {
             float u[8];
             hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + blk * d), u);
             for (uint32_t i = 0; i < d; i++) pt[i] = pt[i] - u[i];
@@ -645,9 +647,13 @@ int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk
         uint64_t t0 = c * HQO_CHUNK_TILES, t1 = t0 + HQO_CHUNK_TILES;
         if (t1 > T) t1 = T;
         uint64_t total = 0;
-        for (uint64_t t = t0; t < t1; t++) total += meta[t] >> 3;
+        int too_long = 0;
+        for (uint64_t t = t0; t < t1; t++) {
+            total += meta[t] >> 3;
+            if ((uint32_t)(meta[t] >> 3) > hqo_tile_bound_bits(p)) too_long = 1;
+        }
         int chunk_bad = !(w1 >= w0 && w1 <= payload_words && w1 - w0 <= chunk_cap)
-                        || (total + 31) / 32 != w1 - w0;
+                        || too_long || (total + 31) / 32 != w1 - w0;
         uint64_t b = w0 * 32, bend = w1 * 32;
         for (uint64_t t = t0; t < t1; t++) {
             uint32_t len = meta[t] >> 3, k = meta[t] & 7u;
