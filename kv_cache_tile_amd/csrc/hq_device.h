@@ -277,6 +277,90 @@ struct LdsBits {
   }
 };
 
+// The 32 k-bit remainders of a lane start at bit `rb` of an LDS bit array:
+// align the k words they occupy, then cut fields at static offsets i*k; the
+// result is packed one remainder per byte (4 per word).
+template <int K>
+__device__ __forceinline__ void extract_remainders_k(const uint32_t* w, uint32_t rb, uint32_t (&rpk)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) rpk[j] = 0u;
+  if constexpr (K > 0) {
+    const uint32_t base = rb >> 5, sh = rb & 31u;
+    uint32_t raw[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; j++) raw[j] = w[base + j];
+    uint32_t seg[K + 1];
+#pragma unroll
+    for (int j = 0; j < K; j++) seg[j] = __builtin_amdgcn_alignbit(raw[j + 1], raw[j], sh);
+    seg[K] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      constexpr uint32_t mask = (1u << K) - 1u;
+      const int o = i * K, j = o >> 5, b = o & 31;
+      uint32_t r;
+      if (b + K <= 32) r = (seg[j] >> b) & mask;
+      else r = __builtin_amdgcn_alignbit(seg[j + 1], seg[j], b) & mask;
+      rpk[i >> 2] |= r << (8 * (i & 3));
+    }
+  }
+}
+
+__device__ __forceinline__ void extract_remainders(const uint32_t* w, uint32_t rb, uint32_t k, uint32_t (&rpk)[8]) {
+  switch (k) {
+    case 0: extract_remainders_k<0>(w, rb, rpk); break;
+    case 1: extract_remainders_k<1>(w, rb, rpk); break;
+    case 2: extract_remainders_k<2>(w, rb, rpk); break;
+    case 3: extract_remainders_k<3>(w, rb, rpk); break;
+    case 4: extract_remainders_k<4>(w, rb, rpk); break;
+    case 5: extract_remainders_k<5>(w, rb, rpk); break;
+    case 6: extract_remainders_k<6>(w, rb, rpk); break;
+    default: extract_remainders_k<7>(w, rb, rpk); break;
+  }
+}
+
+// Unary codes of an LDS bit array.  `W` holds the next `nb` bits (bits past
+// nb are zero); the window is topped up to more than 32 bits once every 8
+// codes (refill), so a code is normally found without touching LDS; a code
+// longer than the window falls back to a word-by-word loop.
+struct UnaryReader {
+  const uint32_t* s;
+  uint64_t W;
+  uint32_t nb, idx, pos;     // pos: bit index of W's bit 0
+  __device__ __forceinline__ void init(const uint32_t* words, uint32_t p0) {
+    s = words;
+    const uint32_t i = p0 >> 5, sh = p0 & 31u;
+    W = (((uint64_t)s[i + 1] << 32) | s[i]) >> sh;
+    nb = 64u - sh;
+    idx = i + 2;
+    pos = p0;
+  }
+  __device__ __forceinline__ void refill() {
+    if (nb <= 32u) {
+      W |= (uint64_t)s[idx] << nb;
+      idx++;
+      nb += 32u;
+    }
+  }
+  // zeros before the next one bit, consuming the one; limit = tile end
+  __device__ __forceinline__ uint32_t next(uint32_t limit) {
+    uint32_t q = 0;
+    while (W == 0ull) {                     // rare: the run is longer than the window
+      q += nb;
+      pos += nb;
+      if (pos >= limit) return 0xFFFFFFFFu;
+      W = ((uint64_t)s[idx + 1] << 32) | s[idx];
+      idx += 2;
+      nb = 64u;
+    }
+    const uint32_t lo = (uint32_t)W, hi = (uint32_t)(W >> 32);
+    const uint32_t z = lo != 0u ? (uint32_t)__builtin_ctz(lo) : 32u + (uint32_t)__builtin_ctz(hi);
+    W = (W >> z) >> 1;
+    nb -= z + 1u;
+    pos += z + 1u;
+    return q + z;
+  }
+};
+
 // position (0..31) of the r-th set bit (r counted from 0) of w; w has > r ones
 __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
   uint32_t base = 0;

@@ -476,36 +476,30 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       if constexpr (CB_LANE > 0) {
         if (ok) cbits = lds_read32(stage, start + (uint32_t)q * CB_LANE);
       }
-      const uint32_t rmask = (1u << k) - 1u;
-      LdsBits rd, ud;
+      uint32_t rpk[8];
+      UnaryReader ud;
       if (ok) {
-        rd.init(stage, start + B + (uint32_t)q * kLaneElems * k);
+        extract_remainders(stage, start + B + (uint32_t)q * kLaneElems * k, k, rpk);
         ud.init(stage, q == 0 ? ub : ustart[tau * LPT + q]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) rpk[j] = 0u;
       }
 #pragma unroll
       for (int b = 0; b < BPL; b++) {
         uint32_t u[D];
 #pragma unroll
         for (int i = 0; i < D; i++) {
-          uint32_t r = 0, qv = 0;
+          const int e = b * D + i;
+          uint32_t qv = 0;
           if (ok) {
-            rd.refill();
-            r = (uint32_t)rd.buf & rmask;
-            rd.skip(k);
-            ud.refill();
-            while (ud.buf == 0ull && ud.pos < end) {         // a run longer than the buffer
-              qv += ud.nb;
-              ud.pos += ud.nb;
-              ud.nb = 0;
-              ud.refill();
-              ud.refill();
-            }
-            const uint32_t z = (uint32_t)__builtin_ctzll(ud.buf | (1ull << 63));
-            qv += z;
-            ud.skip(z + 1u);
+            if ((e & 7) == 0) ud.refill();
+            qv = ud.next(end);
           }
+          const uint32_t r = (rpk[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          if (qv > 0xFFFFu) lane_ok = false;
           const uint32_t uu = (qv << k) | r;
-          if (qv > 0xFFFFu || uu > 0xFFFFu) lane_ok = false;
+          if (uu > 0xFFFFu) lane_ok = false;
           u[i] = uu;
         }
         float pt[D];
