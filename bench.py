@@ -13,6 +13,7 @@ with the fraction of the 8 TB/s HBM peak.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "encode/decode GB/s of bf16 input (E8, 4 bps) at 1 GPU; % of HBM peak"
+KERNEL_SOURCES = ("kv_cache_tile_amd/csrc/hq_lib.hip", "kv_cache_tile_amd/csrc/hq_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_hbm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources: HBM traffic measured with the counters
+    is only reported while the kernels are the ones it was measured on."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for
+    a plain copy of known size), or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(numel: int, tiles: int, chunks: int, bps: float) -> float:
@@ -62,6 +90,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--cpu-layers", type=int, default=2, help="layers timed on the CPU oracle (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain copy kernel over this many MiB "
+                         "(reference point for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the codec "
@@ -110,6 +141,13 @@ def main():
         dec_ms += [ev[L + l][0].elapsed_time(ev[L + l][1]) for l in range(L)]
     wall = time.perf_counter() - t0
     ms_per_step = 1000.0 * wall / args.steps
+    if args.calib_copy_mib > 0:
+        # reads and writes exactly calib_copy_mib MiB (int32 negation kernel)
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     flags = sum(h.flags() for h in hs)
     bits_payload = sum(h.bits_payload() for h in hs)
@@ -147,8 +185,13 @@ def main():
         "bps_payload": round(bits_payload / (numel * L), 4), "bps_total": round(bits_total / (numel * L), 4),
         "compression_vs_bf16": round(16.0 * numel * L / bits_total, 3), "nmse": err / ref, "status_flags": flags,
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": alg},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom_name), "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_us": round(dom_us, 2)},
+        "roofline_per_kernel": {
+            nm: {"achieved": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "avg_launch_us": round(us, 2), "traffic": measured_traffic(nm)}
+            for nm, us in (("encode_kernel", enc_avg_us), ("decode_kernel", dec_avg_us))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
