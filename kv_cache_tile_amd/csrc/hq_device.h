@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// two floats -> packed bf16 pair (low half = lo), round to nearest even
+// (v_cvt_pk_bf16_f32); the same bits as bf16_rne_bits for finite values
+typedef __bf16 hq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hq_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const hq_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hq_bf16x2));
+}
+
 __device__ __forceinline__ uint32_t zigzag(int32_t v) {
   return ((uint32_t)v << 1) ^ (uint32_t)(v >> 31);
 }
@@ -177,21 +186,6 @@ __device__ __forceinline__ void block_symbols(const int32_t* d, uint32_t* u) {
   }
 }
 
-// inverse: symbols + coset bit -> lattice point (floats)
-template <int LAT>
-__device__ __forceinline__ void block_point(const uint32_t* u, uint32_t p, float* pt, A2Consts k) {
-  constexpr int D = LatticeTraits<LAT>::dim;
-  int32_t d[D];
-  int32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < D; i++) {
-    d[i] = unzigzag(u[i]);
-    if (i < D - 1) s += d[i];
-  }
-  if constexpr (LAT == 4 || LAT == 8) d[D - 1] = 2 * d[D - 1] + (s & 1);
-  code_point<LAT>(d, p, pt, k);
-}
-
 // Subtractive dither (Methodology 4): v uniform on a box that is a
 // fundamental region of a sublattice (E8, D4: [-1,1)^d of 2Z^d; Z: [-1/2,1/2);
 // A2: [-1/2,1/2) x sqrt3 [-1/2,1/2) of Z x sqrt3 Z), reduced into the Voronoi
@@ -216,150 +210,98 @@ __device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, f
   for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
 }
 
-// --------------------------------------------------------------------------
-// Fast Walsh-Hadamard butterfly on a tile held as 32 consecutive elements per
-// lane in LPT lanes (lane q of the tile holds elements 32q .. 32q+31).
-// Strides h = 1..16 are in registers, h = 32, 64, 128 pair lane q with
-// q ^ (h/32).  Each output is exactly the oracle's a_j + a_{j+h} or
-// a_j - a_{j+h} (Methodology 1).
-// --------------------------------------------------------------------------
-template <int LPT>
-__device__ __forceinline__ void fwht_tile(float (&a)[kLaneElems], int q) {
-#pragma unroll
-  for (int h = 1; h < kLaneElems; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < kLaneElems; j++) {
-      if (j & h) continue;
-      float lo = a[j], hi = a[j + h];
-      a[j] = lo + hi;
-      a[j + h] = lo - hi;
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < LPT; m <<= 1) {
-    const bool upper = (q & m) != 0;
-#pragma unroll
-    for (int j = 0; j < kLaneElems; j++) {
-      float other = __shfl_xor(a[j], m);
-      a[j] = upper ? (other - a[j]) : (a[j] + other);
-    }
-  }
+// Index of the lowest set bit of w, all ones when w is 0 (v_ffbl_b32).  Written
+// as the instruction itself: the C builtin leaves w == 0 undefined, and the
+// compiler then folds the range checks that the fast unary path relies on.
+__device__ __forceinline__ uint32_t ffbl(uint32_t w) {
+  uint32_t r;
+  asm("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(w));
+  return r;
 }
 
-// Sequential reader of an LDS bit array: `buf` holds the next `nb` bits
-// (1 <= nb <= 64 after refill), bit 0 = the bit at position `pos`.
-struct LdsBits {
-  const uint32_t* w;
-  uint32_t fw;      // next word to load
-  uint32_t nb;
-  uint64_t buf;
-  uint32_t pos;
-  __device__ __forceinline__ void init(const uint32_t* words, uint32_t p) {
-    w = words;
-    pos = p;
-    fw = p >> 5;
-    const uint32_t s = p & 31u;
-    buf = (uint64_t)(w[fw] >> s);
-    nb = 32u - s;
-    fw++;
-  }
-  __device__ __forceinline__ void refill() {
-    if (nb <= 32u) {
-      buf |= (uint64_t)w[fw] << nb;
-      fw++;
-      nb += 32u;
-    }
-  }
-  __device__ __forceinline__ void skip(uint32_t n) {   // n <= nb
-    buf = n >= 64u ? 0ull : (buf >> n);
-    nb -= n;
-    pos += n;
-  }
-};
-
-// The 32 k-bit remainders of a lane start at bit `rb` of an LDS bit array:
-// align the k words they occupy, then cut fields at static offsets i*k; the
-// result is packed one remainder per byte (4 per word).
-template <int K>
-__device__ __forceinline__ void extract_remainders_k(const uint32_t* w, uint32_t rb, uint32_t (&rpk)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; j++) rpk[j] = 0u;
-  if constexpr (K > 0) {
-    const uint32_t base = rb >> 5, sh = rb & 31u;
-    uint32_t raw[K + 1];
-#pragma unroll
-    for (int j = 0; j <= K; j++) raw[j] = w[base + j];
-    uint32_t seg[K + 1];
-#pragma unroll
-    for (int j = 0; j < K; j++) seg[j] = __builtin_amdgcn_alignbit(raw[j + 1], raw[j], sh);
-    seg[K] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      constexpr uint32_t mask = (1u << K) - 1u;
-      const int o = i * K, j = o >> 5, b = o & 31;
-      uint32_t r;
-      if (b + K <= 32) r = (seg[j] >> b) & mask;
-      else r = __builtin_amdgcn_alignbit(seg[j + 1], seg[j], b) & mask;
-      rpk[i >> 2] |= r << (8 * (i & 3));
-    }
-  }
-}
-
-__device__ __forceinline__ void extract_remainders(const uint32_t* w, uint32_t rb, uint32_t k, uint32_t (&rpk)[8]) {
-  switch (k) {
-    case 0: extract_remainders_k<0>(w, rb, rpk); break;
-    case 1: extract_remainders_k<1>(w, rb, rpk); break;
-    case 2: extract_remainders_k<2>(w, rb, rpk); break;
-    case 3: extract_remainders_k<3>(w, rb, rpk); break;
-    case 4: extract_remainders_k<4>(w, rb, rpk); break;
-    case 5: extract_remainders_k<5>(w, rb, rpk); break;
-    case 6: extract_remainders_k<6>(w, rb, rpk); break;
-    default: extract_remainders_k<7>(w, rb, rpk); break;
-  }
-}
-
-// Unary codes of an LDS bit array.  `W` holds the next `nb` bits (bits past
-// nb are zero); the window is topped up to more than 32 bits once every 8
-// codes (refill), so a code is normally found without touching LDS; a code
-// longer than the window falls back to a word-by-word loop.
-struct UnaryReader {
+// Unary codes of an LDS bit array, read through a 64-bit window {hi:lo}
+// that holds the next nb valid bits (bits past nb are zero).  take() is the
+// straight-line path: the next code is the lowest one bit of lo, found only
+// when the run of zeros is shorter than 31 bits; any other case (longer run,
+// window exhausted) shows up as z >= 31 in the group's running maximum, and
+// the group is then read again from its saved state with next_exact().
+// pos() = idx * 32 - nb is the bit index of the window's first bit.
+struct UnaryWindow {
   const uint32_t* s;
-  uint64_t W;
-  uint32_t nb, idx, pos;     // pos: bit index of W's bit 0
+  uint32_t lo, hi, nb, idx;
   __device__ __forceinline__ void init(const uint32_t* words, uint32_t p0) {
     s = words;
     const uint32_t i = p0 >> 5, sh = p0 & 31u;
-    W = (((uint64_t)s[i + 1] << 32) | s[i]) >> sh;
+    const uint32_t w0 = s[i], w1 = s[i + 1];
+    lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    hi = sh ? (w1 >> sh) : w1;
     nb = 64u - sh;
-    idx = i + 2;
-    pos = p0;
+    idx = i + 2u;
   }
+  __device__ __forceinline__ uint32_t pos() const { return idx * 32u - nb; }
+  // top the window up to more than 32 bits (one word)
   __device__ __forceinline__ void refill() {
     if (nb <= 32u) {
-      W |= (uint64_t)s[idx] << nb;
+      const uint64_t W = (((uint64_t)hi << 32) | lo) | ((uint64_t)s[idx] << nb);
+      lo = (uint32_t)W;
+      hi = (uint32_t)(W >> 32);
       idx++;
       nb += 32u;
     }
   }
-  // zeros before the next one bit, consuming the one; limit = tile end
-  __device__ __forceinline__ uint32_t next(uint32_t limit) {
+  // next code on the fast path; valid only while the running max of z stays < 31
+  __device__ __forceinline__ uint32_t take(uint32_t& zmax) {
+    const uint32_t z = ffbl(lo);
+    zmax = zmax > z ? zmax : z;
+    const uint32_t c = z + 1u;
+    lo = __builtin_amdgcn_alignbit(hi, lo, c);
+    hi = hi >> c;
+    nb -= c;
+    return z;
+  }
+  // next code, any length; returns 0xFFFFFFFF if the run reaches `limit`
+  __device__ __forceinline__ uint32_t next_exact(uint32_t limit) {
+    uint64_t W = ((uint64_t)hi << 32) | lo;
     uint32_t q = 0;
-    while (W == 0ull) {                     // rare: the run is longer than the window
+    while (W == 0ull) {
       q += nb;
-      pos += nb;
-      if (pos >= limit) return 0xFFFFFFFFu;
+      if (idx * 32u >= limit) return 0xFFFFFFFFu;
       W = ((uint64_t)s[idx + 1] << 32) | s[idx];
-      idx += 2;
+      idx += 2u;
       nb = 64u;
     }
-    const uint32_t lo = (uint32_t)W, hi = (uint32_t)(W >> 32);
-    const uint32_t z = lo != 0u ? (uint32_t)__builtin_ctz(lo) : 32u + (uint32_t)__builtin_ctz(hi);
+    const uint32_t l = (uint32_t)W, h = (uint32_t)(W >> 32);
+    const uint32_t z = l != 0u ? (uint32_t)__builtin_ctz(l) : 32u + (uint32_t)__builtin_ctz(h);
     W = (W >> z) >> 1;
     nb -= z + 1u;
-    pos += z + 1u;
+    lo = (uint32_t)W;
+    hi = (uint32_t)(W >> 32);
     return q + z;
   }
 };
+
+// Bits [o, o + w) of the little-endian bit string seg[] (w <= 32).  Called
+// with o and w fixed by fully unrolled loops, so seg[] is indexed statically.
+__device__ __forceinline__ uint32_t seg_bits(const uint32_t* seg, int o, int w) {
+  const int j = o >> 5, b = o & 31;
+  if (b + w <= 32) return __builtin_amdgcn_ubfe(seg[j], b, w);
+  return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(seg[j + 1], seg[j], b), 0, w);
+}
+
+// Signed coordinate of the e-th code of a lane: unzigzag((q << K) | r) with r
+// the e-th K-bit field of the remainder plane.  The zigzag sign is r's low
+// bit (as 0 / -1); the magnitude is q above r's upper K-1 bits.
+template <int K>
+__device__ __forceinline__ int32_t code_coord(const uint32_t* seg, int e, uint32_t qz) {
+  if constexpr (K == 0) {
+    return (int32_t)(qz >> 1) ^ -(int32_t)(qz & 1u);
+  } else {
+    const int o = e * K;
+    const int32_t neg = __builtin_amdgcn_sbfe((int32_t)seg[o >> 5], o & 31, 1);
+    if constexpr (K == 1) return (int32_t)qz ^ neg;
+    else return (int32_t)((qz << (K - 1)) | seg_bits(seg, o + 1, K - 1)) ^ neg;
+  }
+}
 
 // position (0..31) of the r-th set bit (r counted from 0) of w; w has > r ones
 __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {

@@ -1,0 +1,9 @@
+// hq_kern_d4.hip — the D4 lattice's encode and decode kernels (every tile
+// size, with and without the KV dither), instantiated in a translation unit
+// of their own so that the four lattices compile in parallel.
+#include "hq_kernels.h"
+
+namespace hq {
+EncFn enc_fn_d4(uint32_t n, bool dither) { return enc_table<4>(n, dither); }
+DecFn dec_fn_d4(uint32_t n, bool dither) { return dec_table<4>(n, dither); }
+}  // namespace hq

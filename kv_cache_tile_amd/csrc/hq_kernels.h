@@ -1,0 +1,651 @@
+// hq_kernels.h — the HyperQuant encode and decode kernels for gfx950.
+//
+// Method: "HyperQuant: A Rate-Distortion-Optimal Quantization Pipeline for
+// Large Language and Diffusion Models", gist.science explainer, section
+// "Methodology: The HyperQuant Pipeline", components 1-4 (RHT, lattice,
+// bit-stripping + Rice, KV dither).
+//
+// Encode: one workgroup = one chunk of 64 tiles at a time (persistent
+// workgroups take chunks from an atomic ticket).  Lane q of a tile holds its
+// elements 32q..32q+31: load, sign flip, butterfly, scale, lattice search,
+// symbols and the Rice parameter are all in registers; tile lengths are
+// scanned within the chunk, the chunk's word offset in the stream comes from
+// a decoupled look-back over earlier chunks' published sizes, and the bits
+// are packed into LDS and written out with coalesced stores.
+// Decode: one workgroup per unit of tiles of a chunk (grid-strided): the
+// unit's bits are staged in LDS, each lane finds where its unary codes start
+// (a popcount scan), parses its 32 codes with a reader specialised on the
+// tile's Rice parameter, rebuilds the lattice points, runs the butterfly and
+// stores.
+//
+// The templates are instantiated once per lattice, in hq_kern_<lattice>.hip
+// (separate translation units, built in parallel); hq_lib.hip holds the host
+// side and reaches the kernels through the tables declared at the end.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "hq.h"
+#include "hq_device.h"
+
+namespace hq {
+
+// Look-back words: (epoch << 34) | (flag << 32) | value.  The value travels
+// inside the atomic word itself, so relaxed agent-scope atomics suffice: no
+// other memory is published through them (release/acquire at agent scope
+// would write back / invalidate the whole L2 of the XCD on every chunk).
+constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
+constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+
+// --------------------------------------------------------------------------
+// Encode kernel
+// --------------------------------------------------------------------------
+template <int LAT, int N, bool DITHER>
+__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems)) __attribute__((amdgpu_waves_per_eu(4)))
+encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
+              uint32_t key_sign, uint32_t key_dither, A2Consts a2,
+              uint32_t* __restrict__ payload, uint64_t cap_words,
+              uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
+              uint32_t* __restrict__ chunk_off, uint32_t* __restrict__ status,
+              uint32_t* __restrict__ ws, uint32_t stage_words) {
+  constexpr int LPT = N / kLaneElems;                       // lanes per tile
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
+  constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;   // coset bits per lane
+  constexpr uint32_t B = CB_LANE * LPT;                     // coset bits per tile
+
+  extern __shared__ uint32_t smem[];
+  uint32_t* stage = smem;                                   // [stage_words]
+  uint32_t* tile_len = smem + stage_words;                  // [64]
+  uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
+  uint32_t* misc = tile_off + kChunkTiles;                  // [4]
+
+  const int tid = threadIdx.x;
+  const int tau = tid / LPT;
+  const int q = tid % LPT;
+  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);
+
+  // sign diagonal entries of this lane's 32 positions (Methodology 1)
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+
+  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
+
+  if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t epoch = misc[2] & kEpochMask;
+
+  for (;;) {
+    if (tid == 0) {
+      uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      misc[0] = tk;
+      if ((uint64_t)tk == C + gridDim.x - 1) {               // last ticket: all taken, reset for next call
+        __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    const uint64_t chunk = misc[0];
+    if (chunk >= C) break;
+
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const bool active = t < T;
+
+    // ---- load + sign (bf16 -> fp32 is exact) ----
+    float a[kLaneElems];
+    if (active) {
+      const uint64_t base = t * N + (uint64_t)q * kLaneElems;
+      if (bf16) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          uint4 w = p[v];
+          uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int h = 0; h < 4; h++) {
+            a[v * 8 + 2 * h] = as_f(ww[h] << 16);
+            a[v * 8 + 2 * h + 1] = as_f(ww[h] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
+#pragma unroll
+        for (int v = 0; v < 8; v++) {
+          float4 w = p[v];
+          a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ (((sgn >> i) & 1u) << 31));
+
+    // ---- RHT: butterfly, then 1/sqrt(n) (with the lane's butterfly sign) ----
+    fwht_tile_signed<LPT>(a, q);
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * lane_scale;
+
+    // ---- tile energy: pairwise tree over the tile, step = bf16(rms * c) ----
+    float sq[kLaneElems];
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) sq[i] = a[i] * a[i];
+#pragma unroll
+    for (int m = kLaneElems; m > 1; m >>= 1) {
+#pragma unroll
+      for (int i = 0; i < m / 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+    }
+    float ss = sq[0];
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) ss = ss + __shfl_xor(ss, m);
+    bool nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
+    float s = 0.0f;
+    uint32_t sbits = 0;
+    if (!nonfinite) {
+      float rms = sqrtf(ss * inv_n);
+      float r = rms * c;
+      sbits = bf16_rne_bits(r);
+      if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
+      else if ((sbits & 0x7F80u) == 0) sbits = 0;
+      s = as_f(sbits << 16);
+    }
+    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = nonfinite ? 0.0f : a[i] * inv;
+
+    // ---- KV: add the dither (Methodology 4) ----
+    if constexpr (DITHER) {
+      const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
+#pragma unroll
+      for (int b = 0; b < BPL; b++) {
+        float u[D];
+        dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), u, a2);
+#pragma unroll
+        for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + u[i];
+      }
+    }
+
+    // ---- nearest lattice point, strip, zigzag ----
+    uint32_t sym[kLaneElems];
+    uint32_t cb = 0;
+#pragma unroll
+    for (int b = 0; b < BPL; b++) {
+      int32_t d[D];
+      uint32_t p;
+      nearest<LAT>(&a[b * D], d, p, a2);
+      block_symbols<LAT>(d, &sym[b * D]);
+      cb |= p << b;
+    }
+
+    // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
+    // S[k] = sum of sym >> k over this lane.  When every symbol of the wave
+    // fits a byte, four symbols share a register and one shift, one mask and
+    // one byte-sum (v_sad_u8) add four terms.
+    uint32_t S[8];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) mx |= sym[i];
+    if (__all(mx < 256u)) {
+      uint32_t P[kLaneElems / 4];
+#pragma unroll
+      for (int j = 0; j < kLaneElems / 4; j++)
+        P[j] = sym[4 * j] | (sym[4 * j + 1] << 8) | (sym[4 * j + 2] << 16) | (sym[4 * j + 3] << 24);
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const uint32_t bmask = 0x01010101u * (0xFFu >> k);
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> k) & bmask, 0u, acc);
+        S[k] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> k;
+        S[k] = acc;
+      }
+    }
+    uint32_t best_k = 0, best_c = 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t tot = S[k];
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+      uint32_t cost = tot + (uint32_t)N * (1u + k);
+      if (cost < best_c) { best_c = cost; best_k = k; }
+    }
+    const uint32_t k = best_k;
+    // this lane's unary quotients: sum (q_i + 1) bits; exclusive prefix over the tile's lanes
+    uint32_t lane_unary = 0;
+#pragma unroll
+    for (int kk = 0; kk < 8; kk++) if (kk == (int)k) lane_unary = S[kk];
+    lane_unary += (uint32_t)kLaneElems;
+    uint32_t incl = lane_unary;
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) {
+      uint32_t v = __shfl_up(incl, m, LPT);
+      if (q >= m) incl += v;
+    }
+    const uint32_t lane_excl = incl - lane_unary;
+    const uint32_t tlen = B + best_c;
+    if (q == 0) tile_len[tau] = active ? tlen : 0u;
+    __syncthreads();
+
+    // ---- chunk scan: bit offset of every tile inside the chunk ----
+    if (tid < kChunkTiles) {
+      uint32_t v = tile_len[tid], inc = v;
+#pragma unroll
+      for (int m = 1; m < kChunkTiles; m <<= 1) {
+        uint32_t o = __shfl_up(inc, m, kChunkTiles);
+        if (tid >= m) inc += o;
+      }
+      tile_off[tid] = inc - v;
+      if (tid == kChunkTiles - 1) misc[1] = inc;
+    }
+    __syncthreads();
+    const uint32_t total_bits = misc[1];
+    uint32_t W = (total_bits + 31u) >> 5;
+    const bool fits = W + 2 <= stage_words;
+
+    // publish this chunk's size early so later chunks can look back past it
+    if (tid == 0) {
+      uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
+      __hip_atomic_store(&look[chunk], (tag << 32) | W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (uint32_t i = tid; i < W + 2 && i < stage_words; i += blockDim.x) stage[i] = 0u;
+    __syncthreads();
+
+    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane ----
+    if (active && fits) {
+      const uint32_t t0 = tile_off[tau];
+      if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
+      if (k > 0) {
+        // four k-bit remainders (at most 28 bits) per OR into the staging bits
+        const uint32_t rmask = (1u << k) - 1u;
+        uint32_t rpos = t0 + B + (uint32_t)q * kLaneElems * k;
+#pragma unroll
+        for (int g = 0; g < kLaneElems / 4; g++) {
+          const uint32_t f = (sym[4 * g] & rmask) | ((sym[4 * g + 1] & rmask) << k) |
+                             ((sym[4 * g + 2] & rmask) << (2u * k)) | ((sym[4 * g + 3] & rmask) << (3u * k));
+          lds_or_bits(stage, rpos, f, 4u * k);
+          rpos += 4u * k;
+        }
+      }
+      uint32_t upos = t0 + B + (uint32_t)N * k + lane_excl;
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) {
+        upos += sym[i] >> k;
+        atomicOr(&stage[upos >> 5], 1u << (upos & 31u));
+        upos += 1u;
+      }
+    }
+    __syncthreads();
+
+    // ---- decoupled look-back, one predecessor per lane of wave 0 ----
+    if (tid < 64) {
+      uint32_t excl = 0;
+      if (chunk > 0) {
+        int64_t base = (int64_t)chunk - 1;
+        for (;;) {
+          const int64_t j = base - tid;
+          uint64_t v;
+          uint32_t flag;
+          if (j < 0) {
+            v = 0;
+            flag = kFlagIncl;                                // before chunk 0: prefix 0
+          } else {
+            for (;;) {
+              v = __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const uint32_t hi = (uint32_t)(v >> 32);
+              if ((hi >> 2) == epoch && (hi & 3u) != 0) { flag = hi & 3u; break; }
+              __builtin_amdgcn_s_sleep(1);
+            }
+          }
+          const uint64_t incl_mask = __ballot(flag == kFlagIncl);
+          const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
+          uint32_t part = (tid <= first) ? (uint32_t)v : 0u;
+#pragma unroll
+          for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m);
+          excl += part;
+          if (incl_mask) break;
+          base -= 64;
+        }
+      }
+      if (tid == 0) {
+        if (chunk > 0) {
+          uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
+          __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        misc[3] = excl;
+        chunk_off[chunk] = excl;
+        if (chunk == C - 1) chunk_off[C] = excl + W;
+        if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+      }
+    }
+    __syncthreads();
+    const uint32_t excl = misc[3];
+    if (fits && (uint64_t)excl + W <= cap_words) {
+      for (uint32_t i = tid; i < W; i += blockDim.x) payload[excl + i] = stage[i];
+    }
+    if (active && q == 0) {
+      step_out[t] = (uint16_t)sbits;
+      meta_out[t] = (uint16_t)((tlen << 3) | k);
+      if (nonfinite) atomicOr(status, HQ_FLAG_NONFINITE);
+    }
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------------------
+// Decode kernel
+// --------------------------------------------------------------------------
+// decode work unit: TPW tiles of a chunk (a half chunk at n = 256, so that
+// workgroups stay at 256 threads and several fit on a CU)
+template <int N>
+struct DecodeGeom {
+  static constexpr int LPT = N / kLaneElems;
+  static constexpr int TPW = (256 / LPT) < kChunkTiles ? (256 / LPT) : kChunkTiles;
+  static constexpr int SUB = kChunkTiles / TPW;
+  static constexpr int THREADS = TPW * LPT;
+};
+
+// Rice parse and lattice rebuild of one lane's 32 codes for Rice parameter
+// K: a[e] = (lattice point - dither) * s.  Remainders come from the lane's
+// K-bit fields (static offsets), quotients from the unary window, 8 codes per
+// group; a group whose fast read saw a run of 31+ zeros (or ran out of window)
+// is read again exactly.  Returns false if the codes are not a valid stream
+// (a symbol above 16 bits, or a run past `end`); `upos` is left at the bit
+// after the lane's last code.
+template <int LAT, bool DITHER, int K>
+__device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, uint32_t u0, uint32_t end,
+                                           uint32_t cbits, float s, uint32_t key_dither, uint32_t g_lane,
+                                           A2Consts a2, float (&a)[kLaneElems], uint32_t& upos) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+  uint32_t seg[K + 1];
+  seg[K] = 0u;
+  if constexpr (K > 0) {
+    const uint32_t base = rb >> 5, sh = rb & 31u;
+    uint32_t raw[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; j++) raw[j] = stage[base + j];
+#pragma unroll
+    for (int j = 0; j < K; j++) seg[j] = __builtin_amdgcn_alignbit(raw[j + 1], raw[j], sh);
+  }
+  UnaryWindow uw;
+  uw.init(stage, u0);
+  bool ok = true;
+  // E8 without dither: (d + p/2) * s as one fma, exact for every finite s;
+  // for s = +-0 the addend -0 keeps the sign of d * s
+  const float zero_add = (s == 0.0f) ? -0.0f : 0.0f;
+  const float half_s = 0.5f * s;
+#pragma unroll
+  for (int g = 0; g < kLaneElems / 8; g++) {
+    uw.refill();
+    const UnaryWindow saved = uw;
+    uint32_t z[8], zmax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) z[i] = uw.take(zmax);
+    if (__any(zmax >= 31u)) {
+      if (zmax >= 31u) {
+        // rare: read the group again exactly (a rolled loop; codes shift in from the top)
+        uw = saved;
+#pragma unroll 1
+        for (int i = 0; i < 8; i++) {
+          uint32_t qv = uw.next_exact(end);
+          if (qv > (0xFFFFu >> K)) { ok = false; qv = 0u; }
+#pragma unroll
+          for (int j = 0; j < 7; j++) z[j] = z[j + 1];
+          z[7] = qv;
+        }
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < 8 / D; bb++) {
+      const int b = g * (8 / D) + bb;                       // block index in the lane
+      int32_t d[D];
+#pragma unroll
+      for (int i = 0; i < D; i++) d[i] = code_coord<K>(seg, b * D + i, z[bb * D + i]);
+      if constexpr (LAT == 4 || LAT == 8) {
+        int32_t par = 0;
+#pragma unroll
+        for (int i = 0; i < D - 1; i++) par ^= d[i];
+        d[D - 1] = (int32_t)(((uint32_t)d[D - 1] << 1) | ((uint32_t)par & 1u));
+      }
+      const uint32_t p = (cbits >> b) & 1u;
+      if constexpr (LAT == 8 && !DITHER) {
+        const float add = p ? half_s : zero_add;
+#pragma unroll
+        for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf((float)d[i], s, add);
+      } else {
+        float pt[D];
+        code_point<LAT>(d, p, pt, a2);
+        if constexpr (DITHER) {
+          float du[D];
+          dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), du, a2);
+#pragma unroll
+          for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
+        }
+#pragma unroll
+        for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
+      }
+    }
+  }
+  upos = uw.pos();
+  return ok;
+}
+
+template <int LAT, int N, bool DITHER>
+__global__ void __launch_bounds__(DecodeGeom<N>::THREADS)
+decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
+              const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
+              const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
+              uint32_t key_sign, uint32_t key_dither, A2Consts a2, void* __restrict__ out, uint32_t bf16,
+              uint32_t* __restrict__ status, uint32_t stage_words, uint32_t chunk_cap_words,
+              uint32_t tile_bound) {
+  constexpr int LPT = N / kLaneElems;
+  constexpr int TPW = DecodeGeom<N>::TPW;
+  constexpr int SUB = DecodeGeom<N>::SUB;
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr int BPL = kLaneElems / D;
+  constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
+  constexpr uint32_t B = CB_LANE * LPT;
+
+  extern __shared__ uint32_t smem[];
+  uint32_t* stage = smem;                                   // [stage_words] this unit's bits + guard
+  uint32_t* tile_off = stage + stage_words;                 // [64] bit offset of each tile in the chunk
+  uint32_t* tile_ok = tile_off + kChunkTiles;               // [64]
+  uint32_t* ustart = tile_ok + kChunkTiles;                 // [TPW * LPT] first unary bit per lane
+  uint32_t* misc = ustart + TPW * LPT;                      // [4]
+
+  const int tid = threadIdx.x;
+  const int tau = tid / LPT;
+  const int q = tid % LPT;
+
+  uint32_t sgn = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
+
+  const uint64_t units = C * SUB;
+  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const uint64_t chunk = unit / SUB;
+    const int first = (int)(unit % SUB) * TPW;              // first tile of this unit in the chunk
+    const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
+    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) <= chunk_cap_words;
+
+    // tile offsets inside the chunk; a chunk whose size disagrees with its tiles is dropped
+    if (tid < kChunkTiles) {
+      const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
+      const uint32_t m = tt < T ? (uint32_t)meta[tt] : 0u;
+      const uint32_t len = m >> 3, kk = m & 7u;
+      uint32_t inc = len;
+#pragma unroll
+      for (int s2 = 1; s2 < kChunkTiles; s2 <<= 1) {
+        uint32_t o = __shfl_up(inc, s2, kChunkTiles);
+        if (tid >= s2) inc += o;
+      }
+      tile_off[tid] = inc - len;
+      const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
+      const bool too_long = __any(len > tile_bound);        // longer than any valid tile can be
+      const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == w1 - w0;
+      tile_ok[tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
+      // this unit's bit range [tile_off[first], tile_off[first + TPW]) in whole words
+      if (tid == first) misc[0] = chunk_ok ? (inc - len) : 0u;
+      if (tid == first + TPW - 1) misc[1] = chunk_ok ? inc : 0u;
+    }
+    __syncthreads();
+    const uint32_t sw = misc[0] >> 5;                       // first staged word (chunk-relative)
+    const uint32_t WL = ((misc[1] + 31u) >> 5) - sw;        // words staged
+    const uint32_t base_bit = sw * 32u;
+    for (uint32_t i = tid; i < WL; i += blockDim.x) stage[i] = payload[w0 + sw + i];
+    if (tid < 8) stage[WL + tid] = 0u;                      // guard words for the readers
+    __syncthreads();
+
+    const int ct = first + tau;                             // tile index in the chunk
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)ct;
+    const bool active = t < T;
+    const uint32_t m = active ? (uint32_t)meta[t] : 0u;
+    const uint32_t len = m >> 3, k = m & 7u;
+    const uint32_t sraw = active ? (uint32_t)step[t] : 0u;
+    // a non-finite step is never written by the encoder: corrupt tile
+    bool ok = active && tile_ok[ct] != 0u && (sraw & 0x7F80u) != 0x7F80u;
+    const uint32_t start = tile_off[ct] - base_bit, end = start + len;
+    const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
+
+    // ---- where does each lane's first unary code start?  Every codeword has
+    // exactly one 1 in the unary plane: count ones word by word (lane q takes
+    // words q, q+LPT, ...) and mark the bit after the (32 q)-th one. ----
+    const uint32_t words = ok ? (end - ub + 31u) >> 5 : 0u;
+    uint32_t carry = 0;
+    for (uint32_t r = 0;; r++) {
+      const bool more = r * LPT < words;
+      if (!__any(more)) break;
+      const uint32_t j = r * LPT + (uint32_t)q;
+      uint32_t w = 0;
+      if (j < words) {
+        const uint32_t p = ub + 32u * j;
+        w = lds_read32(stage, p);
+        const uint32_t valid = end - p;
+        if (valid < 32u) w &= (1u << valid) - 1u;
+      }
+      const uint32_t c = __builtin_popcount(w);
+      uint32_t inc = c;
+#pragma unroll
+      for (int s2 = 1; s2 < LPT; s2 <<= 1) {
+        uint32_t o = __shfl_up(inc, s2, LPT);
+        if (q >= s2) inc += o;
+      }
+      const uint32_t before = carry + inc - c, after = carry + inc;
+      const uint32_t mm = before / 32u + 1u;
+      if (c != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
+        ustart[tau * LPT + mm] = ub + 32u * j + select_bit(w, 32u * mm - before - 1u) + 1u;
+      carry += __shfl(inc, LPT - 1, LPT);
+    }
+    ok = ok && carry == (uint32_t)N;
+    __syncthreads();
+
+    // ---- parse and rebuild, specialised on the tile's Rice parameter; a lane
+    // of an invalid tile reads from bit 0 with no run limit (in bounds, result
+    // discarded) ----
+    float a[kLaneElems];
+    bool lane_ok;
+    {
+      const float s = as_f(sraw << 16);
+      uint32_t cbits = 0;
+      if constexpr (CB_LANE > 0) cbits = lds_read32(stage, ok ? start + (uint32_t)q * CB_LANE : 0u);
+      const uint32_t rb = ok ? start + B + (uint32_t)q * kLaneElems * k : 0u;
+      const uint32_t u0 = ok ? (q == 0 ? ub : ustart[tau * LPT + q]) : 0u;
+      const uint32_t lim = ok ? end : 0u;
+      const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
+      uint32_t upos = 0;
+      bool pok;
+      switch (k) {
+#define HQ_PARSE_CASE(KK) \
+        case KK: pok = parse_lane<LAT, DITHER, KK>(stage, rb, u0, lim, cbits, s, key_dither, g_lane, a2, a, upos); break;
+        HQ_PARSE_CASE(0) HQ_PARSE_CASE(1) HQ_PARSE_CASE(2) HQ_PARSE_CASE(3)
+        HQ_PARSE_CASE(4) HQ_PARSE_CASE(5) HQ_PARSE_CASE(6)
+        default: pok = parse_lane<LAT, DITHER, 7>(stage, rb, u0, lim, cbits, s, key_dither, g_lane, a2, a, upos); break;
+#undef HQ_PARSE_CASE
+      }
+      lane_ok = ok && pok;
+      if (q == LPT - 1 && upos != end) lane_ok = false;      // the last one ends the tile
+    }
+    // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
+    int all_ok = lane_ok ? 1 : 0;
+#pragma unroll
+    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
+    lane_ok = all_ok != 0;
+
+    // ---- inverse RHT and store (an invalid tile decodes to zeros) ----
+    if (active) {
+      if (!lane_ok) {
+        if (q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+      }
+      fwht_tile_signed<LPT>(a, q);
+      // lane q holds (-1)^popcount(q) times the butterfly output: fold that
+      // sign into the scale; + 0.0f turns a -0 into +0 (every zero of the
+      // exact butterfly is +0), then apply the sign diagonal
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) {
+        const float o = a[i] * lane_scale + 0.0f;
+        a[i] = as_f(as_u(o) ^ (((sgn >> i) & 1u) << 31));
+      }
+      const uint64_t base = t * N + (uint64_t)q * kLaneElems;
+      if (bf16) {
+        uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; h++) w[h] = bf16x2_rne(a[v * 8 + 2 * h], a[v * 8 + 2 * h + 1]);
+          p[v] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else {
+        float4* p = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + base);
+#pragma unroll
+        for (int v = 0; v < 8; v++) p[v] = make_float4(a[v * 4], a[v * 4 + 1], a[v * 4 + 2], a[v * 4 + 3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---- per-lattice kernel tables (defined in hq_kern_<lattice>.hip) ----------
+using EncFn = void (*)(const void*, uint32_t, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t,
+                       A2Consts, uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*,
+                       uint32_t);
+using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
+                       uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t, uint32_t*, uint32_t,
+                       uint32_t, uint32_t);
+
+template <int LAT>
+EncFn enc_table(uint32_t n, bool dither) {
+  if (n == 64) return dither ? encode_kernel<LAT, 64, true> : encode_kernel<LAT, 64, false>;
+  if (n == 128) return dither ? encode_kernel<LAT, 128, true> : encode_kernel<LAT, 128, false>;
+  return dither ? encode_kernel<LAT, 256, true> : encode_kernel<LAT, 256, false>;
+}
+template <int LAT>
+DecFn dec_table(uint32_t n, bool dither) {
+  if (n == 64) return dither ? decode_kernel<LAT, 64, true> : decode_kernel<LAT, 64, false>;
+  if (n == 128) return dither ? decode_kernel<LAT, 128, true> : decode_kernel<LAT, 128, false>;
+  return dither ? decode_kernel<LAT, 256, true> : decode_kernel<LAT, 256, false>;
+}
+
+EncFn enc_fn_z(uint32_t n, bool dither);
+EncFn enc_fn_a2(uint32_t n, bool dither);
+EncFn enc_fn_d4(uint32_t n, bool dither);
+EncFn enc_fn_e8(uint32_t n, bool dither);
+DecFn dec_fn_z(uint32_t n, bool dither);
+DecFn dec_fn_a2(uint32_t n, bool dither);
+DecFn dec_fn_d4(uint32_t n, bool dither);
+DecFn dec_fn_e8(uint32_t n, bool dither);
+
+}  // namespace hq

@@ -573,11 +573,14 @@ int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t
 /* bits, and every tile of a chunk whose word count disagrees with its      */
 /* tiles' lengths, exceeds the capacity bound or holds a tile longer than   */
 /* the per-tile bound, decode to zero (+0 with                              */
-/* the sign diagonal applied, no dither) and are reported.  Valid streams   */
-/* never meet these conditions.                                             */
+/* the sign diagonal applied, no dither) and are reported.  So does a tile  */
+/* whose step is not a finite bf16 (the encoder stores the bf16 of a finite */
+/* RMS times c, or 0).  Valid streams never meet these conditions.          */
 /* ------------------------------------------------------------------------ */
 
 /* parse one tile starting at bit b (reads never reach bend); 0 = ok */
+static int step_bad(uint16_t step) { return (step & 0x7F80u) == 0x7F80u; }
+
 static int parse_tile(const uint32_t *w, uint64_t b, uint64_t bend, uint32_t len, uint32_t k,
                       uint32_t n, uint32_t nb, uint32_t *cos, uint32_t *sym)
 {
@@ -657,7 +660,7 @@ int hqo_decode(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk
         uint64_t b = w0 * 32, bend = w1 * 32;
         for (uint64_t t = t0; t < t1; t++) {
             uint32_t len = meta[t] >> 3, k = meta[t] & 7u;
-            int bad = chunk_bad || parse_tile(payload, b, bend, len, k, n, nb, cos, sym);
+            int bad = chunk_bad || step_bad(step[t]) || parse_tile(payload, b, bend, len, k, n, nb, cos, sym);
             if (bad) status = HQO_ECORRUPT;
             rebuild_tile(p, t, bad, step[t], cos, sym, x_out, t);
             b += len;
@@ -678,7 +681,7 @@ int hqo_decode_tiles(const uint16_t *step, const uint16_t *meta, const uint32_t 
     uint64_t b = 0;
     for (uint64_t t = t0; t < t1; t++) {
         uint32_t len = meta[t - t0] >> 3, k = meta[t - t0] & 7u;
-        int bad = parse_tile(bits, b, bits_words * 32, len, k, n, nb, cos, sym);
+        int bad = step_bad(step[t - t0]) || parse_tile(bits, b, bits_words * 32, len, k, n, nb, cos, sym);
         if (bad) status = HQO_ECORRUPT;
         rebuild_tile(p, t, bad, step[t - t0], cos, sym, x_out, t - t0);
         b += len;

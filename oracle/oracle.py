@@ -29,7 +29,9 @@ CHUNK_TILES = 64
 
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (plain C99, no contraction, no fast-math)."""
-    if force or not os.path.exists(LIB_PATH):
+    stale = not os.path.exists(LIB_PATH) or any(
+        os.path.getmtime(f) > os.path.getmtime(LIB_PATH) for f in (SRC, os.path.join(HERE, "hq_oracle.h")))
+    if force or stale:
         tmp = LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
         os.replace(tmp, LIB_PATH)

@@ -138,22 +138,25 @@ def test_decoder_on_oracle_streams_and_corruption():
     c = rate_c(lat, n, 4.0)
     e = oracle.encode(x, n, lat, c, 4)
     rng = np.random.default_rng(0)
-    for trial in range(12):
+    for trial in range(16):
         pay = e.payload.copy()
         meta = e.meta.copy()
         off = e.chunk_off.copy()
-        if trial % 3 == 0:
+        step = e.step.copy()
+        if trial % 4 == 0:
             for _ in range(3):
                 w = rng.integers(0, pay.size)
                 pay[w] ^= np.uint32(1) << np.uint32(rng.integers(0, 32))
-        elif trial % 3 == 1:
+        elif trial % 4 == 1:
             meta[rng.integers(0, meta.size)] += np.uint16(8 * int(rng.integers(1, 4)))
-        else:
+        elif trial % 4 == 2:
             off[1 + rng.integers(0, off.size - 1)] -= 1
-        ee = oracle.Encoded(e.step, meta, off, pay, 0)
+        else:                                                # a non-finite step: corrupt tile
+            step[rng.integers(0, step.size)] = (0x7F80, 0xFF80, 0x7FC0, 0x7F81)[trial // 4]
+        ee = oracle.Encoded(step, meta, off, pay, 0)
         ref, st = oracle.decode(ee, 200, n, n, lat, c, 4, oracle.F32)
         h = hq.HQTensor(torch.from_numpy(pay.view(np.int32)).to(_dev()),
-                        torch.from_numpy(e.step.view(np.int16)).to(_dev()),
+                        torch.from_numpy(step.view(np.int16)).to(_dev()),
                         torch.from_numpy(meta.view(np.int16)).to(_dev()),
                         torch.from_numpy(off.view(np.int32)).to(_dev()),
                         torch.zeros(1, dtype=torch.int32, device=_dev()), (200, n), torch.float32, n, lat, 4.0, 4)

@@ -208,6 +208,29 @@ def test_corrupt_streams_are_rejected_not_crashing():
     assert st == oracle.ECORRUPT
 
 
+def test_nonfinite_step_decodes_as_corrupt_tile():
+    # the encoder stores bf16(RMS * c) or 0, never an infinity or a NaN: a tile
+    # that carries one is corrupt and decodes to zeros (the sign diagonal's
+    # signed zeros), the other tiles are untouched
+    x = workloads.gaussian(64, 128, key=4)
+    c = rate_c("E8", 128, 4.0)
+    e = oracle.encode(x, 128, "E8", c, 9)
+    clean, st = oracle.decode(e, 64, 128, 128, "E8", c, 9, oracle.F32)
+    assert st == oracle.OK
+    sign = oracle.sign_bits(9, 128).astype(np.uint32) << np.uint32(31)
+    for bad in (0x7F80, 0xFF80, 0x7FC0, 0x7F81):
+        step = e.step.copy()
+        step[5] = bad
+        out, st = oracle.decode(oracle.Encoded(step, e.meta, e.chunk_off, e.payload, 0), 64, 128, 128, "E8",
+                                c, 9, oracle.F32)
+        assert st == oracle.ECORRUPT
+        ob = out.view(np.uint32).reshape(-1, 128)
+        np.testing.assert_array_equal(ob[5], sign)
+        keep = np.ones(64, bool)
+        keep[5] = False
+        np.testing.assert_array_equal(ob[keep], clean.view(np.uint32).reshape(-1, 128)[keep])
+
+
 def test_payload_bound_holds_on_adversarial_tiles():
     # spikes, constants, alternating signs, heavy tails: the measured length of
     # every tile stays below the capacity bound used to size buffers
