@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "encode/decode GB/s of bf16 input (E8, 4 bps) at 1 GPU; % of HBM peak"
-KERNEL_SOURCES = ("kv_cache_tile_amd/csrc/hq_lib.hip", "kv_cache_tile_amd/csrc/hq_device.h")
+KERNEL_SOURCES = ("kv_cache_tile_amd/csrc/hq_lib.hip", "kv_cache_tile_amd/csrc/hq_kernels.h",
+                  "kv_cache_tile_amd/csrc/hq_device.h", "kv_cache_tile_amd/csrc/hq_kern_e8.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_hbm_traffic.json")
 
 

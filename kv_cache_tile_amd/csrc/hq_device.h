@@ -132,6 +132,61 @@ __device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t&
   p = useB ? 1u : 0u;
 }
 
+// E8 straight to Rice symbols, for the encoder's quantiser: the same choice
+// and tie rules as nearest_e8 followed by block_symbols, arranged for fewer
+// operations.  With f = rint(t) and delta = t - f:
+//  - floor(t) = f - [delta < 0], so the half-integer candidate's coset parity
+//    is f's parity flipped by the number of negative deltas (an XOR of signs);
+//  - the moved coordinate is the first one whose |delta| equals the max (A)
+//    or the min (B); one chain finds it and carries its delta;
+//  - A moves it by +1 if delta >= 0 else -1; B moves floor(t) by +1 if
+//    t >= floor(t) + 1/2, i.e. if delta < 0 or delta == 1/2, else by -1.
+__device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, uint32_t& p) {
+  float dl[8], ad[8];
+  int32_t fi[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float f = __builtin_rintf(t[i]);
+    dl[i] = t[i] - f;
+    ad[i] = __builtin_fabsf(dl[i]);
+    fi[i] = (int32_t)f;
+  }
+  const uint32_t px = (uint32_t)(((fi[0] ^ fi[1]) ^ (fi[2] ^ fi[3])) ^ ((fi[4] ^ fi[5]) ^ (fi[6] ^ fi[7])));
+  const uint32_t pn = ((as_u(dl[0]) ^ as_u(dl[1])) ^ (as_u(dl[2]) ^ as_u(dl[3]))) ^
+                      ((as_u(dl[4]) ^ as_u(dl[5])) ^ (as_u(dl[6]) ^ as_u(dl[7])));
+  const bool oddA = (px & 1u) != 0u;
+  const bool oddB = oddA != ((pn >> 31) != 0u);
+  const float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(ad[0], ad[1]), __builtin_fmaxf(ad[2], ad[3])),
+                                   __builtin_fmaxf(__builtin_fmaxf(ad[4], ad[5]), __builtin_fmaxf(ad[6], ad[7])));
+  const float mn = __builtin_fminf(__builtin_fminf(__builtin_fminf(ad[0], ad[1]), __builtin_fminf(ad[2], ad[3])),
+                                   __builtin_fminf(__builtin_fminf(ad[4], ad[5]), __builtin_fminf(ad[6], ad[7])));
+  const float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
+  float diff = sabs - 2.0f;
+  if (oddA) diff = diff + (1.0f - 2.0f * mx);
+  if (oddB) diff = diff - 2.0f * mn;
+  const bool useB = diff > 0.0f;
+  const float target = useB ? mn : mx;
+  int j = 7;
+  float dlj = dl[7];
+#pragma unroll
+  for (int i = 6; i >= 0; i--) {
+    const bool eq = ad[i] == target;
+    j = eq ? i : j;
+    dlj = eq ? dl[i] : dlj;
+  }
+  const bool odd = useB ? oddB : oddA;
+  const bool up = useB ? (dlj < 0.0f || dlj == 0.5f) : (dlj >= 0.0f);
+  const int32_t delta = odd ? (up ? 1 : -1) : 0;
+  const int32_t floor_mask = useB ? -1 : 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    int32_t d = fi[i] + (((int32_t)as_u(dl[i]) >> 31) & floor_mask) + (i == j ? delta : 0);
+    if (i == 7) d >>= 1;                                   // stored halved: parity of the others' sum
+    u[i] = zigzag(d);
+  }
+  p = useB ? 1u : 0u;
+}
+
 // A2 = R u (R + (1/2, sqrt3/2)), R = Z x sqrt3 Z; code (p, m, n') with point
 // (m + p/2, sqrt3 (n' + p/2)).
 __device__ __forceinline__ void nearest_a2(const float* t, int32_t* d, uint32_t& p, A2Consts k) {

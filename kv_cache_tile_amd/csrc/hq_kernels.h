@@ -72,6 +72,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
 
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
+  uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
   if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -173,58 +174,103 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     uint32_t cb = 0;
 #pragma unroll
     for (int b = 0; b < BPL; b++) {
-      int32_t d[D];
       uint32_t p;
-      nearest<LAT>(&a[b * D], d, p, a2);
-      block_symbols<LAT>(d, &sym[b * D]);
+      if constexpr (LAT == 8) {
+        nearest_e8_symbols(&a[b * D], &sym[b * D], p);
+      } else {
+        int32_t d[D];
+        nearest<LAT>(&a[b * D], d, p, a2);
+        block_symbols<LAT>(d, &sym[b * D]);
+      }
       cb |= p << b;
     }
 
     // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
-    // S[k] = sum of sym >> k over this lane.  When every symbol of the wave
+    // cost(k) = S(k) + n (1 + k) with S(k) = sum of sym >> k is convex in k
+    // (S(k) - S(k+1) = sum ceil((sym >> k) / 2) does not grow with k), so the
+    // smallest minimiser is the first k with S(k) - S(k+1) <= n (7 if none).
+    // Three sums around the tile's previous k settle it when k has not moved;
+    // otherwise the wave computes all eight.  When every symbol of the wave
     // fits a byte, four symbols share a register and one shift, one mask and
     // one byte-sum (v_sad_u8) add four terms.
-    uint32_t S[8];
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < kLaneElems; i++) mx |= sym[i];
-    if (__all(mx < 256u)) {
-      uint32_t P[kLaneElems / 4];
+    const bool bytes = __all(mx < 256u);
+    uint32_t P[kLaneElems / 4];
 #pragma unroll
-      for (int j = 0; j < kLaneElems / 4; j++)
-        P[j] = sym[4 * j] | (sym[4 * j + 1] << 8) | (sym[4 * j + 2] << 16) | (sym[4 * j + 3] << 24);
+    for (int j = 0; j < kLaneElems / 4; j++)
+      P[j] = sym[4 * j] | (sym[4 * j + 1] << 8) | (sym[4 * j + 2] << 16) | (sym[4 * j + 3] << 24);
+    uint32_t k = 0, best_c = 0, lane_sum = 0;
+    bool settled = false;
+    if (bytes && k_prev < 8u) {
+      const uint32_t kb = k_prev == 0u ? 0u : (k_prev >= 6u ? 5u : k_prev - 1u);
+      uint32_t L[3], Tt[3];
 #pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const uint32_t bmask = 0x01010101u * (0xFFu >> k);
+      for (int jj = 0; jj < 3; jj++) {
+        const uint32_t kk = kb + (uint32_t)jj;
+        const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
         uint32_t acc = 0;
 #pragma unroll
-        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> k) & bmask, 0u, acc);
-        S[k] = acc;
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> kk) & bmask, 0u, acc);
+        L[jj] = acc;
+        uint32_t tot = acc;
+#pragma unroll
+        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+        Tt[jj] = tot;
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> k;
-        S[k] = acc;
+      const bool drop0 = Tt[0] - Tt[1] > (uint32_t)N, drop1 = Tt[1] - Tt[2] > (uint32_t)N;
+      int pick = -1;
+      if (kb == 0u && !drop0) pick = 0;
+      else if (drop0 && !drop1) pick = 1;
+      else if (kb == 5u && drop0 && drop1) pick = 2;
+      if (pick >= 0) {
+        settled = true;
+        k = kb + (uint32_t)pick;
+        const uint32_t tot = pick == 0 ? Tt[0] : (pick == 1 ? Tt[1] : Tt[2]);
+        lane_sum = pick == 0 ? L[0] : (pick == 1 ? L[1] : L[2]);
+        best_c = tot + (uint32_t)N * (1u + k);
       }
     }
-    uint32_t best_k = 0, best_c = 0xFFFFFFFFu;
+    if (__any(!settled)) {
+      uint32_t S[8];
+      if (bytes) {
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      uint32_t tot = S[k];
+        for (int kk = 0; kk < 8; kk++) {
+          const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
+          uint32_t acc = 0;
 #pragma unroll
-      for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
-      uint32_t cost = tot + (uint32_t)N * (1u + k);
-      if (cost < best_c) { best_c = cost; best_k = k; }
+          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> kk) & bmask, 0u, acc);
+          S[kk] = acc;
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> kk;
+          S[kk] = acc;
+        }
+      }
+      uint32_t bk = 0, bc = 0xFFFFFFFFu;
+#pragma unroll
+      for (int kk = 0; kk < 8; kk++) {
+        uint32_t tot = S[kk];
+#pragma unroll
+        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+        const uint32_t cost = tot + (uint32_t)N * (1u + kk);
+        if (cost < bc) { bc = cost; bk = kk; }
+      }
+      if (!settled) {
+        k = bk;
+        best_c = bc;
+#pragma unroll
+        for (int kk = 0; kk < 8; kk++) if (kk == (int)bk) lane_sum = S[kk];
+      }
     }
-    const uint32_t k = best_k;
+    k_prev = k;
     // this lane's unary quotients: sum (q_i + 1) bits; exclusive prefix over the tile's lanes
-    uint32_t lane_unary = 0;
-#pragma unroll
-    for (int kk = 0; kk < 8; kk++) if (kk == (int)k) lane_unary = S[kk];
-    lane_unary += (uint32_t)kLaneElems;
+    const uint32_t lane_unary = lane_sum + (uint32_t)kLaneElems;
     uint32_t incl = lane_unary;
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) {
