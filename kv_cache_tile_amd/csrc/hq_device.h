@@ -370,11 +370,29 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
   return base;
 }
 
-// The same butterfly for the encoder, with the cross-lane stages as one
-// fused multiply-add per element: the lane with the stage bit clear computes
-// own + partner, the other own - partner, which is the exact value
-// a_j - a_{j+h} negated (fma with a +-1 factor rounds once, like an add).
-// Each upper role flips the sign a lane holds, so on return lane q holds
+// One cross-lane stage on eight elements: a[o + i] += f * partner's a[o + i]
+// as v_fmac_f32_dpp, the partner selected by the DPP control.  One fused
+// multiply-add with a +-1 factor rounds once, like the butterfly's add.
+// s_nop 4: a VGPR written by a VALU op (or EXEC written by SALU) right
+// before must not be read through DPP within 2 (5) wait states.
+#define HQ_FMAC_DPP8(CTRL, a, o, f)                                                               \
+  asm("s_nop 4\n"                                                                                \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                           \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"                              \
+      : "+v"(a[(o) + 0]), "+v"(a[(o) + 1]), "+v"(a[(o) + 2]), "+v"(a[(o) + 3]), "+v"(a[(o) + 4]),  \
+        "+v"(a[(o) + 5]), "+v"(a[(o) + 6]), "+v"(a[(o) + 7])                                       \
+      : "v"(f))
+
+// The butterfly with the cross-lane stages as one fused multiply-add per
+// element: the lane with the stage bit clear computes own + partner, the
+// other own - partner, which is the exact value a_j - a_{j+h} negated.  Each
+// upper role flips the sign a lane holds, so on return lane q holds
 // (-1)^popcount(q) times the oracle's values; the caller folds that sign
 // into the 1/sqrt(n) scale.  The sign of an exact zero may differ from the
 // oracle's, which no later encode step depends on.
@@ -393,13 +411,18 @@ __device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) 
 #pragma unroll
   for (int m = 1; m < LPT; m <<= 1) {
     const float f = (q & m) ? -1.0f : 1.0f;
+    if (m == 1) {                                            // partner lane ^ 1: quad_perm 1,0,3,2
 #pragma unroll
-    for (int j = 0; j < kLaneElems; j++) {
-      int other;
-      if (m == 1) other = __builtin_amdgcn_mov_dpp(__float_as_int(a[j]), 0xB1, 0xF, 0xF, true);       // quad_perm 1,0,3,2
-      else if (m == 2) other = __builtin_amdgcn_mov_dpp(__float_as_int(a[j]), 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
-      else other = __builtin_amdgcn_ds_swizzle(__float_as_int(a[j]), 0x101F);                        // lane ^ 4 (32-lane bit mode)
-      a[j] = __builtin_fmaf(__int_as_float(other), f, a[j]);
+      for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("quad_perm:[1,0,3,2]", a, o, f);
+    } else if (m == 2) {                                     // partner lane ^ 2: quad_perm 2,3,0,1
+#pragma unroll
+      for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("quad_perm:[2,3,0,1]", a, o, f);
+    } else {                                                 // lane ^ 4 (32-lane bit mode swizzle)
+#pragma unroll
+      for (int j = 0; j < kLaneElems; j++) {
+        const int other = __builtin_amdgcn_ds_swizzle(__float_as_int(a[j]), 0x101F);
+        a[j] = __builtin_fmaf(__int_as_float(other), f, a[j]);
+      }
     }
   }
 }

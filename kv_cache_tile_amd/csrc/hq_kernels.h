@@ -38,6 +38,32 @@ namespace hq {
 constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 
+// Draw a chunk ticket; the holder of the last one resets the counter and
+// moves the epoch on, leaving the workspace ready for the next call.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint32_t last_ticket, uint32_t epoch) {
+  const uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tk == last_ticket) {
+    __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return tk;
+}
+
+// Sign diagonal (Methodology 1): bit i of lane q's mask is the sign of tile
+// element 32 q + i.  Threads 0..N-1 hash one element each, a ballot gathers
+// 64 bits per wave into LDS (the workgroup has at least N threads).
+template <int N>
+__device__ __forceinline__ uint32_t sign_mask(uint32_t* smask, uint32_t key_sign, int tid, int q) {
+  const uint32_t bit = tid < N ? (pcg_hash(key_sign + (uint32_t)tid) >> 31) : 0u;
+  const uint64_t bal = __ballot(bit);
+  if (tid < N && (tid & 63) == 0) {
+    smask[tid >> 5] = (uint32_t)bal;
+    if (N > 32) smask[(tid >> 5) + 1] = (uint32_t)(bal >> 32);
+  }
+  __syncthreads();
+  return smask[q];
+}
+
 // --------------------------------------------------------------------------
 // Encode kernel
 // --------------------------------------------------------------------------
@@ -60,6 +86,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   uint32_t* tile_len = smem + stage_words;                  // [64]
   uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
   uint32_t* misc = tile_off + kChunkTiles;                  // [4]
+  uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -67,28 +94,28 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);
 
   // sign diagonal entries of this lane's 32 positions (Methodology 1)
-  uint32_t sgn = 0;
-#pragma unroll
-  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
 
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
-  if (tid == 0) misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Chunk tickets: a workgroup takes tickets one after another until it
+  // draws one >= C.
+  // Every workgroup reads the epoch before its first ticket, so the holder
+  // of the very last ticket (C + grid - 1) can reset the counter and bump
+  // the epoch for the next call.
+  const uint32_t last_ticket = (uint32_t)(C + gridDim.x - 1);
+  if (tid == 0) {
+    const uint32_t ep = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
+    misc[2] = ep;
+    misc[0] = take_ticket(ws, last_ticket, ep);
+  }
+  for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
-  const uint32_t epoch = misc[2] & kEpochMask;
+  const uint32_t epoch = misc[2];
+  uint64_t chunk = misc[0];
 
   for (;;) {
-    if (tid == 0) {
-      uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      misc[0] = tk;
-      if ((uint64_t)tk == C + gridDim.x - 1) {               // last ticket: all taken, reset for next call
-        __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    const uint64_t chunk = misc[0];
     if (chunk >= C) break;
 
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
@@ -155,7 +182,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) a[i] = nonfinite ? 0.0f : a[i] * inv;
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv;
+    if (__any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
+      if (nonfinite) {
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+      }
+    }
 
     // ---- KV: add the dither (Methodology 4) ----
     if constexpr (DITHER) {
@@ -279,10 +312,18 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     const uint32_t lane_excl = incl - lane_unary;
     const uint32_t tlen = B + best_c;
-    if (q == 0) tile_len[tau] = active ? tlen : 0u;
+    if (q == 0) {
+      tile_len[tau] = active ? tlen : 0u;
+      if (active) {
+        step_out[t] = (uint16_t)sbits;
+        meta_out[t] = (uint16_t)((tlen << 3) | k);
+        if (nonfinite) atomicOr(status, HQ_FLAG_NONFINITE);
+      }
+    }
     __syncthreads();
 
-    // ---- chunk scan: bit offset of every tile inside the chunk ----
+    // ---- chunk scan: bit offset of every tile inside the chunk; publish the
+    // chunk's size at once so later chunks can look back past it ----
     if (tid < kChunkTiles) {
       uint32_t v = tile_len[tid], inc = v;
 #pragma unroll
@@ -291,22 +332,20 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         if (tid >= m) inc += o;
       }
       tile_off[tid] = inc - v;
-      if (tid == kChunkTiles - 1) misc[1] = inc;
+      if (tid == kChunkTiles - 1) {
+        misc[1] = inc;
+        const uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
+        __hip_atomic_store(&look[chunk], (tag << 32) | ((inc + 31u) >> 5), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     const uint32_t total_bits = misc[1];
-    uint32_t W = (total_bits + 31u) >> 5;
+    const uint32_t W = (total_bits + 31u) >> 5;
     const bool fits = W + 2 <= stage_words;
 
-    // publish this chunk's size early so later chunks can look back past it
-    if (tid == 0) {
-      uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
-      __hip_atomic_store(&look[chunk], (tag << 32) | W, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    for (uint32_t i = tid; i < W + 2 && i < stage_words; i += blockDim.x) stage[i] = 0u;
-    __syncthreads();
-
-    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane ----
+    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane
+    // (the staging words are zero: cleared at the start and after each copy) ----
     if (active && fits) {
       const uint32_t t0 = tile_off[tau];
       if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
@@ -332,7 +371,9 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     __syncthreads();
 
-    // ---- decoupled look-back, one predecessor per lane of wave 0 ----
+    // ---- wave 0: decoupled look-back, one predecessor per lane.  It comes
+    // after the packing: by then the nearest predecessors have published
+    // their sizes, and waiting lanes poll less ----
     if (tid < 64) {
       uint32_t excl = 0;
       if (chunk > 0) {
@@ -374,17 +415,22 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
       }
     }
+
     __syncthreads();
+
+    // ---- copy the chunk's words out, clearing the staging area behind ----
     const uint32_t excl = misc[3];
-    if (fits && (uint64_t)excl + W <= cap_words) {
-      for (uint32_t i = tid; i < W; i += blockDim.x) payload[excl + i] = stage[i];
+    const bool store = fits && (uint64_t)excl + W <= cap_words;
+    const uint32_t zw = W + 2 < stage_words ? W + 2 : stage_words;
+    for (uint32_t i = tid; i < zw; i += blockDim.x) {
+      if (store && i < W) payload[excl + i] = stage[i];
+      stage[i] = 0u;
     }
-    if (active && q == 0) {
-      step_out[t] = (uint16_t)sbits;
-      meta_out[t] = (uint16_t)((tlen << 3) | k);
-      if (nonfinite) atomicOr(status, HQ_FLAG_NONFINITE);
-    }
+    // next ticket only now: a chunk's size is published when its workgroup
+    // gets to it, and later chunks' look-backs wait for that
+    if (tid == 0) misc[0] = take_ticket(ws, last_ticket, epoch);
     __syncthreads();
+    chunk = misc[0];
   }
 }
 
@@ -508,14 +554,13 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   uint32_t* tile_ok = tile_off + kChunkTiles;               // [64]
   uint32_t* ustart = tile_ok + kChunkTiles;                 // [TPW * LPT] first unary bit per lane
   uint32_t* misc = ustart + TPW * LPT;                      // [4]
+  uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
   const int q = tid % LPT;
 
-  uint32_t sgn = 0;
-#pragma unroll
-  for (int i = 0; i < kLaneElems; i++) sgn |= (pcg_hash(key_sign + (uint32_t)(q * kLaneElems + i)) >> 31) << i;
+  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
   const uint64_t units = C * SUB;

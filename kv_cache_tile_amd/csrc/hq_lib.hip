@@ -139,7 +139,7 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
   EncFn fn = enc_fn(lat, tile, kv != 0);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
-  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4) * 4;
+  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4 + 8) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C, &grid);
   if (rc) return rc;
@@ -167,7 +167,7 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   const uint32_t chunk_cap = (uint32_t)(((uint64_t)kChunkTiles * P.bound + 31) / 32);
   // a unit's bits start anywhere in a word: one extra word, plus the readers' guard
   const uint32_t stage_words = (uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 8;
-  const size_t lds = (size_t)(stage_words + 2 * kChunkTiles + tpw * lpt + 4) * 4;
+  const size_t lds = (size_t)(stage_words + 2 * kChunkTiles + tpw * lpt + 4 + 8) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
   if (rc) return rc;
