@@ -38,6 +38,108 @@ namespace hq {
 constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 
+// Rice fields of one lane (32 symbols, parameter K) into the staging bits of
+// its tile starting at bit t0, from the byte-packed symbols P (symbol 4j + m
+// is byte m of P[j]; every symbol of the wave is below 256).
+//  - Remainder plane: the K-bit remainders of 4 symbols become one 4K-bit
+//    field with byte dot products (weights 1, 2^K, 4^K, 8^K), the 8 fields
+//    are assembled at static offsets in K registers, then written as K or K+1
+//    words at the lane's bit alignment: plain stores for the words the lane
+//    owns, OR for the two it may share with its neighbours.
+//  - Unary plane: the codes (q zeros, then a one) of 8 symbols are gathered
+//    in one register and ORed in at once; a group longer than 32 bits sets
+//    its bits one by one.
+template <int K, int N, uint32_t B>
+__device__ __forceinline__ void pack_lane_bytes(uint32_t* stage, uint32_t t0, int q,
+                                                const uint32_t (&P)[kLaneElems / 2], uint32_t lane_excl) {
+  if constexpr (K > 0) {
+    constexpr uint32_t rmask4 = 0x01010101u * ((1u << K) - 1u);
+    uint32_t w[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; j++) w[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < kLaneElems / 4; j++) {
+      const uint32_t x = P[j] & rmask4;
+      uint32_t f;
+      if constexpr (3 * K <= 7) {
+        f = __builtin_amdgcn_udot4(x, 1u | (1u << (K + 8)) | (1u << (2 * K + 16)) | (1u << (3 * K + 24)), 0u, false);
+      } else {
+        const uint32_t hi = __builtin_amdgcn_udot4(x, (1u << 16) | (1u << (K + 24)), 0u, false);
+        f = __builtin_amdgcn_udot4(x, 1u | (1u << (K + 8)), hi << (2 * K), false);
+      }
+      const int o = j * 4 * K, wj = o >> 5, b = o & 31;
+      w[wj] |= f << b;
+      if (b + 4 * K > 32) w[wj + 1] |= f >> (32 - b);
+    }
+    const uint32_t rpos = t0 + B + (uint32_t)q * (uint32_t)(kLaneElems * K);
+    const uint32_t wi = rpos >> 5, sh = rpos & 31u;
+    if (sh == 0u) {
+      // starts and ends on word boundaries: every word is this lane's own
+#pragma unroll
+      for (int j = 0; j < K; j++) stage[wi + j] = w[j];
+    } else {
+      atomicOr(&stage[wi], w[0] << sh);
+#pragma unroll
+      for (int j = 1; j < K; j++) stage[wi + j] = (w[j] << sh) | (w[j - 1] >> (32u - sh));
+      atomicOr(&stage[wi + K], w[K - 1] >> (32u - sh));
+    }
+  }
+  uint32_t upos = t0 + B + (uint32_t)N * (uint32_t)K + lane_excl;
+#pragma unroll
+  for (int g = 0; g < kLaneElems / 8; g++) {
+    uint32_t G = 0u, tb = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int e = 8 * g + i;
+      const uint32_t p = tb + __builtin_amdgcn_ubfe(P[e >> 2], 8 * (e & 3) + K, 8 - K);
+      G |= 1u << (p & 31u);
+      tb = p + 1u;
+    }
+    if (tb <= 32u) {
+      const uint32_t sh = upos & 31u, wi = upos >> 5;
+      atomicOr(&stage[wi], G << sh);
+      if (sh != 0u && sh + tb > 32u) atomicOr(&stage[wi + 1], G >> (32u - sh));
+    } else {
+      uint32_t pos = upos;
+#pragma unroll 1
+      for (int i = 0; i < 8; i++) {
+        const int e = 8 * g + i;
+        pos += __builtin_amdgcn_ubfe(P[e >> 2], 8 * (e & 3) + K, 8 - K);
+        atomicOr(&stage[pos >> 5], 1u << (pos & 31u));
+        pos += 1u;
+      }
+    }
+    upos += tb;
+  }
+}
+
+// The same fields from 16-bit symbol pairs (R[i / 2], half i % 2) with a
+// runtime k, for waves with a symbol of 256 or more: remainders four at a
+// time, one OR per unary code.
+template <int N, uint32_t B>
+__device__ __forceinline__ void pack_lane_pairs(uint32_t* stage, uint32_t t0, int q,
+                                                const uint32_t (&R)[kLaneElems / 2], uint32_t k, uint32_t lane_excl) {
+  if (k > 0) {
+    const uint32_t rmask = (1u << k) - 1u;
+    uint32_t rpos = t0 + B + (uint32_t)q * kLaneElems * k;
+#pragma unroll
+    for (int g = 0; g < kLaneElems / 4; g++) {
+      const uint32_t lo = R[2 * g], hi = R[2 * g + 1];
+      const uint32_t f = (lo & rmask) | (((lo >> 16) & rmask) << k) | ((hi & rmask) << (2u * k)) |
+                         (((hi >> 16) & rmask) << (3u * k));
+      lds_or_bits(stage, rpos, f, 4u * k);
+      rpos += 4u * k;
+    }
+  }
+  uint32_t upos = t0 + B + (uint32_t)N * k + lane_excl;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) {
+    upos += __builtin_amdgcn_ubfe(R[i >> 1], 16 * (i & 1), 16) >> k;
+    atomicOr(&stage[upos >> 5], 1u << (upos & 31u));
+    upos += 1u;
+  }
+}
+
 // Draw a chunk ticket; the holder of the last one resets the counter and
 // moves the epoch on, leaving the workspace ready for the next call.
 __device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint32_t last_ticket, uint32_t epoch) {
@@ -202,18 +304,27 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       }
     }
 
-    // ---- nearest lattice point, strip, zigzag ----
-    uint32_t sym[kLaneElems];
+    // ---- nearest lattice point, strip, zigzag: symbols as 16-bit pairs
+    // (every symbol is below 2^12: |t| <= sqrt(n) / c' for the table's c) ----
+    uint32_t S2[kLaneElems / 2];
     uint32_t cb = 0;
+#pragma unroll
+    for (int i = 0; i < kLaneElems / 2; i++) S2[i] = 0u;
 #pragma unroll
     for (int b = 0; b < BPL; b++) {
       uint32_t p;
+      uint32_t u[D];
       if constexpr (LAT == 8) {
-        nearest_e8_symbols(&a[b * D], &sym[b * D], p);
+        nearest_e8_symbols(&a[b * D], u, p);
       } else {
         int32_t d[D];
         nearest<LAT>(&a[b * D], d, p, a2);
-        block_symbols<LAT>(d, &sym[b * D]);
+        block_symbols<LAT>(d, u);
+      }
+#pragma unroll
+      for (int i = 0; i < D; i++) {
+        const int e = b * D + i;
+        S2[e >> 1] |= u[i] << (16 * (e & 1));
       }
       cb |= p << b;
     }
@@ -228,12 +339,20 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     // one byte-sum (v_sad_u8) add four terms.
     uint32_t mx = 0;
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) mx |= sym[i];
-    const bool bytes = __all(mx < 256u);
-    uint32_t P[kLaneElems / 4];
+    for (int i = 0; i < kLaneElems / 2; i++) mx |= S2[i];
+    const bool bytes = __all((mx & 0xFF00FF00u) == 0u);
+    // R: the byte-packed symbols (R[j], byte m = symbol 4j + m) when every
+    // symbol of the wave fits a byte, else the 16-bit pairs
+    uint32_t R[kLaneElems / 2];
+    if (bytes) {
 #pragma unroll
-    for (int j = 0; j < kLaneElems / 4; j++)
-      P[j] = sym[4 * j] | (sym[4 * j + 1] << 8) | (sym[4 * j + 2] << 16) | (sym[4 * j + 3] << 24);
+      for (int j = 0; j < kLaneElems / 4; j++) R[j] = __builtin_amdgcn_perm(S2[2 * j + 1], S2[2 * j], 0x06040200u);
+#pragma unroll
+      for (int j = kLaneElems / 4; j < kLaneElems / 2; j++) R[j] = 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLaneElems / 2; j++) R[j] = S2[j];
+    }
     uint32_t k = 0, best_c = 0, lane_sum = 0;
     bool settled = false;
     if (bytes && k_prev < 8u) {
@@ -245,7 +364,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
         uint32_t acc = 0;
 #pragma unroll
-        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> kk) & bmask, 0u, acc);
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((R[j] >> kk) & bmask, 0u, acc);
         L[jj] = acc;
         uint32_t tot = acc;
 #pragma unroll
@@ -266,39 +385,33 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       }
     }
     if (__any(!settled)) {
-      uint32_t S[8];
-      if (bytes) {
-#pragma unroll
-        for (int kk = 0; kk < 8; kk++) {
+      // rare: all eight sums, one k per (rolled) iteration, running minimum
+      uint32_t bk = 0, bc = 0xFFFFFFFFu, bsum = 0;
+#pragma unroll 1
+      for (uint32_t kk = 0; kk < 8u; kk++) {
+        uint32_t acc = 0;
+        if (bytes) {
           const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
-          uint32_t acc = 0;
 #pragma unroll
-          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((P[j] >> kk) & bmask, 0u, acc);
-          S[kk] = acc;
+          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((R[j] >> kk) & bmask, 0u, acc);
+        } else {
+          // 16-bit halves: each half's sum stays below 2^16 (16 symbols < 2^12)
+          const uint32_t hmask = 0x00010001u * (0xFFFFu >> kk);
+          uint32_t a2acc = 0;
+#pragma unroll
+          for (int j = 0; j < kLaneElems / 2; j++) a2acc += (R[j] >> kk) & hmask;
+          acc = (a2acc & 0xFFFFu) + (a2acc >> 16);
         }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 8; kk++) {
-          uint32_t acc = 0;
-#pragma unroll
-          for (int i = 0; i < kLaneElems; i++) acc += sym[i] >> kk;
-          S[kk] = acc;
-        }
-      }
-      uint32_t bk = 0, bc = 0xFFFFFFFFu;
-#pragma unroll
-      for (int kk = 0; kk < 8; kk++) {
-        uint32_t tot = S[kk];
+        uint32_t tot = acc;
 #pragma unroll
         for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
         const uint32_t cost = tot + (uint32_t)N * (1u + kk);
-        if (cost < bc) { bc = cost; bk = kk; }
+        if (cost < bc) { bc = cost; bk = kk; bsum = acc; }
       }
       if (!settled) {
         k = bk;
         best_c = bc;
-#pragma unroll
-        for (int kk = 0; kk < 8; kk++) if (kk == (int)bk) lane_sum = S[kk];
+        lane_sum = bsum;
       }
     }
     k_prev = k;
@@ -349,24 +462,17 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     if (active && fits) {
       const uint32_t t0 = tile_off[tau];
       if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
-      if (k > 0) {
-        // four k-bit remainders (at most 28 bits) per OR into the staging bits
-        const uint32_t rmask = (1u << k) - 1u;
-        uint32_t rpos = t0 + B + (uint32_t)q * kLaneElems * k;
-#pragma unroll
-        for (int g = 0; g < kLaneElems / 4; g++) {
-          const uint32_t f = (sym[4 * g] & rmask) | ((sym[4 * g + 1] & rmask) << k) |
-                             ((sym[4 * g + 2] & rmask) << (2u * k)) | ((sym[4 * g + 3] & rmask) << (3u * k));
-          lds_or_bits(stage, rpos, f, 4u * k);
-          rpos += 4u * k;
+      if (bytes) {
+        switch (k) {
+#define HQ_PACK_CASE(KK) \
+          case KK: pack_lane_bytes<KK, N, B>(stage, t0, q, R, lane_excl); break;
+          HQ_PACK_CASE(0) HQ_PACK_CASE(1) HQ_PACK_CASE(2) HQ_PACK_CASE(3)
+          HQ_PACK_CASE(4) HQ_PACK_CASE(5) HQ_PACK_CASE(6)
+          default: pack_lane_bytes<7, N, B>(stage, t0, q, R, lane_excl); break;
+#undef HQ_PACK_CASE
         }
-      }
-      uint32_t upos = t0 + B + (uint32_t)N * k + lane_excl;
-#pragma unroll
-      for (int i = 0; i < kLaneElems; i++) {
-        upos += sym[i] >> k;
-        atomicOr(&stage[upos >> 5], 1u << (upos & 31u));
-        upos += 1u;
+      } else {
+        pack_lane_pairs<N, B>(stage, t0, q, R, k, lane_excl);
       }
     }
     __syncthreads();
