@@ -217,6 +217,24 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   const uint32_t epoch = misc[2];
   uint64_t chunk = misc[0];
 
+  // bf16 input of the chunk about to be processed, loaded one phase ahead
+  // (issued after the previous chunk's packing, in flight during its
+  // look-back and copy-out)
+  uint4 pre[4];
+  auto prefetch = [&](uint64_t ch) {
+    const uint64_t tt = ch * kChunkTiles + (uint64_t)tau;
+    if (bf16 && ch < C && tt < T) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + tt * N +
+                                                      (uint64_t)q * kLaneElems);
+#pragma unroll
+      for (int v = 0; v < 4; v++) pre[v] = p[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; v++) pre[v] = make_uint4(0u, 0u, 0u, 0u);   // (dead between uses)
+    }
+  };
+  prefetch(chunk);
+
   for (;;) {
     if (chunk >= C) break;
 
@@ -228,10 +246,9 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     if (active) {
       const uint64_t base = t * N + (uint64_t)q * kLaneElems;
       if (bf16) {
-        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + base);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
-          uint4 w = p[v];
+          const uint4 w = pre[v];
           uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int h = 0; h < 4; h++) {
@@ -456,6 +473,11 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     const uint32_t total_bits = misc[1];
     const uint32_t W = (total_bits + 31u) >> 5;
     const bool fits = W + 2 <= stage_words;
+    // next ticket now (its reply arrives during the packing): this chunk's
+    // size is already published, and the next chunk's input can be loaded
+    // while this one is looked back and copied out
+    uint32_t next_ticket = 0;
+    if (tid == 64) next_ticket = take_ticket(ws, last_ticket, epoch);
 
     // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane
     // (the staging words are zero: cleared at the start and after each copy) ----
@@ -475,7 +497,10 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         pack_lane_pairs<N, B>(stage, t0, q, R, k, lane_excl);
       }
     }
+    if (tid == 64) misc[0] = next_ticket;
     __syncthreads();
+    const uint64_t next = misc[0];
+    prefetch(next);
 
     // ---- wave 0: decoupled look-back, one predecessor per lane.  It comes
     // after the packing: by then the nearest predecessors have published
@@ -532,11 +557,8 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       if (store && i < W) payload[excl + i] = stage[i];
       stage[i] = 0u;
     }
-    // next ticket only now: a chunk's size is published when its workgroup
-    // gets to it, and later chunks' look-backs wait for that
-    if (tid == 0) misc[0] = take_ticket(ws, last_ticket, epoch);
     __syncthreads();
-    chunk = misc[0];
+    chunk = next;
   }
 }
 
