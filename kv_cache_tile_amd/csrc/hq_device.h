@@ -370,6 +370,17 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
   return base;
 }
 
+// Lanes of a tile.  At n = 256 (8 lanes per tile) physical lanes 4..7 hold
+// logical lanes 7..4, so that the stride-128 butterfly partner q ^ 4 is the
+// half-row mirror p ^ 7, a DPP pattern; the partners q ^ 1 and q ^ 2 stay
+// p ^ 1 and p ^ 2 (quad permutes).  Everything that depends on a lane's
+// place in the tile uses the logical lane q.
+template <int LPT>
+__device__ __forceinline__ int tile_lane(int p) { return (LPT == 8 && p >= 4) ? (p ^ 3) : p; }
+// physical xor distance to the logical partner q ^ m
+template <int LPT>
+__device__ __forceinline__ constexpr int partner_xor(int m) { return (LPT == 8 && m == 4) ? 7 : m; }
+
 // One cross-lane stage on eight elements: a[o + i] += f * partner's a[o + i]
 // as v_fmac_f32_dpp, the partner selected by the DPP control.  One fused
 // multiply-add with a +-1 factor rounds once, like the butterfly's add.
@@ -417,12 +428,9 @@ __device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) 
     } else if (m == 2) {                                     // partner lane ^ 2: quad_perm 2,3,0,1
 #pragma unroll
       for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("quad_perm:[2,3,0,1]", a, o, f);
-    } else {                                                 // lane ^ 4 (32-lane bit mode swizzle)
+    } else {                                                 // partner q ^ 4 = lane p ^ 7: half-row mirror
 #pragma unroll
-      for (int j = 0; j < kLaneElems; j++) {
-        const int other = __builtin_amdgcn_ds_swizzle(__float_as_int(a[j]), 0x101F);
-        a[j] = __builtin_fmaf(__int_as_float(other), f, a[j]);
-      }
+      for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("row_half_mirror", a, o, f);
     }
   }
 }

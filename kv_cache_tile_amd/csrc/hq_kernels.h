@@ -192,7 +192,8 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
-  const int q = tid % LPT;
+  const int p_lane = tid % LPT;                            // physical lane in the tile
+  const int q = tile_lane<LPT>(p_lane);                     // logical lane
   uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);
 
   // sign diagonal entries of this lane's 32 positions (Methodology 1)
@@ -287,7 +288,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     float ss = sq[0];
 #pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) ss = ss + __shfl_xor(ss, m);
+    for (int m = 1; m < LPT; m <<= 1) ss = ss + __shfl_xor(ss, partner_xor<LPT>(m));
     bool nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
     float s = 0.0f;
     uint32_t sbits = 0;
@@ -385,7 +386,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         L[jj] = acc;
         uint32_t tot = acc;
 #pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, partner_xor<LPT>(m));
         Tt[jj] = tot;
       }
       const bool drop0 = Tt[0] - Tt[1] > (uint32_t)N, drop1 = Tt[1] - Tt[2] > (uint32_t)N;
@@ -421,7 +422,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         }
         uint32_t tot = acc;
 #pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, m);
+        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, partner_xor<LPT>(m));
         const uint32_t cost = tot + (uint32_t)N * (1u + kk);
         if (cost < bc) { bc = cost; bk = kk; bsum = acc; }
       }
@@ -434,13 +435,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     k_prev = k;
     // this lane's unary quotients: sum (q_i + 1) bits; exclusive prefix over the tile's lanes
     const uint32_t lane_unary = lane_sum + (uint32_t)kLaneElems;
-    uint32_t incl = lane_unary;
+    uint32_t lane_excl = 0, span = lane_unary;              // exclusive prefix in logical lane order
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) {
-      uint32_t v = __shfl_up(incl, m, LPT);
-      if (q >= m) incl += v;
+      const uint32_t other = __shfl_xor(span, partner_xor<LPT>(m));
+      if (q & m) lane_excl += other;
+      span += other;
     }
-    const uint32_t lane_excl = incl - lane_unary;
     const uint32_t tlen = B + best_c;
     if (q == 0) {
       tile_len[tau] = active ? tlen : 0u;
@@ -686,7 +687,8 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
-  const int q = tid % LPT;
+  const int p_lane = tid % LPT;                            // physical lane in the tile
+  const int q = tile_lane<LPT>(p_lane);                     // logical lane
 
   const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
@@ -738,14 +740,15 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
     // ---- where does each lane's first unary code start?  Every codeword has
-    // exactly one 1 in the unary plane: count ones word by word (lane q takes
-    // words q, q+LPT, ...) and mark the bit after the (32 q)-th one. ----
+    // exactly one 1 in the unary plane: count ones word by word (physical lane
+    // p takes words p, p+LPT, ...) and mark the bit after the (32 q)-th one for
+    // logical lane q. ----
     const uint32_t words = ok ? (end - ub + 31u) >> 5 : 0u;
     uint32_t carry = 0;
     for (uint32_t r = 0;; r++) {
       const bool more = r * LPT < words;
       if (!__any(more)) break;
-      const uint32_t j = r * LPT + (uint32_t)q;
+      const uint32_t j = r * LPT + (uint32_t)p_lane;
       uint32_t w = 0;
       if (j < words) {
         const uint32_t p = ub + 32u * j;
@@ -758,7 +761,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 #pragma unroll
       for (int s2 = 1; s2 < LPT; s2 <<= 1) {
         uint32_t o = __shfl_up(inc, s2, LPT);
-        if (q >= s2) inc += o;
+        if (p_lane >= s2) inc += o;
       }
       const uint32_t before = carry + inc - c, after = carry + inc;
       const uint32_t mm = before / 32u + 1u;
