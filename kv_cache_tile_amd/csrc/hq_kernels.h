@@ -656,13 +656,17 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
         for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
       }
     }
+    // the group's values are final here: keeps the compiler from holding all
+    // 32 quotients and rebuilding every block at the end (register pressure)
+    asm volatile("" : "+v"(a[8 * g + 0]), "+v"(a[8 * g + 1]), "+v"(a[8 * g + 2]), "+v"(a[8 * g + 3]),
+                      "+v"(a[8 * g + 4]), "+v"(a[8 * g + 5]), "+v"(a[8 * g + 6]), "+v"(a[8 * g + 7]));
   }
   upos = uw.pos();
   return ok;
 }
 
 template <int LAT, int N, bool DITHER>
-__global__ void __launch_bounds__(DecodeGeom<N>::THREADS)
+__global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 3 : 5)))
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
               const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
               const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
