@@ -134,28 +134,34 @@ __device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t&
 
 // E8 straight to Rice symbols, for the encoder's quantiser: the same choice
 // and tie rules as nearest_e8 followed by block_symbols, arranged for fewer
-// operations.  With f = rint(t) and delta = t - f:
+// vector operations.  With f = rint(t) and delta = t - f:
 //  - floor(t) = f - [delta < 0], so the half-integer candidate's coset parity
-//    is f's parity flipped by the number of negative deltas (an XOR of signs);
+//    is f's parity flipped by the number of negative deltas;
 //  - the moved coordinate is the first one whose |delta| equals the max (A)
-//    or the min (B); one chain finds it and carries its delta;
-//  - A moves it by +1 if delta >= 0 else -1; B moves floor(t) by +1 if
-//    t >= floor(t) + 1/2, i.e. if delta < 0 or delta == 1/2, else by -1.
+//    or the min (B); A moves it by +1 if delta >= 0 else -1; B moves
+//    floor(t) by +1 if t >= floor(t) + 1/2, i.e. if delta < 0 or
+//    delta == 1/2, else by -1.
+// The per-coordinate conditions are lane masks, so "first equal", its sign
+// and the parity of the negative deltas are scalar mask operations.  The
+// symbol zz(d) = |2 d + 1/2| - 1/2 is formed in fp32 as |fma(f, 2, c)| - 1/2,
+// where c = 1/2 - 2 [B and delta < 0] + 2 [moved] dir carries the floor
+// correction and the move (exact: every value is a small integer or half).
 __device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, uint32_t& p) {
-  float dl[8], ad[8];
-  int32_t fi[8];
+  float f[8], dl[8], ad[8];
+  bool neg[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const float f = __builtin_rintf(t[i]);
-    dl[i] = t[i] - f;
+    f[i] = __builtin_rintf(t[i]);
+    dl[i] = t[i] - f[i];
     ad[i] = __builtin_fabsf(dl[i]);
-    fi[i] = (int32_t)f;
+    neg[i] = dl[i] < 0.0f;
   }
-  const uint32_t px = (uint32_t)(((fi[0] ^ fi[1]) ^ (fi[2] ^ fi[3])) ^ ((fi[4] ^ fi[5]) ^ (fi[6] ^ fi[7])));
-  const uint32_t pn = ((as_u(dl[0]) ^ as_u(dl[1])) ^ (as_u(dl[2]) ^ as_u(dl[3]))) ^
-                      ((as_u(dl[4]) ^ as_u(dl[5])) ^ (as_u(dl[6]) ^ as_u(dl[7])));
-  const bool oddA = (px & 1u) != 0u;
-  const bool oddB = oddA != ((pn >> 31) != 0u);
+  const float sf = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));   // exact
+  const bool oddA = ((int32_t)sf & 1) != 0;
+  bool nneg = false;
+#pragma unroll
+  for (int i = 0; i < 8; i++) nneg = nneg ^ neg[i];
+  const bool oddB = oddA != nneg;
   const float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(ad[0], ad[1]), __builtin_fmaxf(ad[2], ad[3])),
                                    __builtin_fmaxf(__builtin_fmaxf(ad[4], ad[5]), __builtin_fmaxf(ad[6], ad[7])));
   const float mn = __builtin_fminf(__builtin_fminf(__builtin_fminf(ad[0], ad[1]), __builtin_fminf(ad[2], ad[3])),
@@ -166,23 +172,29 @@ __device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, 
   if (oddB) diff = diff - 2.0f * mn;
   const bool useB = diff > 0.0f;
   const float target = useB ? mn : mx;
-  int j = 7;
-  float dlj = dl[7];
-#pragma unroll
-  for (int i = 6; i >= 0; i--) {
-    const bool eq = ad[i] == target;
-    j = eq ? i : j;
-    dlj = eq ? dl[i] : dlj;
-  }
-  const bool odd = useB ? oddB : oddA;
-  const bool up = useB ? (dlj < 0.0f || dlj == 0.5f) : (dlj >= 0.0f);
-  const int32_t delta = odd ? (up ? 1 : -1) : 0;
-  const int32_t floor_mask = useB ? -1 : 0;
+  // (bitwise operators on the conditions: they stay lane masks)
+  bool first[8], seen = false, negj = false;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    int32_t d = fi[i] + (((int32_t)as_u(dl[i]) >> 31) & floor_mask) + (i == j ? delta : 0);
-    if (i == 7) d >>= 1;                                   // stored halved: parity of the others' sum
-    u[i] = zigzag(d);
+    const bool eq = ad[i] == target;
+    first[i] = eq & !seen;
+    seen = seen | eq;
+    negj = negj | (first[i] & neg[i]);
+  }
+  const bool odd = useB ? oddB : oddA;
+  const bool up = useB ? (negj | (target == 0.5f)) : !negj;
+  const float mv = odd ? (up ? 2.0f : -2.0f) : 0.0f;       // twice the move
+#pragma unroll
+  for (int i = 0; i < 7; i++) {
+    const float c0 = (useB & neg[i]) ? -1.5f : 0.5f;
+    const float c = first[i] ? c0 + mv : c0;
+    u[i] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(f[i], 2.0f, c)) - 0.5f);
+  }
+  {
+    // the last coordinate is stored halved (floor), its parity being the others' sum's
+    const float d7 = f[7] + (((useB & neg[7]) ? -1.0f : 0.0f) + (first[7] ? 0.5f * mv : 0.0f));
+    const float h = __builtin_floorf(d7 * 0.5f);
+    u[7] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(h, 2.0f, 0.5f)) - 0.5f);
   }
   p = useB ? 1u : 0u;
 }
@@ -369,6 +381,25 @@ __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
   }
   return base;
 }
+
+// Sign diagonal on packed bf16 pairs.  For a lane's 32-bit sign mask sgn
+// (bit i = sign of element i), pair_sign_words() spreads each 16-element half
+// h into W[h]: sign of element 2k at bit 2k, of element 2k + 1 at bit 2k + 16
+// (k = 0..7).  pair_sign_mask() shifts pair p's two bits to 15 and 31, the
+// sign bits of the packed pair (element 2p low, 2p + 1 high).
+__device__ __forceinline__ void pair_sign_words(uint32_t sgn, uint32_t (&W)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const uint32_t sg = (sgn >> (16 * h)) & 0xFFFFu;
+    W[h] = (sg & 0x5555u) | ((sg & 0xAAAAu) << 15);
+  }
+}
+__device__ __forceinline__ uint32_t pair_sign_mask(const uint32_t (&W)[2], int p) {
+  return (W[p >> 3] << (15 - 2 * (p & 7))) & 0x80008000u;
+}
+// The same values hidden from loop-invariant code motion: the 32 per-element
+// masks would otherwise be hoisted out of the chunk loop and held in 32 VGPRs.
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 // Lanes of a tile.  At n = 256 (8 lanes per tile) physical lanes 4..7 hold
 // logical lanes 7..4, so that the stride-128 butterfly partner q ^ 4 is the
