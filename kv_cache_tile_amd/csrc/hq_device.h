@@ -146,21 +146,28 @@ __device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t&
 // symbol zz(d) = |2 d + 1/2| - 1/2 is formed in fp32 as |fma(f, 2, c)| - 1/2,
 // where c = 1/2 - 2 [B and delta < 0] + 2 [moved] dir carries the floor
 // correction and the move (exact: every value is a small integer or half).
-__device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, uint32_t& p) {
-  float f[8], dl[8], ad[8];
-  bool neg[8];
+struct E8Choice {
+  float f[8];        // rint(t)
+  bool neg[8];       // t - rint(t) < 0
+  bool first[8];     // the moved coordinate (at most one)
+  bool useB;         // half-integer coset
+  float mv;          // twice the move: +-2, or 0 when no coordinate moves
+};
+
+__device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
+  float dl[8], ad[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    f[i] = __builtin_rintf(t[i]);
-    dl[i] = t[i] - f[i];
+    c.f[i] = __builtin_rintf(t[i]);
+    dl[i] = t[i] - c.f[i];
     ad[i] = __builtin_fabsf(dl[i]);
-    neg[i] = dl[i] < 0.0f;
+    c.neg[i] = dl[i] < 0.0f;
   }
-  const float sf = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));   // exact
+  const float sf = ((c.f[0] + c.f[1]) + (c.f[2] + c.f[3])) + ((c.f[4] + c.f[5]) + (c.f[6] + c.f[7]));   // exact
   const bool oddA = ((int32_t)sf & 1) != 0;
   bool nneg = false;
 #pragma unroll
-  for (int i = 0; i < 8; i++) nneg = nneg ^ neg[i];
+  for (int i = 0; i < 8; i++) nneg = nneg ^ c.neg[i];
   const bool oddB = oddA != nneg;
   const float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(ad[0], ad[1]), __builtin_fmaxf(ad[2], ad[3])),
                                    __builtin_fmaxf(__builtin_fmaxf(ad[4], ad[5]), __builtin_fmaxf(ad[6], ad[7])));
@@ -170,33 +177,50 @@ __device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, 
   float diff = sabs - 2.0f;
   if (oddA) diff = diff + (1.0f - 2.0f * mx);
   if (oddB) diff = diff - 2.0f * mn;
-  const bool useB = diff > 0.0f;
-  const float target = useB ? mn : mx;
+  c.useB = diff > 0.0f;
+  const float target = c.useB ? mn : mx;
   // (bitwise operators on the conditions: they stay lane masks)
-  bool first[8], seen = false, negj = false;
+  bool seen = false, negj = false;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const bool eq = ad[i] == target;
-    first[i] = eq & !seen;
+    c.first[i] = eq & !seen;
     seen = seen | eq;
-    negj = negj | (first[i] & neg[i]);
+    negj = negj | (c.first[i] & c.neg[i]);
   }
-  const bool odd = useB ? oddB : oddA;
-  const bool up = useB ? (negj | (target == 0.5f)) : !negj;
-  const float mv = odd ? (up ? 2.0f : -2.0f) : 0.0f;       // twice the move
+  const bool odd = c.useB ? oddB : oddA;
+  const bool up = c.useB ? (negj | (target == 0.5f)) : !negj;
+  c.mv = odd ? (up ? 2.0f : -2.0f) : 0.0f;
+}
+
+__device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, uint32_t& p) {
+  E8Choice c;
+  e8_choose(t, c);
 #pragma unroll
   for (int i = 0; i < 7; i++) {
-    const float c0 = (useB & neg[i]) ? -1.5f : 0.5f;
-    const float c = first[i] ? c0 + mv : c0;
-    u[i] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(f[i], 2.0f, c)) - 0.5f);
+    const float c0 = (c.useB & c.neg[i]) ? -1.5f : 0.5f;
+    const float cc = c.first[i] ? c0 + c.mv : c0;
+    u[i] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(c.f[i], 2.0f, cc)) - 0.5f);
   }
   {
     // the last coordinate is stored halved (floor), its parity being the others' sum's
-    const float d7 = f[7] + (((useB & neg[7]) ? -1.0f : 0.0f) + (first[7] ? 0.5f * mv : 0.0f));
+    const float d7 = c.f[7] + (((c.useB & c.neg[7]) ? -1.0f : 0.0f) + (c.first[7] ? 0.5f * c.mv : 0.0f));
     const float h = __builtin_floorf(d7 * 0.5f);
     u[7] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(h, 2.0f, 0.5f)) - 0.5f);
   }
-  p = useB ? 1u : 0u;
+  p = c.useB ? 1u : 0u;
+}
+
+// The nearest E8 point itself (same choice): point = f + c with
+// c = (B ? (delta < 0 ? -1/2 : +1/2) : 0) + [moved] dir.
+__device__ __forceinline__ void nearest_e8_point(const float* t, float* pt) {
+  E8Choice c;
+  e8_choose(t, c);
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float c0 = c.useB ? (c.neg[i] ? -0.5f : 0.5f) : 0.0f;
+    pt[i] = c.f[i] + (c.first[i] ? c0 + 0.5f * c.mv : c0);
+  }
 }
 
 // A2 = R u (R + (1/2, sqrt3/2)), R = Z x sqrt3 Z; code (p, m, n') with point
@@ -268,11 +292,15 @@ __device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, f
     else v[i] = a * 0x1p-24f - 0.5f;
   }
   if constexpr (LAT == 2) v[1] = k.sqrt3 * v[1];
-  int32_t d[D];
-  uint32_t p;
-  nearest<LAT>(v, d, p, k);
   float pt[D];
-  code_point<LAT>(d, p, pt, k);
+  if constexpr (LAT == 8) {
+    nearest_e8_point(v, pt);
+  } else {
+    int32_t d[D];
+    uint32_t p;
+    nearest<LAT>(v, d, p, k);
+    code_point<LAT>(d, p, pt, k);
+  }
 #pragma unroll
   for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
 }

@@ -319,17 +319,6 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       }
     }
 
-    // ---- KV: add the dither (Methodology 4) ----
-    if constexpr (DITHER) {
-      const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
-#pragma unroll
-      for (int b = 0; b < BPL; b++) {
-        float u[D];
-        dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), u, a2);
-#pragma unroll
-        for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + u[i];
-      }
-    }
 
     // ---- nearest lattice point, strip, zigzag: symbols as 16-bit pairs
     // (every symbol is below 2^12: |t| <= sqrt(n) / c' for the table's c) ----
@@ -341,6 +330,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     for (int b = 0; b < BPL; b++) {
       uint32_t p;
       uint32_t u[D];
+      if constexpr (DITHER) {
+        // KV: add the dither (Methodology 4), block by block
+        float du[D];
+        dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
+#pragma unroll
+        for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + du[i];
+      }
       if constexpr (LAT == 8) {
         if (b > 0) {
           // one 8-block at a time: its inputs are released together with the
