@@ -678,8 +678,10 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
   return ok;
 }
 
+// Occupancy target: 6 waves per SIMD (80 VGPRs) without dither, 5 with it
+// (a few spilled registers); latency hiding pays for more than the spills.
 template <int LAT, int N, bool DITHER>
-__global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 4 : 6)))
+__global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 6)))
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
               const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
               const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
