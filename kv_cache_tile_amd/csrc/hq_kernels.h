@@ -189,12 +189,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
   uint32_t* misc = tile_off + kChunkTiles;                  // [4]
   uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
+  uint32_t* goff = smask + 8;                               // [kGroupChunks] chunk word offsets in the group
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
   const int p_lane = tid % LPT;                            // physical lane in the tile
   const int q = tile_lane<LPT>(p_lane);                     // logical lane
-  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);
+  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);     // one word per group
 
   // sign diagonal entries of this lane's 32 positions (Methodology 1)
   const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
@@ -204,12 +205,14 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
-  // Chunk tickets: a workgroup takes tickets one after another until it
-  // draws one >= C.
-  // Every workgroup reads the epoch before its first ticket, so the holder
-  // of the very last ticket (C + grid - 1) can reset the counter and bump
-  // the epoch for the next call.
-  const uint32_t last_ticket = (uint32_t)(C + gridDim.x - 1);
+  // Tickets number groups of kGroupChunks consecutive chunks; a workgroup
+  // takes tickets one after another until it draws one >= the group count,
+  // and one look-back places a whole group.  Every workgroup reads the epoch
+  // before its first ticket, so the holder of the very last ticket
+  // (groups + grid - 1) can reset the counter and bump the epoch for the
+  // next call.
+  const uint64_t CG = (C + kGroupChunks - 1) / kGroupChunks;
+  const uint32_t last_ticket = (uint32_t)(CG + gridDim.x - 1);
   if (tid == 0) {
     const uint32_t ep = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
     misc[2] = ep;
@@ -218,11 +221,14 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
   const uint32_t epoch = misc[2];
-  uint64_t chunk = misc[0];
+  uint64_t grp = misc[0];
+  uint64_t chunk = grp * kGroupChunks;
+  uint32_t gi = 0, gw = 0;                                  // chunk of the group, group words staged so far
+  bool gfits = true;
 
   // bf16 input of the chunk about to be processed, loaded one phase ahead
-  // (issued after the previous chunk's packing, in flight during its
-  // look-back and copy-out)
+  // (the next chunk of a group during this one's scan and packing; a new
+  // group's first chunk during the previous group's look-back and copy-out)
   uint4 pre[4];
   auto prefetch = [&](uint64_t ch) {
     const uint64_t tt = ch * kChunkTiles + (uint64_t)tau;
@@ -239,7 +245,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   prefetch(chunk);
 
   for (;;) {
-    if (chunk >= C) break;
+    if (grp >= CG) break;
 
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
@@ -466,8 +472,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     __syncthreads();
 
-    // ---- chunk scan: bit offset of every tile inside the chunk; publish the
-    // chunk's size at once so later chunks can look back past it ----
+    // the group's next chunk: load its input during this one's scan and packing
+    const bool last = (gi + 1 == (uint32_t)kGroupChunks) || (chunk + 1 >= C);
+    if (!last) prefetch(chunk + 1);
+
+    // ---- chunk scan: bit offset of every tile inside the chunk; after the
+    // group's last chunk, publish the group's size at once so later groups
+    // can look back past it ----
     if (tid < kChunkTiles) {
       uint32_t v = tile_len[tid], inc = v;
 #pragma unroll
@@ -478,25 +489,29 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       tile_off[tid] = inc - v;
       if (tid == kChunkTiles - 1) {
         misc[1] = inc;
-        const uint64_t tag = (uint64_t)((epoch << 2) | (chunk == 0 ? kFlagIncl : kFlagAgg));
-        __hip_atomic_store(&look[chunk], (tag << 32) | ((inc + 31u) >> 5), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (last) {
+          const uint64_t tag = (uint64_t)((epoch << 2) | (grp == 0 ? kFlagIncl : kFlagAgg));
+          __hip_atomic_store(&look[grp], (tag << 32) | (gw + ((inc + 31u) >> 5)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     __syncthreads();
     const uint32_t total_bits = misc[1];
     const uint32_t W = (total_bits + 31u) >> 5;
-    const bool fits = W + 2 <= stage_words;
-    // next ticket now (its reply arrives during the packing): this chunk's
-    // size is already published, and the next chunk's input can be loaded
-    // while this one is looked back and copied out
+    const bool fits = gw + W + 2 <= stage_words;
+    gfits = gfits && fits;
+    if (tid == 0) goff[gi] = gw;                            // this chunk's word offset in the group
+    // after the group's last chunk: next ticket now (its reply arrives
+    // during the packing)
     uint32_t next_ticket = 0;
-    if (tid == 64) next_ticket = take_ticket(ws, last_ticket, epoch);
+    if (last && tid == 64) next_ticket = take_ticket(ws, last_ticket, epoch);
 
-    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane
-    // (the staging words are zero: cleared at the start and after each copy) ----
+    // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane,
+    // at the chunk's word offset in the group's staging area (zero: cleared at
+    // the start and after each copy) ----
     if (active && fits) {
-      const uint32_t t0 = tile_off[tau];
+      const uint32_t t0 = gw * 32u + tile_off[tau];
       if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
       if (bytes) {
         switch (k) {
@@ -511,25 +526,32 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         pack_lane_pairs<N, B>(stage, t0, q, R, k, lane_excl);
       }
     }
-    if (tid == 64) misc[0] = next_ticket;
+    if (last && tid == 64) misc[0] = next_ticket;
     __syncthreads();
+    if (!last) {
+      gw += W;
+      gi++;
+      chunk++;
+      continue;
+    }
+    const uint32_t gtotal = gw + W;                         // the group's words
     const uint64_t next = misc[0];
-    prefetch(next);
+    prefetch(next * kGroupChunks);
 
-    // ---- wave 0: decoupled look-back, one predecessor per lane.  It comes
-    // after the packing: by then the nearest predecessors have published
-    // their sizes, and waiting lanes poll less ----
+    // ---- wave 0: decoupled look-back over groups, one predecessor per lane.
+    // It comes after the packing: by then the nearest predecessors have
+    // published their sizes, and waiting lanes poll less ----
     if (tid < 64) {
       uint32_t excl = 0;
-      if (chunk > 0) {
-        int64_t base = (int64_t)chunk - 1;
+      if (grp > 0) {
+        int64_t base = (int64_t)grp - 1;
         for (;;) {
           const int64_t j = base - tid;
           uint64_t v;
           uint32_t flag;
           if (j < 0) {
             v = 0;
-            flag = kFlagIncl;                                // before chunk 0: prefix 0
+            flag = kFlagIncl;                                // before group 0: prefix 0
           } else {
             for (;;) {
               v = __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -549,30 +571,35 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         }
       }
       if (tid == 0) {
-        if (chunk > 0) {
+        if (grp > 0) {
           uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
-          __hip_atomic_store(&look[chunk], (tag << 32) | (uint64_t)(excl + W), __ATOMIC_RELAXED,
+          __hip_atomic_store(&look[grp], (tag << 32) | (uint64_t)(excl + gtotal), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
         }
         misc[3] = excl;
-        chunk_off[chunk] = excl;
-        if (chunk == C - 1) chunk_off[C] = excl + W;
-        if (!fits || (uint64_t)excl + W > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+        const uint64_t c0 = grp * kGroupChunks;
+        for (uint32_t i = 0; i <= gi; i++) chunk_off[c0 + i] = excl + goff[i];
+        if (chunk == C - 1) chunk_off[C] = excl + gtotal;
+        if (!gfits || (uint64_t)excl + gtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
       }
     }
 
     __syncthreads();
 
-    // ---- copy the chunk's words out, clearing the staging area behind ----
+    // ---- copy the group's words out, clearing the staging area behind ----
     const uint32_t excl = misc[3];
-    const bool store = fits && (uint64_t)excl + W <= cap_words;
-    const uint32_t zw = W + 2 < stage_words ? W + 2 : stage_words;
+    const bool store = gfits && (uint64_t)excl + gtotal <= cap_words;
+    const uint32_t zw = gtotal + 2 < stage_words ? gtotal + 2 : stage_words;
     for (uint32_t i = tid; i < zw; i += blockDim.x) {
-      if (store && i < W) payload[excl + i] = stage[i];
+      if (store && i < gtotal) payload[excl + i] = stage[i];
       stage[i] = 0u;
     }
     __syncthreads();
-    chunk = next;
+    grp = next;
+    chunk = grp * kGroupChunks;
+    gi = 0;
+    gw = 0;
+    gfits = true;
   }
 }
 

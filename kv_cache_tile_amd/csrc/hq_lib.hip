@@ -92,7 +92,8 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
   P->C = (P->T + kChunkTiles - 1) / kChunkTiles;
   P->bound = bound;
   P->c = c;
-  P->stage_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 4;
+  // encode staging: a group of chunks, each word-aligned, plus guard words
+  P->stage_words = (uint32_t)kGroupChunks * ((uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 1) + 4;
   P->cap_words = (P->T * bound + 31) / 32 + P->C;
   P->ws_bytes = 8 + 8 * P->C;
   return HQ_OK;
@@ -139,9 +140,9 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
   EncFn fn = enc_fn(lat, tile, kv != 0);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
-  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4 + 8) * 4;
+  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4 + 8 + kGroupChunks) * 4;
   int grid;
-  rc = grid_for((const void*)fn, block, lds, P.C, &grid);
+  rc = grid_for((const void*)fn, block, lds, (P.C + kGroupChunks - 1) / kGroupChunks, &grid);
   if (rc) return rc;
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
