@@ -15,7 +15,7 @@ namespace hq {
 
 constexpr int kChunkTiles = 64;   // tiles per chunk of the stream
 constexpr int kLaneElems = 32;    // tile elements held by one lane
-constexpr int kGroupChunks = 2;   // chunks an encode workgroup stages per ticket (one look-back each)
+constexpr int kMaxGroupChunks = 4;   // most chunks an encode workgroup stages per ticket (one look-back each)
 
 // --------------------------------------------------------------------------
 // Counter-based generator: the "pcg" hash of Jarzynski & Olano (JCGT 9(3),

@@ -176,7 +176,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
               uint32_t* __restrict__ payload, uint64_t cap_words,
               uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
               uint32_t* __restrict__ chunk_off, uint32_t* __restrict__ status,
-              uint32_t* __restrict__ ws, uint32_t stage_words) {
+              uint32_t* __restrict__ ws, uint32_t stage_words, uint32_t group_chunks) {
   constexpr int LPT = N / kLaneElems;                       // lanes per tile
   constexpr int D = LatticeTraits<LAT>::dim;
   constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
@@ -189,7 +189,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
   uint32_t* misc = tile_off + kChunkTiles;                  // [4]
   uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
-  uint32_t* goff = smask + 8;                               // [kGroupChunks] chunk word offsets in the group
+  uint32_t* goff = smask + 8;                               // [group_chunks] chunk word offsets in the group
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -205,13 +205,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
-  // Tickets number groups of kGroupChunks consecutive chunks; a workgroup
+  // Tickets number groups of group_chunks consecutive chunks; a workgroup
   // takes tickets one after another until it draws one >= the group count,
   // and one look-back places a whole group.  Every workgroup reads the epoch
   // before its first ticket, so the holder of the very last ticket
   // (groups + grid - 1) can reset the counter and bump the epoch for the
   // next call.
-  const uint64_t CG = (C + kGroupChunks - 1) / kGroupChunks;
+  const uint64_t CG = (C + group_chunks - 1) / group_chunks;
   const uint32_t last_ticket = (uint32_t)(CG + gridDim.x - 1);
   if (tid == 0) {
     const uint32_t ep = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
@@ -222,7 +222,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   __syncthreads();
   const uint32_t epoch = misc[2];
   uint64_t grp = misc[0];
-  uint64_t chunk = grp * kGroupChunks;
+  uint64_t chunk = grp * group_chunks;
   uint32_t gi = 0, gw = 0;                                  // chunk of the group, group words staged so far
   bool gfits = true;
 
@@ -473,7 +473,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     __syncthreads();
 
     // the group's next chunk: load its input during this one's scan and packing
-    const bool last = (gi + 1 == (uint32_t)kGroupChunks) || (chunk + 1 >= C);
+    const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
     if (!last) prefetch(chunk + 1);
 
     // ---- chunk scan: bit offset of every tile inside the chunk; after the
@@ -536,7 +536,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     const uint32_t gtotal = gw + W;                         // the group's words
     const uint64_t next = misc[0];
-    prefetch(next * kGroupChunks);
+    prefetch(next * group_chunks);
 
     // ---- wave 0: decoupled look-back over groups, one predecessor per lane.
     // It comes after the packing: by then the nearest predecessors have
@@ -577,7 +577,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
                              __HIP_MEMORY_SCOPE_AGENT);
         }
         misc[3] = excl;
-        const uint64_t c0 = grp * kGroupChunks;
+        const uint64_t c0 = grp * group_chunks;
         for (uint32_t i = 0; i <= gi; i++) chunk_off[c0 + i] = excl + goff[i];
         if (chunk == C - 1) chunk_off[C] = excl + gtotal;
         if (!gfits || (uint64_t)excl + gtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
@@ -596,7 +596,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     __syncthreads();
     grp = next;
-    chunk = grp * kGroupChunks;
+    chunk = grp * group_chunks;
     gi = 0;
     gw = 0;
     gfits = true;
@@ -896,7 +896,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 // ---- per-lattice kernel tables (defined in hq_kern_<lattice>.hip) ----------
 using EncFn = void (*)(const void*, uint32_t, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t,
                        A2Consts, uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*,
-                       uint32_t);
+                       uint32_t, uint32_t);
 using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
                        uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t, uint32_t*, uint32_t,
                        uint32_t, uint32_t);

@@ -73,7 +73,7 @@ uint32_t tile_bound_bits(uint32_t n, uint32_t lat, uint32_t dither, float c) {
 
 struct Plan {
   uint64_t T, C, cap_words, ws_bytes;
-  uint32_t bound, stage_words;
+  uint32_t bound, chunk_words;
   float c;
 };
 
@@ -92,8 +92,7 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
   P->C = (P->T + kChunkTiles - 1) / kChunkTiles;
   P->bound = bound;
   P->c = c;
-  // encode staging: a group of chunks, each word-aligned, plus guard words
-  P->stage_words = (uint32_t)kGroupChunks * ((uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 1) + 4;
+  P->chunk_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 1;   // one chunk, word-aligned
   P->cap_words = (P->T * bound + 31) / 32 + P->C;
   P->ws_bytes = 8 + 8 * P->C;
   return HQ_OK;
@@ -140,16 +139,30 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
   EncFn fn = enc_fn(lat, tile, kv != 0);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
-  const size_t lds = (size_t)(P.stage_words + 2 * kChunkTiles + 4 + 8 + kGroupChunks) * 4;
+  // chunks staged per ticket: as many (up to kMaxGroupChunks) as fit a
+  // workgroup's LDS with room for two workgroups per CU
+  int dev = 0, max_lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return HQ_EHIP;
+  const size_t lds_cap = (size_t)max_lds < (size_t)80 * 1024 ? (size_t)max_lds : (size_t)80 * 1024;
+  uint32_t group = kMaxGroupChunks, stage_words = 0;
+  size_t lds = 0;
+  for (;; group >>= 1) {
+    stage_words = group * P.chunk_words + 4;
+    lds = (size_t)(stage_words + 2 * kChunkTiles + 4 + 8 + kMaxGroupChunks) * 4;
+    if (lds <= lds_cap || group == 1) break;
+  }
+  if (lds > (size_t)max_lds) return HQ_EINVAL;
   int grid;
-  rc = grid_for((const void*)fn, block, lds, (P.C + kGroupChunks - 1) / kGroupChunks, &grid);
+  rc = grid_for((const void*)fn, block, lds, (P.C + group - 1) / group, &grid);
   if (rc) return rc;
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   const float inv_n = 1.0f / (float)tile;   // exact: tile is a power of two
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, x, (uint32_t)(dtype == HQ_BF16), P.T, P.C, P.c, inv_sqrtn, inv_n,
                      derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, payload, cap, step, meta,
-                     chunk_off, status, (uint32_t*)ws, P.stage_words);
+                     chunk_off, status, (uint32_t*)ws, stage_words, group);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
