@@ -96,6 +96,17 @@ def test_tile_counts(T):
     check_full(x, 128, "E8", 4.0, seed=T, kv=False, dtype="bf16")
 
 
+# The encoder stages several chunks per ticket (as many as LDS allows, at
+# most 4): chunk counts of 5, 6, 8, 10 and 17 give partial last groups and
+# several groups, at both tile sizes the configurations use.
+@pytest.mark.parametrize("chunks", [5, 6, 8, 10, 17])
+@pytest.mark.parametrize("tile", [128, 256])
+def test_chunk_groups(chunks, tile):
+    T = 64 * (chunks - 1) + 7
+    x = workloads.gaussian(T, tile, key=1000 + chunks)
+    check_full(x, tile, "E8", 4.0, seed=chunks, kv=False, dtype="bf16")
+
+
 @pytest.mark.parametrize("bps", [1.5, 3.0, 5.0, 8.0])
 @pytest.mark.parametrize("tile", [128, 256])
 def test_rate_extremes(bps, tile):
@@ -121,14 +132,16 @@ def test_special_values():
 def test_repeatable_and_workspace_reuse():
     # the ticket counter and look-back tags reset themselves between calls of
     # different sizes sharing one workspace
-    for T in (320, 64 * 300 + 17, 70, 64 * 40):
-        x = workloads.gaussian(T, 128, key=T)
+    # (tile and rate change the chunks staged per ticket, hence the ticket count)
+    for T, tile, bps in ((320, 128, 4.0), (64 * 300 + 17, 128, 4.0), (70, 128, 4.0), (64 * 40, 128, 4.0),
+                         (64 * 9 + 3, 256, 8.0), (64 * 5, 256, 2.0), (64 * 13, 128, 4.0)):
+        x = workloads.gaussian(T, tile, key=T)
         xd, _ = to_device(x, "bf16")
-        outs = [gpu_encode(xd, 128, "E8", 4.0, 5, False)[1] for _ in range(3)]
+        outs = [gpu_encode(xd, tile, "E8", bps, 5, False)[1] for _ in range(3)]
         for o in outs[1:]:
             for k in ("step", "meta", "off", "payload"):
                 np.testing.assert_array_equal(o[k], outs[0][k])
-        check_full(x, 128, "E8", 4.0, seed=5, kv=False, dtype="bf16")
+        check_full(x, tile, "E8", bps, seed=5, kv=False, dtype="bf16")
 
 
 def test_decoder_on_oracle_streams_and_corruption():
