@@ -258,3 +258,16 @@ def test_config4_dit_layer(layer):
     # 0.5% unit-scale outliers (50x the bulk) rotate to a +-spike pattern and
     # code slightly longer, so this stack lands ~0.09 bps above target
     assert abs(bps - 4.0) < 0.15
+
+
+def test_beyond_2_31_scalars():
+    # 2^31 + 2^20 scalars (4.3 GB of bf16): tile indices, element offsets and
+    # payload word offsets run past the signed 32-bit range; the sampled
+    # chunks include the ones on either side of element 2^31, and the last
+    rows, cols = (1 << 17) + 64, 16384
+    xd = workloads.dit_layer_device(rows, cols, 0, _dev())
+    xo = workloads.bf16_bits(xd)
+    T = rows * cols // 256
+    C = (T + 63) // 64
+    straddle = (1 << 31) // 256 // 64
+    sampled_parity(xd, xo, 256, "E8", 4.0, (31 << 32) | 1, False, [0, straddle - 1, straddle, C - 1])
