@@ -135,24 +135,28 @@ __device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t&
 
 // E8 straight to Rice symbols, for the encoder's quantiser: the same choice
 // and tie rules as nearest_e8 followed by block_symbols, arranged for fewer
-// vector operations.  With f = rint(t) and delta = t - f:
+// operations.  With f = rint(t) and delta = t - f:
 //  - floor(t) = f - [delta < 0], so the half-integer candidate's coset parity
 //    is f's parity flipped by the number of negative deltas;
 //  - the moved coordinate is the first one whose |delta| equals the max (A)
 //    or the min (B); A moves it by +1 if delta >= 0 else -1; B moves
 //    floor(t) by +1 if t >= floor(t) + 1/2, i.e. if delta < 0 or
 //    delta == 1/2, else by -1.
-// The per-coordinate conditions are lane masks, so "first equal", its sign
-// and the parity of the negative deltas are scalar mask operations.  The
-// symbol zz(d) = |2 d + 1/2| - 1/2 is formed in fp32 as |fma(f, 2, c)| - 1/2,
-// where c = 1/2 - 2 [B and delta < 0] + 2 [moved] dir carries the floor
-// correction and the move (exact: every value is a small integer or half).
+// Every integer code is d = f + adj: adj = -[B and delta < 0] (the floor)
+// for the coordinates that do not move, and that plus the move for the one
+// that does.  The symbol zz(d) = |2 d + 1/2| - 1/2 is the truncation of
+// |fma(f, 2, 1/2 + 2 adj)| to an integer (exact: small integers and halves).
+// The per-coordinate conditions are lane masks ("first equal" and the parity
+// of the negative deltas are scalar mask operations), and the moved
+// coordinate's 1/2 + 2 adj is one per-lane value, so each coordinate costs two
+// selects, an fma and a conversion.
 struct E8Choice {
   float f[8];        // rint(t)
   bool neg[8];       // t - rint(t) < 0
-  bool first[8];     // the moved coordinate (at most one)
+  bool first[8];     // the moved coordinate, if any moves (at most one)
   bool useB;         // half-integer coset
-  float mv;          // twice the move: +-2, or 0 when no coordinate moves
+  bool negj;         // the first coordinate's delta is negative
+  float mvh;         // the move: +1, -1, or 0 when no coordinate moves
 };
 
 __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
@@ -189,38 +193,44 @@ __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
     seen = seen | eq;
     negj = negj | (c.first[i] & c.neg[i]);
   }
+  c.negj = negj;
   const bool odd = c.useB ? oddB : oddA;
   const bool up = c.useB ? (negj | (target == 0.5f)) : !negj;
-  c.mv = odd ? (up ? 2.0f : -2.0f) : 0.0f;
+  c.mvh = odd ? (up ? 1.0f : -1.0f) : 0.0f;
 }
 
 __device__ __forceinline__ void nearest_e8_symbols(const float* t, uint32_t* u, uint32_t& p) {
   E8Choice c;
   e8_choose(t, c);
+  // 1/2 + 2 adj of the moved coordinate
+  const float K = ((c.useB & c.negj) ? -1.5f : 0.5f) + 2.0f * c.mvh;
 #pragma unroll
   for (int i = 0; i < 7; i++) {
-    const float c0 = (c.useB & c.neg[i]) ? -1.5f : 0.5f;
-    const float cc = c.first[i] ? c0 + c.mv : c0;
-    u[i] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(c.f[i], 2.0f, cc)) - 0.5f);
+    const float x = (c.useB & c.neg[i]) ? -1.5f : 0.5f;
+    const float cc = c.first[i] ? K : x;
+    u[i] = (uint32_t)__builtin_fabsf(__builtin_fmaf(c.f[i], 2.0f, cc));
   }
   {
-    // the last coordinate is stored halved (floor), its parity being the others' sum's
-    const float d7 = c.f[7] + (((c.useB & c.neg[7]) ? -1.0f : 0.0f) + (c.first[7] ? 0.5f * c.mv : 0.0f));
-    const float h = __builtin_floorf(d7 * 0.5f);
-    u[7] = (uint32_t)(__builtin_fabsf(__builtin_fmaf(h, 2.0f, 0.5f)) - 0.5f);
+    // the last coordinate is stored halved (floor), its parity being the others' sum's:
+    // floor((f + adj) / 2) with adj / 2 = (cc - 1/2) / 4
+    const float x = (c.useB & c.neg[7]) ? -0.5f : 0.0f;
+    const float ch = c.first[7] ? __builtin_fmaf(K, 0.25f, -0.125f) : x;
+    const float h = __builtin_floorf(__builtin_fmaf(c.f[7], 0.5f, ch));
+    u[7] = (uint32_t)__builtin_fabsf(__builtin_fmaf(h, 2.0f, 0.5f));
   }
   p = c.useB ? 1u : 0u;
 }
 
-// The nearest E8 point itself (same choice): point = f + c with
-// c = (B ? (delta < 0 ? -1/2 : +1/2) : 0) + [moved] dir.
+// The nearest E8 point itself (same choice): f + adj, plus 1/2 in coset B.
 __device__ __forceinline__ void nearest_e8_point(const float* t, float* pt) {
   E8Choice c;
   e8_choose(t, c);
+  const float base = c.useB ? 0.5f : 0.0f;
+  const float Kp = ((c.useB & c.negj) ? -0.5f : base) + c.mvh;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const float c0 = c.useB ? (c.neg[i] ? -0.5f : 0.5f) : 0.0f;
-    pt[i] = c.f[i] + (c.first[i] ? c0 + 0.5f * c.mv : c0);
+    const float x = (c.useB & c.neg[i]) ? -0.5f : base;
+    pt[i] = c.f[i] + (c.first[i] ? Kp : x);
   }
 }
 

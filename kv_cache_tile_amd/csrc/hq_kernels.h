@@ -37,6 +37,7 @@ namespace hq {
 // would write back / invalidate the whole L2 of the XCD on every chunk).
 constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+constexpr int kLookJ = 4;                                   // look-back predecessors per lane per round
 
 // Rice fields of one lane (32 symbols, parameter K) into the staging bits of
 // its tile starting at bit t0, from the byte-packed symbols P (symbol 4j + m
@@ -140,15 +141,17 @@ __device__ __forceinline__ void pack_lane_pairs(uint32_t* stage, uint32_t t0, in
   }
 }
 
-// Draw a chunk ticket; the holder of the last one resets the counter and
-// moves the epoch on, leaving the workspace ready for the next call.
-__device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint32_t last_ticket, uint32_t epoch) {
-  const uint32_t tk = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tk == last_ticket) {
+// Draw a group ticket from the counter (the first group of each workgroup is
+// its own index; the counter numbers the groups after those); the holder of
+// the last draw resets the counter and moves the epoch on, leaving the
+// workspace ready for the next call.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint32_t last_draw, uint32_t epoch) {
+  const uint32_t v = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v == last_draw) {
     __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return tk;
+  return gridDim.x + v;
 }
 
 // Sign diagonal (Methodology 1): bit i of lane q's mask is the sign of tile
@@ -176,7 +179,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
               uint32_t* __restrict__ payload, uint64_t cap_words,
               uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
               uint32_t* __restrict__ chunk_off, uint32_t* __restrict__ status,
-              uint32_t* __restrict__ ws, uint32_t stage_words, uint32_t group_chunks) {
+              uint32_t* __restrict__ ws, uint32_t stage_words, uint32_t grp_words, uint32_t group_chunks) {
   constexpr int LPT = N / kLaneElems;                       // lanes per tile
   constexpr int D = LatticeTraits<LAT>::dim;
   constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
@@ -184,12 +187,12 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   constexpr uint32_t B = CB_LANE * LPT;                     // coset bits per tile
 
   extern __shared__ uint32_t smem[];
-  uint32_t* stage = smem;                                   // [stage_words]
+  uint32_t* stage = smem;                                   // [stage_words]: two group areas
   uint32_t* tile_len = smem + stage_words;                  // [64]
   uint32_t* tile_off = tile_len + kChunkTiles;              // [64]
   uint32_t* misc = tile_off + kChunkTiles;                  // [4]
   uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
-  uint32_t* goff = smask + 8;                               // [group_chunks] chunk word offsets in the group
+  uint32_t* goff = smask + 8;                               // [2][kMaxGroupChunks] chunk word offsets per half
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -205,47 +208,140 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
-  // Tickets number groups of group_chunks consecutive chunks; a workgroup
-  // takes tickets one after another until it draws one >= the group count,
-  // and one look-back places a whole group.  Every workgroup reads the epoch
-  // before its first ticket, so the holder of the very last ticket
-  // (groups + grid - 1) can reset the counter and bump the epoch for the
-  // next call.
+  // Tickets number groups of group_chunks consecutive chunks.  Workgroup b's
+  // first group is group b (the grid is at most the group count: no
+  // contended atomic at start-up); after that a workgroup draws tickets
+  // grid + 0, 1, 2, ... from the counter until it gets one >= the group
+  // count, and one look-back places a whole group.  The draws number exactly
+  // groups (grid - groups succeed, each workgroup's last fails), every
+  // workgroup reads the epoch before its first draw, so the holder of the
+  // very last draw (groups - 1) can reset the counter and bump the epoch for
+  // the next call.
   const uint64_t CG = (C + group_chunks - 1) / group_chunks;
-  const uint32_t last_ticket = (uint32_t)(CG + gridDim.x - 1);
-  if (tid == 0) {
-    const uint32_t ep = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
-    misc[2] = ep;
-    misc[0] = take_ticket(ws, last_ticket, ep);
-  }
+  const uint32_t last_draw = (uint32_t)(CG - 1);
+  if (tid == 0)
+    misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
   for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
   const uint32_t epoch = misc[2];
-  uint64_t grp = misc[0];
+  uint64_t grp = blockIdx.x;
   uint64_t chunk = grp * group_chunks;
   uint32_t gi = 0, gw = 0;                                  // chunk of the group, group words staged so far
   bool gfits = true;
 
   // bf16 input of the chunk about to be processed, loaded one phase ahead
   // (the next chunk of a group during this one's scan and packing; a new
-  // group's first chunk during the previous group's look-back and copy-out)
+  // group's first chunk as soon as its ticket is known).
+  // A tile past the end (ragged last chunk, or no chunk left) loads the last
+  // tile instead: its results are never stored, and the registers need no
+  // clearing.
   uint4 pre[4];
   auto prefetch = [&](uint64_t ch) {
-    const uint64_t tt = ch * kChunkTiles + (uint64_t)tau;
-    if (bf16 && ch < C && tt < T) {
+    if (bf16) {
+      uint64_t tt = ch * kChunkTiles + (uint64_t)tau;
+      tt = tt < T ? tt : T - 1;
       const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + tt * N +
                                                       (uint64_t)q * kLaneElems);
 #pragma unroll
       for (int v = 0; v < 4; v++) pre[v] = p[v];
-    } else {
-#pragma unroll
-      for (int v = 0; v < 4; v++) pre[v] = make_uint4(0u, 0u, 0u, 0u);   // (dead between uses)
     }
   };
   prefetch(chunk);
 
+  // The staging area holds two group areas of grp_words (a group's worst
+  // case), at 0 and at stage_words - grp_words; consecutive groups of a
+  // workgroup alternate between them.  A finished group stays in its area
+  // while the next group computes and packs into the other, and is placed at
+  // the start of that group's last chunk: wave 0 runs its look-back (its
+  // predecessors have published long since) while the other waves compute,
+  // and its words are copied out after that chunk's compute barrier.  When
+  // the two areas overlap (less LDS than two worst cases) and the words
+  // actually written would meet, the finished group is placed at once.
+  const uint32_t base1 = stage_words - grp_words;          // the second area's first word
+  uint32_t h = 0;                                           // the current group's area
+  bool pend = false, pgfits = true;
+  uint64_t pgrp = 0, pchunk = 0;
+  uint32_t pgtotal = 0, pgi = 0, ph = 0;
+
+  // wave 0: decoupled look-back over groups.  A round loads kLookJ
+  // predecessors per lane at once (distance d = 64 jj + lane, all loads in
+  // flight together), waits until each has published, and sums the values up
+  // to the nearest inclusive prefix.  Then the group's inclusive prefix, its
+  // chunks' offsets and its status; misc[3] = its first word.
+  auto place = [&]() {
+    uint32_t excl = 0;
+    if (pgrp > 0) {
+      int64_t base = (int64_t)pgrp - 1;
+      for (;;) {
+        uint64_t v[kLookJ];
+#pragma unroll
+        for (int jj = 0; jj < kLookJ; jj++) {
+          const int64_t j = base - (int64_t)(64 * jj + tid);
+          v[jj] = j < 0 ? ((uint64_t)((epoch << 2) | kFlagIncl) << 32)   // before group 0: prefix 0
+                        : __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (;;) {
+          bool done = true;
+#pragma unroll
+          for (int jj = 0; jj < kLookJ; jj++) {
+            const uint32_t hi = (uint32_t)(v[jj] >> 32);
+            if ((hi >> 2) != epoch || (hi & 3u) == 0) {
+              const int64_t j = base - (int64_t)(64 * jj + tid);
+              v[jj] = __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const uint32_t h2 = (uint32_t)(v[jj] >> 32);
+              done = done & ((h2 >> 2) == epoch) & ((h2 & 3u) != 0);
+            }
+          }
+          if (__all(done)) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        uint32_t first = 0xFFFFFFFFu;                        // distance of the nearest inclusive prefix
+#pragma unroll
+        for (int jj = kLookJ - 1; jj >= 0; jj--) {
+          const uint64_t m = __ballot(((uint32_t)(v[jj] >> 32) & 3u) == kFlagIncl);
+          if (m) first = 64u * (uint32_t)jj + (uint32_t)__builtin_ctzll(m);
+        }
+        uint32_t part = 0;
+#pragma unroll
+        for (int jj = 0; jj < kLookJ; jj++)
+          part += (64u * (uint32_t)jj + (uint32_t)tid <= first) ? (uint32_t)v[jj] : 0u;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m);
+        excl += part;
+        if (first != 0xFFFFFFFFu) break;
+        base -= 64 * kLookJ;
+      }
+    }
+    if (tid == 0) {
+      if (pgrp > 0) {
+        uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
+        __hip_atomic_store(&look[pgrp], (tag << 32) | (uint64_t)(excl + pgtotal), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      misc[3] = excl;
+      const uint64_t c0 = pgrp * group_chunks;
+      for (uint32_t i = 0; i <= pgi; i++) chunk_off[c0 + i] = excl + goff[ph * kMaxGroupChunks + i];
+      if (pchunk == C - 1) chunk_off[C] = excl + pgtotal;
+      if (!pgfits || (uint64_t)excl + pgtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+    }
+  };
+  // all threads, after place() and a barrier: the placed group's words out,
+  // clearing its area behind them
+  auto copy_out = [&]() {
+    const uint32_t excl = misc[3];
+    const bool store = pgfits && (uint64_t)excl + pgtotal <= cap_words;
+    const uint32_t zw = pgtotal + 2 < grp_words ? pgtotal + 2 : grp_words;
+    uint32_t* src = stage + (ph ? base1 : 0u);
+    for (uint32_t i = tid; i < zw; i += blockDim.x) {
+      if (store && i < pgtotal) payload[excl + i] = src[i];
+      src[i] = 0u;
+    }
+  };
+
   for (;;) {
     if (grp >= CG) break;
+    const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
+    if (pend && last && tid < 64) place();
 
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
@@ -257,33 +353,30 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     opaque(sw[0]);
     opaque(sw[1]);
     opaque(sg);
-    if (active) {
-      const uint64_t base = t * N + (uint64_t)q * kLaneElems;
-      if (bf16) {
+    // (an inactive tile works on the last tile's data and stores nothing)
+    if (bf16) {
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-          const uint4 w = pre[v];
-          uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      for (int v = 0; v < 4; v++) {
+        const uint4 w = pre[v];
+        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int h = 0; h < 4; h++) {
-            const uint32_t pw = ww[h] ^ pair_sign_mask(sw, 4 * v + h);
-            a[v * 8 + 2 * h] = as_f(pw << 16);
-            a[v * 8 + 2 * h + 1] = as_f(pw & 0xFFFF0000u);
-          }
+        for (int h = 0; h < 4; h++) {
+          uint32_t pw = ww[h] ^ pair_sign_mask(sw, 4 * v + h);
+          opaque(pw);                                       // one xor per pair, then the two halves
+          a[v * 8 + 2 * h] = as_f(pw << 16);
+          a[v * 8 + 2 * h + 1] = as_f(pw & 0xFFFF0000u);
         }
-      } else {
-        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
-#pragma unroll
-        for (int v = 0; v < 8; v++) {
-          float4 w = p[v];
-          a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
-        }
-#pragma unroll
-        for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ ((sg << (31 - i)) & 0x80000000u));
       }
     } else {
+      const uint64_t base = (active ? t : T - 1) * N + (uint64_t)q * kLaneElems;
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+      for (int v = 0; v < 8; v++) {
+        float4 w = p[v];
+        a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
+      }
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ ((sg << (31 - i)) & 0x80000000u));
     }
 
     // ---- RHT: butterfly, then 1/sqrt(n) (with the lane's butterfly sign) ----
@@ -397,11 +490,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       uint32_t L[3], Tt[3];
 #pragma unroll
       for (int jj = 0; jj < 3; jj++) {
+        // sum of (sym >> k) = (sum of sym with its low k bits cleared) >> k
         const uint32_t kk = kb + (uint32_t)jj;
-        const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
+        const uint32_t bmask = 0x01010101u * ((0xFFu << kk) & 0xFFu);
         uint32_t acc = 0;
 #pragma unroll
-        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((R[j] >> kk) & bmask, 0u, acc);
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
+        acc >>= kk;
         L[jj] = acc;
         uint32_t tot = acc;
 #pragma unroll
@@ -428,9 +523,10 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       for (uint32_t kk = 0; kk < 8u; kk++) {
         uint32_t acc = 0;
         if (bytes) {
-          const uint32_t bmask = 0x01010101u * (0xFFu >> kk);
+          const uint32_t bmask = 0x01010101u * ((0xFFu << kk) & 0xFFu);
 #pragma unroll
-          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8((R[j] >> kk) & bmask, 0u, acc);
+          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
+          acc >>= kk;
         } else {
           // 16-bit halves: each half's sum stays below 2^16 (16 symbols < 2^12)
           const uint32_t hmask = 0x00010001u * (0xFFFFu >> kk);
@@ -471,9 +567,12 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       }
     }
     __syncthreads();
+    if (pend && last) {
+      copy_out();
+      pend = false;
+    }
 
     // the group's next chunk: load its input during this one's scan and packing
-    const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
     if (!last) prefetch(chunk + 1);
 
     // ---- chunk scan: bit offset of every tile inside the chunk; after the
@@ -499,31 +598,41 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     __syncthreads();
     const uint32_t total_bits = misc[1];
     const uint32_t W = (total_bits + 31u) >> 5;
-    const bool fits = gw + W + 2 <= stage_words;
+    const bool fits = gw + W + 2 <= grp_words;
     gfits = gfits && fits;
-    if (tid == 0) goff[gi] = gw;                            // this chunk's word offset in the group
-    // after the group's last chunk: next ticket now (its reply arrives
+    if (tid == 0) goff[h * kMaxGroupChunks + gi] = gw;      // this chunk's word offset in the group
+    // after the group's last chunk: the next ticket now (its reply arrives
     // during the packing)
     uint32_t next_ticket = 0;
-    if (last && tid == 64) next_ticket = take_ticket(ws, last_ticket, epoch);
+    if (last && tid == 64) next_ticket = take_ticket(ws, last_draw, epoch);
+
+    // the words about to be written would meet the finished group's: place it now
+    if (pend && (h ? pgtotal + 2 > base1 : gw + W + 2 > base1)) {
+      if (tid < 64) place();
+      __syncthreads();
+      copy_out();
+      pend = false;
+      __syncthreads();
+    }
 
     // ---- pack: coset bits | remainder plane (k bits per symbol) | unary plane,
-    // at the chunk's word offset in the group's staging area (zero: cleared at
-    // the start and after each copy) ----
+    // at the chunk's word offset in the group's area of the staging area
+    // (zero: cleared at the start and after each copy) ----
     if (active && fits) {
+      uint32_t* stage_h = stage + (h ? base1 : 0u);
       const uint32_t t0 = gw * 32u + tile_off[tau];
-      if constexpr (CB_LANE > 0) lds_or_bits(stage, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
+      if constexpr (CB_LANE > 0) lds_or_bits(stage_h, t0 + (uint32_t)q * CB_LANE, cb, CB_LANE);
       if (bytes) {
         switch (k) {
 #define HQ_PACK_CASE(KK) \
-          case KK: pack_lane_bytes<KK, N, B>(stage, t0, q, R, lane_excl); break;
+          case KK: pack_lane_bytes<KK, N, B>(stage_h, t0, q, R, lane_excl); break;
           HQ_PACK_CASE(0) HQ_PACK_CASE(1) HQ_PACK_CASE(2) HQ_PACK_CASE(3)
           HQ_PACK_CASE(4) HQ_PACK_CASE(5) HQ_PACK_CASE(6)
-          default: pack_lane_bytes<7, N, B>(stage, t0, q, R, lane_excl); break;
+          default: pack_lane_bytes<7, N, B>(stage_h, t0, q, R, lane_excl); break;
 #undef HQ_PACK_CASE
         }
       } else {
-        pack_lane_pairs<N, B>(stage, t0, q, R, k, lane_excl);
+        pack_lane_pairs<N, B>(stage_h, t0, q, R, k, lane_excl);
       }
     }
     if (last && tid == 64) misc[0] = next_ticket;
@@ -534,72 +643,25 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       chunk++;
       continue;
     }
-    const uint32_t gtotal = gw + W;                         // the group's words
-    const uint64_t next = misc[0];
-    prefetch(next * group_chunks);
-
-    // ---- wave 0: decoupled look-back over groups, one predecessor per lane.
-    // It comes after the packing: by then the nearest predecessors have
-    // published their sizes, and waiting lanes poll less ----
-    if (tid < 64) {
-      uint32_t excl = 0;
-      if (grp > 0) {
-        int64_t base = (int64_t)grp - 1;
-        for (;;) {
-          const int64_t j = base - tid;
-          uint64_t v;
-          uint32_t flag;
-          if (j < 0) {
-            v = 0;
-            flag = kFlagIncl;                                // before group 0: prefix 0
-          } else {
-            for (;;) {
-              v = __hip_atomic_load(&look[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              const uint32_t hi = (uint32_t)(v >> 32);
-              if ((hi >> 2) == epoch && (hi & 3u) != 0) { flag = hi & 3u; break; }
-              __builtin_amdgcn_s_sleep(1);
-            }
-          }
-          const uint64_t incl_mask = __ballot(flag == kFlagIncl);
-          const int first = incl_mask ? __builtin_ctzll(incl_mask) : 64;
-          uint32_t part = (tid <= first) ? (uint32_t)v : 0u;
-#pragma unroll
-          for (int m = 1; m < 64; m <<= 1) part += __shfl_xor(part, m);
-          excl += part;
-          if (incl_mask) break;
-          base -= 64;
-        }
-      }
-      if (tid == 0) {
-        if (grp > 0) {
-          uint64_t tag = (uint64_t)((epoch << 2) | kFlagIncl);
-          __hip_atomic_store(&look[grp], (tag << 32) | (uint64_t)(excl + gtotal), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
-        misc[3] = excl;
-        const uint64_t c0 = grp * group_chunks;
-        for (uint32_t i = 0; i <= gi; i++) chunk_off[c0 + i] = excl + goff[i];
-        if (chunk == C - 1) chunk_off[C] = excl + gtotal;
-        if (!gfits || (uint64_t)excl + gtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
-      }
-    }
-
-    __syncthreads();
-
-    // ---- copy the group's words out, clearing the staging area behind ----
-    const uint32_t excl = misc[3];
-    const bool store = gfits && (uint64_t)excl + gtotal <= cap_words;
-    const uint32_t zw = gtotal + 2 < stage_words ? gtotal + 2 : stage_words;
-    for (uint32_t i = tid; i < zw; i += blockDim.x) {
-      if (store && i < gtotal) payload[excl + i] = stage[i];
-      stage[i] = 0u;
-    }
-    __syncthreads();
-    grp = next;
+    pend = true;
+    pgrp = grp;
+    pchunk = chunk;
+    pgtotal = gw + W;                                       // the group's words
+    pgi = gi;
+    pgfits = gfits;
+    ph = h;
+    h ^= 1u;
+    grp = misc[0];
     chunk = grp * group_chunks;
+    prefetch(chunk);
     gi = 0;
     gw = 0;
     gfits = true;
+  }
+  if (pend) {                                               // the workgroup's last group
+    if (tid < 64) place();
+    __syncthreads();
+    copy_out();
   }
 }
 
@@ -863,9 +925,22 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       // lane q holds (-1)^popcount(q) times the butterfly output: fold that
       // sign into the scale; + 0.0f turns a -0 into +0 (every zero of the
       // exact butterfly is +0), then apply the sign diagonal (on the packed
-      // bf16 pairs: rounding to nearest even commutes with a sign flip)
+      // bf16 pairs: rounding to nearest even commutes with a sign flip).
+      // fma(a, scale, +0) is that value in one operation, except where a
+      // nonzero product rounds to zero (then it keeps the product's sign): a
+      // second + 0.0f settles those, and is needed only for tiny steps.  The
+      // butterfly's inputs are at least 2^-26 |s| when nonzero (lattice
+      // coordinates are multiples of 1/2, dithered ones at least 2^-25 from
+      // zero), its sums stay multiples of the finest input's unit, so every
+      // nonzero output is at least 2^-50 |s|: no product underflows for
+      // |s| >= 2^-90.
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * lane_scale + 0.0f;
+      for (int i = 0; i < kLaneElems; i++) a[i] = __builtin_fmaf(a[i], lane_scale, 0.0f);
+      if (__any(!(__builtin_fabsf(as_f(sraw << 16)) >= 0x1p-90f))) {
+        asm volatile("");                                   // (a branch, not selects)
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = a[i] + 0.0f;
+      }
       uint32_t sw[2] = {sgnw[0], sgnw[1]}, sg = sgn;
       opaque(sw[0]);
       opaque(sw[1]);
@@ -896,7 +971,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 // ---- per-lattice kernel tables (defined in hq_kern_<lattice>.hip) ----------
 using EncFn = void (*)(const void*, uint32_t, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t,
                        A2Consts, uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*,
-                       uint32_t, uint32_t);
+                       uint32_t, uint32_t, uint32_t);
 using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
                        uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t, uint32_t*, uint32_t,
                        uint32_t, uint32_t);

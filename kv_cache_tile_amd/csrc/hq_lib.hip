@@ -10,6 +10,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "hq.h"
@@ -139,30 +140,42 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
   EncFn fn = enc_fn(lat, tile, kv != 0);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
-  // chunks staged per ticket: as many (up to kMaxGroupChunks) as fit a
-  // workgroup's LDS with room for two workgroups per CU
-  int dev = 0, max_lds = 0;
+  // chunks staged per ticket: as many (up to kMaxGroupChunks) as fit the LDS
+  // share of a workgroup at the occupancy its registers allow; the staging
+  // area takes the whole share, room for a second group's words
+  int dev = 0, max_lds = 0, lds_cu = 0, per_regs = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_regs, (const void*)fn, block, 0) != hipSuccess)
     return HQ_EHIP;
-  const size_t lds_cap = (size_t)max_lds < (size_t)80 * 1024 ? (size_t)max_lds : (size_t)80 * 1024;
-  uint32_t group = kMaxGroupChunks, stage_words = 0;
-  size_t lds = 0;
-  for (;; group >>= 1) {
-    stage_words = group * P.chunk_words + 4;
-    lds = (size_t)(stage_words + 2 * kChunkTiles + 4 + 8 + kMaxGroupChunks) * 4;
-    if (lds <= lds_cap || group == 1) break;
+  size_t lds_cap = per_regs > 0 ? (size_t)lds_cu / (size_t)per_regs : (size_t)max_lds;
+  if (lds_cap > (size_t)max_lds) lds_cap = (size_t)max_lds;
+  const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks;
+  const size_t avail = lds_cap / 4 > fixed_words ? lds_cap / 4 - fixed_words : 0;
+  uint32_t group = kMaxGroupChunks, grp_words = 0;
+  for (;; group--) {
+    grp_words = group * P.chunk_words + 4;
+    if (grp_words <= avail || group == 1) break;
   }
+  const uint32_t stage_words = avail > grp_words ? (uint32_t)avail : grp_words;
+  const size_t lds = (stage_words + fixed_words) * 4;
   if (lds > (size_t)max_lds) return HQ_EINVAL;
   int grid;
   rc = grid_for((const void*)fn, block, lds, (P.C + group - 1) / group, &grid);
   if (rc) return rc;
+  // a smaller grid on request (tests use it so that few chunks still give a
+  // workgroup several groups, alternating between the staging halves)
+  if (const char* e = getenv("HQ_ENCODE_GRID_CAP")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0 && v < grid) grid = (int)v;
+  }
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   const float inv_n = 1.0f / (float)tile;   // exact: tile is a power of two
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, x, (uint32_t)(dtype == HQ_BF16), P.T, P.C, P.c, inv_sqrtn, inv_n,
                      derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, payload, cap, step, meta,
-                     chunk_off, status, (uint32_t*)ws, stage_words, group);
+                     chunk_off, status, (uint32_t*)ws, stage_words, grp_words, group);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
