@@ -440,6 +440,18 @@ __device__ __forceinline__ uint32_t pair_sign_mask(const uint32_t (&W)[2], int p
 // masks would otherwise be hoisted out of the chunk loop and held in 32 VGPRs.
 __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
+// Issue priority of the calling wave (the hardware's four levels, 0..3).
+// Among ready waves the arbiter picks the highest priority, then the oldest:
+// with equal priorities the workgroup dispatched first on a CU races ahead
+// and the CU ends half empty.  The kernels lower a wave's priority as its
+// workgroup's share of the work shrinks, so whichever is behind catches up.
+__device__ __forceinline__ void wave_priority(uint32_t p) {
+  if (p == 0) __builtin_amdgcn_s_setprio(0);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
+}
+
 // Lanes of a tile.  At n = 256 (8 lanes per tile) physical lanes 4..7 hold
 // logical lanes 7..4, so that the stride-128 butterfly partner q ^ 4 is the
 // half-row mirror p ^ 7, a DPP pattern; the partners q ^ 1 and q ^ 2 stay

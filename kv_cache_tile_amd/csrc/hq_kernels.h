@@ -338,8 +338,13 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
   };
 
+  // this workgroup's expected share of chunks; priority falls by quarters of it
+  const uint32_t share = (uint32_t)((C + gridDim.x - 1) / gridDim.x);
+  uint32_t done = 0;
   for (;;) {
     if (grp >= CG) break;
+    const uint32_t quarters = 4u * done++ / share;
+    wave_priority(quarters >= 3u ? 0u : 3u - quarters);
     const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
     if (pend && last && tid < 64) place();
 
@@ -804,7 +809,11 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
   const uint64_t units = C * SUB;
+  // priority by the units this workgroup has left (the current one included)
+  uint64_t left = blockIdx.x < units ? (units - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
   for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    wave_priority(left >= 4u ? 3u : (uint32_t)left - 1u);
+    left--;
     const uint64_t chunk = unit / SUB;
     const int first = (int)(unit % SUB) * TPW;              // first tile of this unit in the chunk
     const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
