@@ -440,6 +440,22 @@ __device__ __forceinline__ uint32_t pair_sign_mask(const uint32_t (&W)[2], int p
 // masks would otherwise be hoisted out of the chunk loop and held in 32 VGPRs.
 __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
+// gfx950's global -> LDS load, 16 bytes a lane: from base + voff (bytes) to
+// the wave's LDS block at byte address lds (m0), lane i's 16 bytes at
+// lds + 16 i.  Written as the instruction: the compiler cannot tell a
+// kernel's stage buffers apart and would otherwise wait for it before every
+// later LDS access; the callers wait for it themselves (vmcnt, then a
+// barrier) before the buffer is read.  It writes no register.
+__device__ __forceinline__ void lds_load16(const uint32_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Issue priority of the calling wave (the hardware's four levels, 0..3).
 // Among ready waves the arbiter picks the highest priority, then the oldest:
 // with equal priorities the workgroup dispatched first on a CU races ahead

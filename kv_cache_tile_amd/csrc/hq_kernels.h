@@ -785,77 +785,159 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   constexpr int LPT = N / kLaneElems;
   constexpr int TPW = DecodeGeom<N>::TPW;
   constexpr int SUB = DecodeGeom<N>::SUB;
+  constexpr int THREADS = DecodeGeom<N>::THREADS;
   constexpr int D = LatticeTraits<LAT>::dim;
   constexpr int BPL = kLaneElems / D;
   constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
   constexpr uint32_t B = CB_LANE * LPT;
 
+  // Two buffer sets, used by alternate units: while a unit is decoded from
+  // one, the next unit's words stream into the other (global -> LDS loads in
+  // flight during the decode), and wave 0 has scanned its chunk from tile
+  // metadata it loaded a unit earlier.  No global load is waited for on the
+  // critical path; two barriers per unit.
   extern __shared__ uint32_t smem[];
-  uint32_t* stage = smem;                                   // [stage_words] this unit's bits + guard
-  uint32_t* tile_off = stage + stage_words;                 // [64] bit offset of each tile in the chunk
-  uint32_t* tile_ok = tile_off + kChunkTiles;               // [64]
-  uint32_t* ustart = tile_ok + kChunkTiles;                 // [TPW * LPT] first unary bit per lane
-  uint32_t* misc = ustart + TPW * LPT;                      // [4]
-  uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
+  uint32_t* stage0 = smem;                                  // [2][stage_words] a unit's words + guard
+  uint32_t* tile_off0 = smem + 2 * stage_words;             // [2][64] bit offset of each tile in the chunk
+  uint32_t* tile_ok0 = tile_off0 + 2 * kChunkTiles;         // [2][64]
+  uint32_t* tile_ms0 = tile_ok0 + 2 * kChunkTiles;          // [2][64] meta | step << 16
+  uint32_t* misc0 = tile_ms0 + 2 * kChunkTiles;             // [2][4] see scan()
+  uint32_t* ustart = misc0 + 8;                             // [TPW * LPT] first unary bit per lane
+  uint32_t* smask = ustart + TPW * LPT;                     // [N / 32] sign diagonal bits
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
   const int p_lane = tid % LPT;                            // physical lane in the tile
   const int q = tile_lane<LPT>(p_lane);                     // logical lane
 
-  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
-  uint32_t sgnw[2];
-  pair_sign_words(sgn, sgnw);
+  // the lane's sign diagonal bits stay in LDS (smask[q]), read where needed
+  (void)sign_mask<N>(smask, key_sign, tid, q);
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
+
+  // tile metadata (wave 0) and chunk offsets (every wave: uniform values) of
+  // a unit's chunk, loaded one unit before its scan
+  uint32_t pm = 0, ps = 0;
+  uint64_t pw0 = 0, pw1 = 0;
+  // (loads only, a tile past the end reading the last one: the scan masks
+  // it; no register is rewritten while the stage loads are in flight)
+  auto fetch = [&](uint64_t un) {
+    const uint64_t ch = un / SUB;
+    if (tid < 64) {
+      uint64_t tt = ch * kChunkTiles + (uint64_t)tid;
+      tt = tt < T ? tt : T - 1;
+      pm = (uint32_t)meta[tt];
+      ps = (uint32_t)step[tt];
+    }
+    pw0 = chunk_off[ch];
+    pw1 = chunk_off[ch + 1];
+  };
+  // wave 0: tile offsets inside the chunk (a chunk whose size disagrees with
+  // its tiles is dropped) and the unit's word range.  misc: [0] 32 (L - w0)
+  // (mod 2^32), where stage word 0 is payload word L, the unit's first word
+  // aligned down to 4; [1] 16-byte vectors to stage; [2], [3] L.
+  auto scan = [&](uint64_t un, int set) {
+    const int first = (int)(un % SUB) * TPW;
+    const bool range_ok = pw1 >= pw0 && pw1 <= payload_words && (pw1 - pw0) <= chunk_cap_words;
+    const bool exists = (un / SUB) * kChunkTiles + (uint64_t)tid < T;
+    const uint32_t mt = exists ? pm : 0u, st_ = exists ? ps : 0u;
+    const uint32_t len = mt >> 3, kk = mt & 7u;
+    uint32_t inc = len;
+#pragma unroll
+    for (int s2 = 1; s2 < kChunkTiles; s2 <<= 1) {
+      uint32_t o = __shfl_up(inc, s2, kChunkTiles);
+      if (tid >= s2) inc += o;
+    }
+    tile_off0[set * kChunkTiles + tid] = inc - len;
+    const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
+    const bool too_long = __any(len > tile_bound);          // longer than any valid tile can be
+    const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == pw1 - pw0;
+    tile_ok0[set * kChunkTiles + tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
+    tile_ms0[set * kChunkTiles + tid] = mt | (st_ << 16);
+    // this unit's bits [tile_off[first], tile_off[first + TPW - 1] + len)
+    const uint32_t f0 = __shfl(inc - len, first, kChunkTiles);
+    const uint32_t f1 = __shfl(inc, first + TPW - 1, kChunkTiles);
+    if (tid == 0) {
+      uint64_t L = pw0;
+      uint32_t nvec = 0;
+      if (chunk_ok) {
+        const uint64_t wa = pw0 + (f0 >> 5), we = pw0 + ((f1 + 31u) >> 5);
+        L = wa & ~3ull;
+        nvec = (uint32_t)((we - L + 3u) >> 2);
+      }
+      misc0[set * 4 + 0] = (uint32_t)(L - pw0) * 32u;
+      misc0[set * 4 + 1] = nvec;
+      misc0[set * 4 + 2] = (uint32_t)L;
+      misc0[set * 4 + 3] = (uint32_t)(L >> 32);
+    }
+  };
+  // all threads: start the unit's words streaming into its stage (16 bytes a
+  // lane, straight to LDS; the stream's last, partial vector by plain loads)
+  // and zero the guard words behind them
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  auto stage_in = [&](int set) {
+    const uint32_t nvec = __builtin_amdgcn_readfirstlane(misc0[set * 4 + 1]);
+    const uint64_t L = (uint64_t)__builtin_amdgcn_readfirstlane(misc0[set * 4 + 2]) |
+                       ((uint64_t)__builtin_amdgcn_readfirstlane(misc0[set * 4 + 3]) << 32);
+    uint32_t* st = stage0 + set * stage_words;
+    uint32_t lt = (uint32_t)tid;
+    opaque(lt);                                             // (recomputed here, not held across the unit)
+    const uint32_t wave0 = __builtin_amdgcn_readfirstlane(lt & ~63u);   // this wave's first thread
+    for (uint32_t r = 0; r * (uint32_t)THREADS < nvec; r++) {
+      const uint32_t j = r * (uint32_t)THREADS + lt;
+      if (j < nvec) {
+        const uint64_t g = L + 4ull * j;
+        if (g + 4u <= payload_words) {
+          // this wave's 1 KB of the stage
+          const uint32_t dst = smem_lds + 4u * ((uint32_t)set * stage_words + 4u * (r * (uint32_t)THREADS + wave0));
+          lds_load16(payload + L, 16u * j, dst);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) st[4u * j + (uint32_t)e] = g + (uint64_t)e < payload_words ? payload[g + e] : 0u;
+        }
+      }
+    }
+    if (lt < 8u) st[4u * nvec + lt] = 0u;
+  };
 
   const uint64_t units = C * SUB;
   // priority by the units this workgroup has left (the current one included)
   uint64_t left = blockIdx.x < units ? (units - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
-  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+  if (blockIdx.x < units) {
+    fetch(blockIdx.x);
+    if (tid < 64) scan(blockIdx.x, 0);
+    if (blockIdx.x + gridDim.x < units) fetch(blockIdx.x + gridDim.x);
+    __syncthreads();
+    stage_in(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  int cur = 0;
+  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x, cur ^= 1) {
     wave_priority(left >= 4u ? 3u : (uint32_t)left - 1u);
     left--;
-    const uint64_t chunk = unit / SUB;
-    const int first = (int)(unit % SUB) * TPW;              // first tile of this unit in the chunk
-    const uint64_t w0 = chunk_off[chunk], w1 = chunk_off[chunk + 1];
-    const bool range_ok = w1 >= w0 && w1 <= payload_words && (w1 - w0) <= chunk_cap_words;
-
-    // tile offsets inside the chunk; a chunk whose size disagrees with its tiles is dropped
-    if (tid < kChunkTiles) {
-      const uint64_t tt = chunk * kChunkTiles + (uint64_t)tid;
-      const uint32_t m = tt < T ? (uint32_t)meta[tt] : 0u;
-      const uint32_t len = m >> 3, kk = m & 7u;
-      uint32_t inc = len;
-#pragma unroll
-      for (int s2 = 1; s2 < kChunkTiles; s2 <<= 1) {
-        uint32_t o = __shfl_up(inc, s2, kChunkTiles);
-        if (tid >= s2) inc += o;
-      }
-      tile_off[tid] = inc - len;
-      const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
-      const bool too_long = __any(len > tile_bound);        // longer than any valid tile can be
-      const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == w1 - w0;
-      tile_ok[tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
-      // this unit's bit range [tile_off[first], tile_off[first + TPW]) in whole words
-      if (tid == first) misc[0] = chunk_ok ? (inc - len) : 0u;
-      if (tid == first + TPW - 1) misc[1] = chunk_ok ? inc : 0u;
+    const uint64_t un = unit + gridDim.x;
+    // this unit's words have landed (each wave waited for its own loads
+    // before its previous stores, the barrier waits for everyone's); wave 0
+    // scans the next unit
+    if (un < units) {
+      if (tid < 64) scan(un, cur ^ 1);
+      if (un + gridDim.x < units) fetch(un + gridDim.x);    // (issued before the stage loads)
     }
     __syncthreads();
-    const uint32_t sw = misc[0] >> 5;                       // first staged word (chunk-relative)
-    const uint32_t WL = ((misc[1] + 31u) >> 5) - sw;        // words staged
-    const uint32_t base_bit = sw * 32u;
-    for (uint32_t i = tid; i < WL; i += blockDim.x) stage[i] = payload[w0 + sw + i];
-    if (tid < 8) stage[WL + tid] = 0u;                      // guard words for the readers
-    __syncthreads();
+    if (un < units) stage_in(cur ^ 1);
 
+    const uint32_t* stage = stage0 + cur * stage_words;
+    const uint64_t chunk = unit / SUB;
+    const int first = (int)(unit % SUB) * TPW;              // first tile of this unit in the chunk
     const int ct = first + tau;                             // tile index in the chunk
     const uint64_t t = chunk * kChunkTiles + (uint64_t)ct;
     const bool active = t < T;
-    const uint32_t m = active ? (uint32_t)meta[t] : 0u;
+    const uint32_t ms = tile_ms0[cur * kChunkTiles + ct];
+    const uint32_t m = active ? (ms & 0xFFFFu) : 0u;
     const uint32_t len = m >> 3, k = m & 7u;
-    const uint32_t sraw = active ? (uint32_t)step[t] : 0u;
+    const uint32_t sraw = active ? (ms >> 16) : 0u;
     // a non-finite step is never written by the encoder: corrupt tile
-    bool ok = active && tile_ok[ct] != 0u && (sraw & 0x7F80u) != 0x7F80u;
-    const uint32_t start = tile_off[ct] - base_bit, end = start + len;
+    bool ok = active && tile_ok0[cur * kChunkTiles + ct] != 0u && (sraw & 0x7F80u) != 0x7F80u;
+    const uint32_t start = tile_off0[cur * kChunkTiles + ct] - misc0[cur * 4 + 0], end = start + len;
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
     // ---- where does each lane's first unary code start?  Every codeword has
@@ -901,7 +983,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       uint32_t cbits = 0;
       if constexpr (CB_LANE > 0) cbits = lds_read32(stage, ok ? start + (uint32_t)q * CB_LANE : 0u);
       const uint32_t rb = ok ? start + B + (uint32_t)q * kLaneElems * k : 0u;
-      const uint32_t u0 = ok ? (q == 0 ? ub : ustart[tau * LPT + q]) : 0u;
+      uint32_t lt = (uint32_t)tid;
+      opaque(lt);                                           // (an address recomputed, not spilled)
+      const uint32_t u0 = ok ? (q == 0 ? ub : ustart[(lt & ~(uint32_t)(LPT - 1)) + (uint32_t)q]) : 0u;
       const uint32_t lim = ok ? end : 0u;
       const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
       uint32_t upos = 0;
@@ -922,6 +1006,11 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 #pragma unroll
     for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
     lane_ok = all_ok != 0;
+
+    // the next unit's stage loads, a unit old by now, are complete before
+    // this unit's stores are issued (vector memory operations retire in
+    // order: the next wait needs no store to finish)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- inverse RHT and store (an invalid tile decodes to zeros) ----
     if (active) {
@@ -950,10 +1039,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 #pragma unroll
         for (int i = 0; i < kLaneElems; i++) a[i] = a[i] + 0.0f;
       }
-      uint32_t sw[2] = {sgnw[0], sgnw[1]}, sg = sgn;
-      opaque(sw[0]);
-      opaque(sw[1]);
-      opaque(sg);
+      const uint32_t sg = smask[q];
+      uint32_t sw[2];
+      pair_sign_words(sg, sw);
       const uint64_t base = t * N + (uint64_t)q * kLaneElems;
       if (bf16) {
         uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
@@ -973,7 +1061,6 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
         for (int v = 0; v < 8; v++) p[v] = make_float4(a[v * 4], a[v * 4 + 1], a[v * 4 + 2], a[v * 4 + 3]);
       }
     }
-    __syncthreads();
   }
 }
 

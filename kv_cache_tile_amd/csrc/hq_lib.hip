@@ -192,9 +192,12 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   const uint32_t tpw = (256 / lpt) < (uint32_t)kChunkTiles ? 256 / lpt : (uint32_t)kChunkTiles;
   const int block = (int)(tpw * lpt);
   const uint32_t chunk_cap = (uint32_t)(((uint64_t)kChunkTiles * P.bound + 31) / 32);
-  // a unit's bits start anywhere in a word: one extra word, plus the readers' guard
-  const uint32_t stage_words = (uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 8;
-  const size_t lds = (size_t)(stage_words + 2 * kChunkTiles + tpw * lpt + 4 + 8) * 4;
+  // a unit's bits start anywhere in a word (one extra word), its first word
+  // is aligned down and its last rounded up to 16 bytes (3 + 3), plus the
+  // readers' guard (8); each of the two stages a multiple of 16 bytes
+  const uint32_t stage_words =
+      ((uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 3 + 3 + 8 + 3) & ~3u;
+  const size_t lds = (size_t)(2 * stage_words + 3 * 2 * kChunkTiles + 8 + tpw * lpt + 8) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
   if (rc) return rc;
