@@ -445,10 +445,12 @@ __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v))
 // lds + 16 i.  Written as the instruction: the compiler cannot tell a
 // kernel's stage buffers apart and would otherwise wait for it before every
 // later LDS access; the callers wait for it themselves (vmcnt, then a
-// barrier) before the buffer is read.  It writes no register.
+// barrier) before the buffer is read.  It writes no vector register; m0 is
+// restored after the issue.
 __device__ __forceinline__ void lds_load16(const uint32_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
 // LDS byte address of a shared-memory pointer
