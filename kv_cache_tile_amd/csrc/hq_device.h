@@ -458,6 +458,45 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// v of the lane at physical xor distance px (1, 2, or the half-row mirror
+// 7) within its 8-lane group, by DPP (no LDS round trip); other distances
+// through the crossbar.  px folds to a constant in the unrolled callers.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int px) {
+  if (px == 1) return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  if (px == 2) return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  if (px == 7) return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  return (uint32_t)__shfl_xor((int)v, px);
+}
+__device__ __forceinline__ float lane_xor(float v, int px) {
+  return __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, v), px));
+}
+
+// Inclusive prefix sum and total of v over the LPT consecutive physical
+// lanes of a tile (lanes p = 0..LPT-1 of an aligned group), all in DPP: row
+// shifts with the group's edge masked (the shift by 4 writes banks 1 and 3
+// only, the upper halves of 8-lane groups), and the total by a butterfly
+// (quad swaps, then the half-row mirror).
+template <int LPT>
+__device__ __forceinline__ void tile_scan(uint32_t v, int p, uint32_t& incl, uint32_t& total) {
+  uint32_t inc = v, s = v;
+  if constexpr (LPT >= 2) {
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, inc, 0x111, 0xF, 0xF, false);   // row_shr:1
+    inc = p >= 1 ? inc + t : inc;
+    s += __builtin_amdgcn_update_dpp(0u, s, 0xB1, 0xF, 0xF, false);                    // quad_perm [1,0,3,2]
+  }
+  if constexpr (LPT >= 4) {
+    const uint32_t t = __builtin_amdgcn_update_dpp(0u, inc, 0x112, 0xF, 0xF, false);   // row_shr:2
+    inc = p >= 2 ? inc + t : inc;
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x4E, 0xF, 0xF, false);                    // quad_perm [2,3,0,1]
+  }
+  if constexpr (LPT >= 8) {
+    inc += __builtin_amdgcn_update_dpp(0u, inc, 0x114, 0xF, 0xA, false);               // row_shr:4, p >= 4
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x141, 0xF, 0xF, false);                   // row_half_mirror
+  }
+  incl = inc;
+  total = s;
+}
+
 // Issue priority of the calling wave (the hardware's four levels, 0..3).
 // Among ready waves the arbiter picks the highest priority, then the oldest:
 // with equal priorities the workgroup dispatched first on a CU races ahead

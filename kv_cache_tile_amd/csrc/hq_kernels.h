@@ -400,7 +400,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     }
     float ss = sq[0];
 #pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) ss = ss + __shfl_xor(ss, partner_xor<LPT>(m));
+    for (int m = 1; m < LPT; m <<= 1) ss = ss + lane_xor(ss, partner_xor<LPT>(m));
     bool nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
     float s = 0.0f;
     uint32_t sbits = 0;
@@ -505,7 +505,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         L[jj] = acc;
         uint32_t tot = acc;
 #pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, partner_xor<LPT>(m));
+        for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
         Tt[jj] = tot;
       }
       const bool drop0 = Tt[0] - Tt[1] > (uint32_t)N, drop1 = Tt[1] - Tt[2] > (uint32_t)N;
@@ -542,7 +542,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
         }
         uint32_t tot = acc;
 #pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += __shfl_xor(tot, partner_xor<LPT>(m));
+        for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
         const uint32_t cost = tot + (uint32_t)N * (1u + kk);
         if (cost < bc) { bc = cost; bk = kk; bsum = acc; }
       }
@@ -558,7 +558,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     uint32_t lane_excl = 0, span = lane_unary;              // exclusive prefix in logical lane order
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) {
-      const uint32_t other = __shfl_xor(span, partner_xor<LPT>(m));
+      const uint32_t other = lane_xor(span, partner_xor<LPT>(m));
       if (q & m) lane_excl += other;
       span += other;
     }
@@ -958,17 +958,13 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
         if (valid < 32u) w &= (1u << valid) - 1u;
       }
       const uint32_t c = __builtin_popcount(w);
-      uint32_t inc = c;
-#pragma unroll
-      for (int s2 = 1; s2 < LPT; s2 <<= 1) {
-        uint32_t o = __shfl_up(inc, s2, LPT);
-        if (p_lane >= s2) inc += o;
-      }
+      uint32_t inc, tot;
+      tile_scan<LPT>(c, p_lane, inc, tot);
       const uint32_t before = carry + inc - c, after = carry + inc;
       const uint32_t mm = before / 32u + 1u;
       if (c != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
         ustart[tau * LPT + mm] = ub + 32u * j + select_bit(w, 32u * mm - before - 1u) + 1u;
-      carry += __shfl(inc, LPT - 1, LPT);
+      carry += tot;
     }
     ok = ok && carry == (uint32_t)N;
     __syncthreads();
@@ -1004,7 +1000,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
     int all_ok = lane_ok ? 1 : 0;
 #pragma unroll
-    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= __shfl_xor(all_ok, s2);
+    for (int s2 = 1; s2 < LPT; s2 <<= 1) all_ok &= (int)lane_xor((uint32_t)all_ok, partner_xor<LPT>(s2));
     lane_ok = all_ok != 0;
 
     // the next unit's stage loads, a unit old by now, are complete before
