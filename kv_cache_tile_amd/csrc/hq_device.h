@@ -453,6 +453,14 @@ __device__ __forceinline__ void lds_load16(const uint32_t* base, uint32_t voff, 
                : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
+// The same for one 16-bit value a lane, zero-extended to a 32-bit LDS word
+// (lane i's at lds + 4 i).
+__device__ __forceinline__ void lds_load_u16(const uint16_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
 // LDS byte address of a shared-memory pointer
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -469,6 +477,21 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int px) {
 }
 __device__ __forceinline__ float lane_xor(float v, int px) {
   return __builtin_bit_cast(float, lane_xor(__builtin_bit_cast(uint32_t, v), px));
+}
+
+// Inclusive prefix sum of v over a whole wave (all 64 lanes active), in DPP:
+// shifts by 1, 2, 4, 8 within each 16-lane row (lanes with no source add 0),
+// then row 0's last value into row 1 and row 2's into row 3 (row_bcast:15),
+// then row 1's last into rows 2 and 3 (row_bcast:31).
+static_assert(kChunkTiles == 64, "a chunk's tiles are scanned by one 64-lane wave");
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 
 // Inclusive prefix sum and total of v over the LPT consecutive physical

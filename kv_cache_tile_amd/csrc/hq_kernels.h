@@ -584,12 +584,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
     // group's last chunk, publish the group's size at once so later groups
     // can look back past it ----
     if (tid < kChunkTiles) {
-      uint32_t v = tile_len[tid], inc = v;
-#pragma unroll
-      for (int m = 1; m < kChunkTiles; m <<= 1) {
-        uint32_t o = __shfl_up(inc, m, kChunkTiles);
-        if (tid >= m) inc += o;
-      }
+      const uint32_t v = tile_len[tid], inc = wave_incl_scan(v);
       tile_off[tid] = inc - v;
       if (tid == kChunkTiles - 1) {
         misc[1] = inc;
@@ -775,7 +770,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
 // Occupancy target: 6 waves per SIMD (80 VGPRs) without dither, 5 with it
 // (a few spilled registers); latency hiding pays for more than the spills.
 template <int LAT, int N, bool DITHER>
-__global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 6)))
+__global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 7)))
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
               const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
               const uint32_t* __restrict__ chunk_off, uint64_t T, uint64_t C, float inv_sqrtn,
@@ -802,7 +797,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   uint32_t* tile_ok0 = tile_off0 + 2 * kChunkTiles;         // [2][64]
   uint32_t* tile_ms0 = tile_ok0 + 2 * kChunkTiles;          // [2][64] meta | step << 16
   uint32_t* misc0 = tile_ms0 + 2 * kChunkTiles;             // [2][4] see scan()
-  uint32_t* ustart = misc0 + 8;                             // [TPW * LPT] first unary bit per lane
+  uint32_t* pmeta0 = misc0 + 8;                             // [2][64] a chunk's meta, loaded ahead
+  uint32_t* pstep0 = pmeta0 + 2 * kChunkTiles;              // [2][64] and its steps
+  uint32_t* ustart = pstep0 + 2 * kChunkTiles;              // [TPW * LPT] first unary bit per lane
   uint32_t* smask = ustart + TPW * LPT;                     // [N / 32] sign diagonal bits
 
   const int tid = threadIdx.x;
@@ -814,19 +811,19 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   (void)sign_mask<N>(smask, key_sign, tid, q);
   const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
-  // tile metadata (wave 0) and chunk offsets (every wave: uniform values) of
-  // a unit's chunk, loaded one unit before its scan
-  uint32_t pm = 0, ps = 0;
+  // tile metadata of a unit's chunk, loaded one unit before its scan by
+  // wave 0 straight into LDS slot `slot` (no registers held; a tile past the
+  // end reads the last one, the scan masks it), and the chunk offsets
+  // (every wave: uniform values)
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   uint64_t pw0 = 0, pw1 = 0;
-  // (loads only, a tile past the end reading the last one: the scan masks
-  // it; no register is rewritten while the stage loads are in flight)
-  auto fetch = [&](uint64_t un) {
+  auto fetch = [&](uint64_t un, int slot) {
     const uint64_t ch = un / SUB;
     if (tid < 64) {
-      uint64_t tt = ch * kChunkTiles + (uint64_t)tid;
-      tt = tt < T ? tt : T - 1;
-      pm = (uint32_t)meta[tt];
-      ps = (uint32_t)step[tt];
+      const uint64_t t0 = ch * kChunkTiles;
+      const uint32_t i = t0 + (uint64_t)tid < T ? (uint32_t)tid : (uint32_t)(T - 1 - t0);
+      lds_load_u16(meta + t0, 2u * i, smem_lds + 4u * (uint32_t)(pmeta0 - smem + slot * kChunkTiles));
+      lds_load_u16(step + t0, 2u * i, smem_lds + 4u * (uint32_t)(pstep0 - smem + slot * kChunkTiles));
     }
     pw0 = chunk_off[ch];
     pw1 = chunk_off[ch + 1];
@@ -835,27 +832,23 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   // its tiles is dropped) and the unit's word range.  misc: [0] 32 (L - w0)
   // (mod 2^32), where stage word 0 is payload word L, the unit's first word
   // aligned down to 4; [1] 16-byte vectors to stage; [2], [3] L.
-  auto scan = [&](uint64_t un, int set) {
+  auto scan = [&](uint64_t un, int set, int slot) {
     const int first = (int)(un % SUB) * TPW;
     const bool range_ok = pw1 >= pw0 && pw1 <= payload_words && (pw1 - pw0) <= chunk_cap_words;
     const bool exists = (un / SUB) * kChunkTiles + (uint64_t)tid < T;
-    const uint32_t mt = exists ? pm : 0u, st_ = exists ? ps : 0u;
+    const uint32_t mt = exists ? pmeta0[slot * kChunkTiles + tid] : 0u;
+    const uint32_t st_ = exists ? pstep0[slot * kChunkTiles + tid] : 0u;
     const uint32_t len = mt >> 3, kk = mt & 7u;
-    uint32_t inc = len;
-#pragma unroll
-    for (int s2 = 1; s2 < kChunkTiles; s2 <<= 1) {
-      uint32_t o = __shfl_up(inc, s2, kChunkTiles);
-      if (tid >= s2) inc += o;
-    }
+    const uint32_t inc = wave_incl_scan(len);
     tile_off0[set * kChunkTiles + tid] = inc - len;
-    const uint32_t total = __shfl(inc, kChunkTiles - 1, kChunkTiles);
+    const uint32_t total = __builtin_amdgcn_readlane(inc, kChunkTiles - 1);
     const bool too_long = __any(len > tile_bound);          // longer than any valid tile can be
     const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == pw1 - pw0;
     tile_ok0[set * kChunkTiles + tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
     tile_ms0[set * kChunkTiles + tid] = mt | (st_ << 16);
     // this unit's bits [tile_off[first], tile_off[first + TPW - 1] + len)
-    const uint32_t f0 = __shfl(inc - len, first, kChunkTiles);
-    const uint32_t f1 = __shfl(inc, first + TPW - 1, kChunkTiles);
+    const uint32_t f0 = __builtin_amdgcn_readlane(inc - len, first);
+    const uint32_t f1 = __builtin_amdgcn_readlane(inc, first + TPW - 1);
     if (tid == 0) {
       uint64_t L = pw0;
       uint32_t nvec = 0;
@@ -873,7 +866,6 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   // all threads: start the unit's words streaming into its stage (16 bytes a
   // lane, straight to LDS; the stream's last, partial vector by plain loads)
   // and zero the guard words behind them
-  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   auto stage_in = [&](int set) {
     const uint32_t nvec = __builtin_amdgcn_readfirstlane(misc0[set * 4 + 1]);
     const uint64_t L = (uint64_t)__builtin_amdgcn_readfirstlane(misc0[set * 4 + 2]) |
@@ -902,10 +894,13 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   const uint64_t units = C * SUB;
   // priority by the units this workgroup has left (the current one included)
   uint64_t left = blockIdx.x < units ? (units - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
+  // unit k (k-th of this workgroup) uses buffer set k & 1; its metadata
+  // slot is k & 1 as well
   if (blockIdx.x < units) {
-    fetch(blockIdx.x);
-    if (tid < 64) scan(blockIdx.x, 0);
-    if (blockIdx.x + gridDim.x < units) fetch(blockIdx.x + gridDim.x);
+    fetch(blockIdx.x, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < 64) scan(blockIdx.x, 0, 0);
+    if (blockIdx.x + gridDim.x < units) fetch(blockIdx.x + gridDim.x, 1);
     __syncthreads();
     stage_in(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -919,8 +914,8 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     // before its previous stores, the barrier waits for everyone's); wave 0
     // scans the next unit
     if (un < units) {
-      if (tid < 64) scan(un, cur ^ 1);
-      if (un + gridDim.x < units) fetch(un + gridDim.x);    // (issued before the stage loads)
+      if (tid < 64) scan(un, cur ^ 1, cur ^ 1);
+      if (un + gridDim.x < units) fetch(un + gridDim.x, cur);   // (issued before the stage loads)
     }
     __syncthreads();
     if (un < units) stage_in(cur ^ 1);

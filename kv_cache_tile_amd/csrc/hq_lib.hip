@@ -197,7 +197,7 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   // readers' guard (8); each of the two stages a multiple of 16 bytes
   const uint32_t stage_words =
       ((uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 3 + 3 + 8 + 3) & ~3u;
-  const size_t lds = (size_t)(2 * stage_words + 3 * 2 * kChunkTiles + 8 + tpw * lpt + 8) * 4;
+  const size_t lds = (size_t)(2 * stage_words + 5 * 2 * kChunkTiles + 8 + tpw * lpt + 8) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
   if (rc) return rc;
