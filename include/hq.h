@@ -90,13 +90,14 @@ int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_
 
 /*
  * hq_encode — weights.  Methodology 1-3.
- *   x          device, [rows][cols] of dtype, row-major, read only
+ *   x          device, [rows][cols] of dtype, row-major, read only, 16-byte
+ *              aligned
  *   seed       selects the sign diagonal D
  *   payload    device, payload_cap_words uint32 (>= hq_plan's capacity)
  *   step, meta device, T uint16 each
  *   chunk_off  device, C+1 uint32
  *   status     device, one uint32 (flags OR-ed in)
- *   workspace  device, workspace_bytes (>= hq_plan's) zero-filled ONCE
+ *   workspace  device, 8-byte aligned, workspace_bytes (>= hq_plan's) zero-filled ONCE
  *              before its first use; the kernels leave it ready for the next
  *              call.  Calls that overlap in time must not share a workspace.
  * The bit stream is a pure function of (x, shape, tile, lattice, bps, seed).
@@ -110,8 +111,13 @@ int hq_encode(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
 /*
  * hq_decode — inverse of hq_encode: Rice parse, lattice point, step, inverse
  * RHT.  Same shape arguments and seed as the encode; writes x_out
- * ([rows][cols] of dtype, device).  payload_words = chunk_off[C] of the
- * stream (the number of valid words); reads never go beyond it.
+ * ([rows][cols] of dtype, device, 16-byte aligned).  payload (device) is
+ * 16-byte aligned; payload_words is at least chunk_off[C] of the stream (the
+ * valid words; the buffer's capacity may be passed); reads never go beyond it.
+ * Errors (HQ_EINVAL for a NULL or misaligned pointer, a bad shape or rate)
+ * are returned before any device work; a stream inconsistent with its
+ * metadata is not an error: its tiles decode to zero and HQ_FLAG_CORRUPT is
+ * OR-ed into *status.
  */
 int hq_decode(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
               const uint16_t *meta, const uint32_t *chunk_off,

@@ -186,7 +186,7 @@ int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* s
   int rc = make_plan(dtype, rows, cols, tile, lat, bps, kv, &P);
   if (rc) return rc;
   if (!payload || !step || !meta || !chunk_off || !status || !out) return HQ_EINVAL;
-  if ((uintptr_t)out & 15) return HQ_EINVAL;
+  if (((uintptr_t)out & 15) || ((uintptr_t)payload & 15)) return HQ_EINVAL;
   DecFn fn = dec_fn(lat, tile, kv != 0);
   const uint32_t lpt = tile / kLaneElems;
   const uint32_t tpw = (256 / lpt) < (uint32_t)kChunkTiles ? 256 / lpt : (uint32_t)kChunkTiles;

@@ -113,6 +113,34 @@ def test_chunk_groups(chunks, tile, grid_cap, monkeypatch):
     check_full(x, tile, "E8", 4.0, seed=chunks, kv=False, dtype="bf16")
 
 
+# The decoder streams a unit's words into LDS 16 bytes a lane; the stream's
+# last vector, when it runs past payload_words, is read word by word.  An
+# exact-size payload (a fresh copy of the valid words) reaches that path; tile
+# counts here give every residue of the word count mod 4.
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("T", [37, 64, 65, 100, 127, 129, 191, 250])
+def test_exact_size_payload(T, tile):
+    x = workloads.gaussian(T, tile, key=3000 + T)
+    xd, xo = to_device(x, "bf16")
+    print(f"[case] exact-size payload T={T} tile={tile}", flush=True)
+    h, g = gpu_encode(xd, tile, "E8", 4.0, T, False)
+    words = g["payload"].size
+    exact = torch.empty(words, dtype=torch.int32, device=_dev())
+    exact.copy_(h.payload[:words])
+    h2 = hq.HQTensor(exact, h.step, h.meta, h.chunk_off, torch.zeros_like(h.status), h.shape, h.dtype, h.tile,
+                     h.lattice, h.bps, h.seed, h.kv)
+    a, b = hq.decode(h), hq.decode(h2)
+    torch.cuda.synchronize()
+    assert h2.flags() == 0 and h.flags() == 0
+    np.testing.assert_array_equal(out_bits(a), out_bits(b))
+    c = rate_c("E8", tile, 4.0)
+    e = oracle.encode(xo, tile, "E8", c, T)
+    np.testing.assert_array_equal(g["payload"], e.payload)
+    ref, st = oracle.decode(e, T, tile, tile, "E8", c, T, oracle.BF16)
+    assert st == oracle.OK
+    np.testing.assert_array_equal(out_bits(b).reshape(-1), oracle_out_bits(ref).reshape(-1))
+
+
 @pytest.mark.parametrize("bps", [1.5, 3.0, 5.0, 8.0])
 @pytest.mark.parametrize("tile", [128, 256])
 def test_rate_extremes(bps, tile):
