@@ -15,6 +15,10 @@ namespace hq {
 
 constexpr int kChunkTiles = 64;   // tiles per chunk of the stream
 constexpr int kLaneElems = 32;    // tile elements held by one lane
+// 1/sqrt(n) is a power of two (n = 64, 256): scaling by it is exact wherever
+// the scaled value is representable
+template <int N>
+constexpr bool kPow2Scale = (N == 64 || N == 256);
 constexpr int kMaxGroupChunks = 4;   // most chunks an encode workgroup stages per ticket (one look-back each)
 
 // --------------------------------------------------------------------------
@@ -562,13 +566,18 @@ __device__ __forceinline__ constexpr int partner_xor(int m) { return (LPT == 8 &
         "+v"(a[(o) + 5]), "+v"(a[(o) + 6]), "+v"(a[(o) + 7])                                       \
       : "v"(f))
 
+// Lane sign of the presigned butterfly: (-1)^popcount(q) for logical lane q.
+__device__ __forceinline__ bool lane_sign_odd(int q) { return (__builtin_popcount((uint32_t)q) & 1) != 0; }
+
 // The butterfly with the cross-lane stages as one fused multiply-add per
-// element: the lane with the stage bit clear computes own + partner, the
-// other own - partner, which is the exact value a_j - a_{j+h} negated.  Each
-// upper role flips the sign a lane holds, so on return lane q holds
-// (-1)^popcount(q) times the oracle's values; the caller folds that sign
-// into the 1/sqrt(n) scale.  The sign of an exact zero may differ from the
-// oracle's, which no later encode step depends on.
+// element, for inputs presigned per lane: lane q must hold (-1)^popcount(q)
+// times its elements.  A cross-lane stage pairs lanes whose signs differ, so
+// the lane with the stage bit clear computes own - partner (the pair's sum)
+// and the other own + partner (the pair's difference, with the sign of its
+// partner); every lane's sign thus flips once per set bit of q, and on return
+// every lane holds the butterfly's exact values.  The sign of an exact zero is
+// +0 wherever no -0 was among the inputs (no sum or difference of such values
+// rounds to -0); with -0 inputs it may differ from the plain butterfly's.
 template <int LPT>
 __device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) {
 #pragma unroll
@@ -583,7 +592,7 @@ __device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) 
   }
 #pragma unroll
   for (int m = 1; m < LPT; m <<= 1) {
-    const float f = (q & m) ? -1.0f : 1.0f;
+    const float f = (q & m) ? 1.0f : -1.0f;
     if (m == 1) {                                            // partner lane ^ 1: quad_perm 1,0,3,2
 #pragma unroll
       for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("quad_perm:[1,0,3,2]", a, o, f);
@@ -595,6 +604,27 @@ __device__ __forceinline__ void fwht_tile_signed(float (&a)[kLaneElems], int q) 
       for (int o = 0; o < kLaneElems; o += 8) HQ_FMAC_DPP8("row_half_mirror", a, o, f);
     }
   }
+}
+
+// Signs of the butterfly's outputs when every input is a signed zero (bit i
+// of z: element 32 q + i is -0): under IEEE rounding to nearest, lo + hi is
+// -0 only for -0 + -0, and lo - hi only for -0 - (+0).  Same stage order and
+// lane pairing as the butterfly.
+template <int LPT>
+__device__ __forceinline__ uint32_t zero_sign_butterfly(uint32_t z, int q) {
+  constexpr uint32_t lo_mask[5] = {0x55555555u, 0x33333333u, 0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
+#pragma unroll
+  for (int st = 0; st < 5; st++) {
+    const int h = 1 << st;
+    const uint32_t lo = z & lo_mask[st], hi = (z >> h) & lo_mask[st];
+    z = (lo & hi) | ((lo & ~hi) << h);
+  }
+#pragma unroll
+  for (int m = 1; m < LPT; m <<= 1) {
+    const uint32_t p = lane_xor(z, partner_xor<LPT>(m));
+    z = (q & m) ? (p & ~z) : (z & p);
+  }
+  return z;
 }
 
 // read 32 bits starting at bit `pos` of an LDS word array (needs one guard word)

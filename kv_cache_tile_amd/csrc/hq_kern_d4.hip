@@ -4,6 +4,6 @@
 #include "hq_kernels.h"
 
 namespace hq {
-EncFn enc_fn_d4(uint32_t n, bool dither) { return enc_table<4>(n, dither); }
+EncFn enc_fn_d4(uint32_t n, bool dither, bool bf16) { return enc_table<4>(n, dither, bf16); }
 DecFn dec_fn_d4(uint32_t n, bool dither) { return dec_table<4>(n, dither); }
 }  // namespace hq

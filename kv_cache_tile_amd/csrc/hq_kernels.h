@@ -172,9 +172,9 @@ __device__ __forceinline__ uint32_t sign_mask(uint32_t* smask, uint32_t key_sign
 // --------------------------------------------------------------------------
 // Encode kernel
 // --------------------------------------------------------------------------
-template <int LAT, int N, bool DITHER>
+template <int LAT, int N, bool DITHER, bool BF16>
 __global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems)) __attribute__((amdgpu_waves_per_eu(4)))
-encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
+encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
               uint32_t key_sign, uint32_t key_dither, A2Consts a2,
               uint32_t* __restrict__ payload, uint64_t cap_words,
               uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
@@ -185,6 +185,7 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
   constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;   // coset bits per lane
   constexpr uint32_t B = CB_LANE * LPT;                     // coset bits per tile
+  constexpr bool bf16 = BF16;                               // input dtype (else fp32)
 
   extern __shared__ uint32_t smem[];
   uint32_t* stage = smem;                                   // [stage_words]: two group areas
@@ -200,12 +201,11 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
   const int q = tile_lane<LPT>(p_lane);                     // logical lane
   uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);     // one word per group
 
-  // sign diagonal entries of this lane's 32 positions (Methodology 1)
-  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q);
+  // sign diagonal entries of this lane's 32 positions (Methodology 1), with
+  // the butterfly's lane sign folded in (inputs presigned per lane)
+  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q) ^ (lane_sign_odd(q) ? 0xFFFFFFFFu : 0u);
   uint32_t sgnw[2];
   pair_sign_words(sgn, sgnw);
-
-  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
 
   // Tickets number groups of group_chunks consecutive chunks.  Workgroup b's
@@ -384,37 +384,78 @@ encode_kernel(const void* __restrict__ x, uint32_t bf16, uint64_t T, uint64_t C,
       for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ ((sg << (31 - i)) & 0x80000000u));
     }
 
-    // ---- RHT: butterfly, then 1/sqrt(n) (with the lane's butterfly sign) ----
+    // ---- RHT: the butterfly (exact values in every lane), then y = z fl(1/sqrt(n)).
+    // When 1/sqrt(n) is a power of two and the input is bf16 the scale is
+    // exact: every butterfly value z is a multiple of 2^-133 (the finest bf16
+    // unit; sums round to coarser multiples), so z / sqrt(n) is representable
+    // even below the normal range.  Then the lane keeps z and the scale is
+    // folded into the quantiser's factor (ydom false). ----
     fwht_tile_signed<LPT>(a, q);
+    constexpr bool ydom = !kPow2Scale<N> || !bf16;
+    if (ydom) {
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * lane_scale;
+      for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
+    }
 
-    // ---- tile energy: pairwise tree over the tile, step = bf16(rms * c) ----
-    float sq[kLaneElems];
+    // ---- tile energy and step = bf16(sqrt(ss / n) * c), ss the pinned
+    // pairwise sum of y^2.  An estimate from fused multiply-add chains decides
+    // the step unless it lies within 64 units in the last place of a bf16
+    // rounding tie: the pinned sum and the estimate are each within 9 and 13
+    // roundings of the exact sum of squares, so their two values of
+    // sqrt(ss / n) * c differ by less than 16 units in the last place.  A wave
+    // with such a tile, or with an estimate outside [2^-90, 2^100] (where
+    // subnormal terms, overflow, a flushed or an infinite step could enter),
+    // computes the pinned sum (steps below 2^-124 are stored as 0). ----
+    float e4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) sq[i] = a[i] * a[i];
+    for (int i = 0; i < kLaneElems; i++) e4[i & 3] = __builtin_fmaf(a[i], a[i], e4[i & 3]);
+    float est = (e4[0] + e4[1]) + (e4[2] + e4[3]);
 #pragma unroll
-    for (int m = kLaneElems; m > 1; m >>= 1) {
+    for (int m = 1; m < LPT; m <<= 1) est = est + lane_xor(est, partner_xor<LPT>(m));
+    if (!ydom) est = est * inv_n;                            // sum of z^2 / n (exact power-of-two scale)
+    const float r_est = sqrtf(est * inv_n) * c;
+    const bool near_tie = ((as_u(r_est) & 0xFFFFu) - 0x7FC0u) <= 0x80u;
+    const bool in_range = est >= 0x1p-90f && est <= 0x1p100f && r_est >= 0x1p-100f && r_est <= 0x1p100f;
+    bool nonfinite = false;
+    uint32_t sbits;
+    if (__any(near_tie || !in_range)) {
+      asm volatile("");                                     // (rare: stays a branch)
+      // the pinned tree as a running stack of partial sums: part[l] holds
+      // the sum of the last complete block of 2^l squares
+      float part[6];
 #pragma unroll
-      for (int i = 0; i < m / 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+      for (int i = 0; i < kLaneElems; i++) {
+        const float y = ydom ? a[i] : a[i] * inv_sqrtn;
+        float v = y * y;
+        int l = 0;
+#pragma unroll
+        for (; (i >> l) & 1; l++) v = part[l] + v;
+        part[l] = v;
+      }
+      float ss = part[5];
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) ss = ss + lane_xor(ss, partner_xor<LPT>(m));
+      nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
+      sbits = 0;
+      if (!nonfinite) {
+        const float rms = sqrtf(ss * inv_n);
+        const float r = rms * c;
+        sbits = bf16_rne_bits(r);
+        if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
+        else if ((sbits & 0x7F80u) < 0x0180u) sbits = 0;    // below 2^-124: stored as 0
+      }
+    } else {
+      sbits = bf16_rne_bits(r_est);
     }
-    float ss = sq[0];
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) ss = ss + lane_xor(ss, partner_xor<LPT>(m));
-    bool nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
-    float s = 0.0f;
-    uint32_t sbits = 0;
-    if (!nonfinite) {
-      float rms = sqrtf(ss * inv_n);
-      float r = rms * c;
-      sbits = bf16_rne_bits(r);
-      if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
-      else if ((sbits & 0x7F80u) == 0) sbits = 0;
-      s = as_f(sbits << 16);
-    }
+    const float s = as_f(sbits << 16);
     const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    // t = y / s; with z kept, z * (inv / sqrt(n)) is the same product: both
+    // scalings are exact (a finite tile energy bounds the step by
+    // sqrt(FLT_MAX / n) * c < 2^61 c, far below 2^122 for the table's rate
+    // constants, so inv / sqrt(n) is a normal number)
+    const float qf = ydom ? inv : inv * inv_sqrtn;
 #pragma unroll
-    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv;
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * qf;
     if (__any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
       asm volatile("");                                     // (stays a branch, not 32 selects)
       if (nonfinite) {
@@ -679,7 +720,9 @@ struct DecodeGeom {
 };
 
 // Rice parse and lattice rebuild of one lane's 32 codes for Rice parameter
-// K: a[e] = (lattice point - dither) * s.  Remainders come from the lane's
+// K: a[e] = (lattice point - dither) * s, every zero +0 (a product with +0
+// added, one fused multiply-add; no nonzero product rounds to zero for the
+// steps the caller passes).  Remainders come from the lane's
 // K-bit fields (static offsets), quotients from the unary window, 8 codes per
 // group; a group whose fast read saw a run of 31+ zeros (or ran out of window)
 // is read again exactly.  Returns false if the codes are not a valid stream
@@ -703,9 +746,8 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
   UnaryWindow uw;
   uw.init(stage, u0);
   bool ok = true;
-  // E8 without dither: (d + p/2) * s as one fma, exact for every finite s;
-  // for s = +-0 the addend -0 keeps the sign of d * s
-  const float zero_add = (s == 0.0f) ? -0.0f : 0.0f;
+  // E8 without dither: (d + p/2) * s as one fma, exact (13 and 8 significant
+  // bits) for normal products
   const float half_s = 0.5f * s;
 #pragma unroll
   for (int g = 0; g < kLaneElems / 8; g++) {
@@ -742,7 +784,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
       }
       const uint32_t p = (cbits >> b) & 1u;
       if constexpr (LAT == 8 && !DITHER) {
-        const float add = p ? half_s : zero_add;
+        const float add = p ? half_s : 0.0f;
 #pragma unroll
         for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf((float)d[i], s, add);
       } else {
@@ -755,7 +797,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
           for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
         }
 #pragma unroll
-        for (int i = 0; i < D; i++) a[b * D + i] = pt[i] * s;
+        for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf(pt[i], s, 0.0f);
       }
     }
     // the group's values are final here: keeps the compiler from holding all
@@ -767,8 +809,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
   return ok;
 }
 
-// Occupancy target: 6 waves per SIMD (80 VGPRs) without dither, 5 with it
-// (a few spilled registers); latency hiding pays for more than the spills.
+// Occupancy target: 7 waves per SIMD (72 VGPRs) without dither, 5 with it.
 template <int LAT, int N, bool DITHER>
 __global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 7)))
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
@@ -809,7 +850,6 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 
   // the lane's sign diagonal bits stay in LDS (smask[q]), read where needed
   (void)sign_mask<N>(smask, key_sign, tid, q);
-  const float lane_scale = (__builtin_popcount((uint32_t)q) & 1) ? -inv_sqrtn : inv_sqrtn;
 
   // tile metadata of a unit's chunk, loaded one unit before its scan by
   // wave 0 straight into LDS slot `slot` (no registers held; a tile past the
@@ -930,8 +970,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     const uint32_t m = active ? (ms & 0xFFFFu) : 0u;
     const uint32_t len = m >> 3, k = m & 7u;
     const uint32_t sraw = active ? (ms >> 16) : 0u;
-    // a non-finite step is never written by the encoder: corrupt tile
-    bool ok = active && tile_ok0[cur * kChunkTiles + ct] != 0u && (sraw & 0x7F80u) != 0x7F80u;
+    // the encoder writes +0 or a finite step of at least 2^-124, nothing
+    // else: any other step marks a corrupt tile
+    bool ok = active && tile_ok0[cur * kChunkTiles + ct] != 0u && (sraw == 0u || sraw - 0x180u < 0x7E00u);
     const uint32_t start = tile_off0[cur * kChunkTiles + ct] - misc0[cur * 4 + 0], end = start + len;
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
@@ -966,13 +1007,31 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 
     // ---- parse and rebuild, specialised on the tile's Rice parameter; a lane
     // of an invalid tile reads from bit 0 with no run limit (in bounds, result
-    // discarded) ----
+    // discarded).  The values reach the oracle's in one of two ways:
+    //  - a step of at least 2^-124 (every other nonzero one is corrupt): the
+    //    rebuild takes the step times the butterfly's lane sign (and, for E8,
+    //    D4 and Z without dither, times 1/sqrt(n) where that is a power of
+    //    two), every zero is +0, and the presigned butterfly ends with the
+    //    exact values (the rest of the scale follows it).  E8, D4 and Z points
+    //    are multiples of 1/2 with at most 14 significant bits, so every
+    //    product and butterfly value is a multiple of 2^-134 (2^-138 scaled),
+    //    representable wherever it falls.  A2's sqrt3 coordinate and dithered
+    //    ones are rounded, so their products are not scaled; a product rounded
+    //    once is the same product negated, and it is not zero (a dithered
+    //    coordinate is at least 2^-25 from zero, 2^-25 * 2^-124 is the least
+    //    subnormal).  No value is ever -0.
+    //  - a +0 step: every value is a signed zero.  The rebuild takes the step
+    //    1 to see each value's sign, and the signs go through the butterfly's
+    //    rules for zeros (at the store). ----
+    constexpr bool kFoldScale = kPow2Scale<N> && LAT != 2 && !DITHER;
     float a[kLaneElems];
     bool lane_ok;
+    const bool zero_step = sraw == 0u;
     {
       const float s = as_f(sraw << 16);
       uint32_t cbits = 0;
       if constexpr (CB_LANE > 0) cbits = lds_read32(stage, ok ? start + (uint32_t)q * CB_LANE : 0u);
+      const float s_lane = zero_step ? 1.0f : (lane_sign_odd(q) ? -s : s) * (kFoldScale ? inv_sqrtn : 1.0f);
       const uint32_t rb = ok ? start + B + (uint32_t)q * kLaneElems * k : 0u;
       uint32_t lt = (uint32_t)tid;
       opaque(lt);                                           // (an address recomputed, not spilled)
@@ -983,15 +1042,16 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       bool pok;
       switch (k) {
 #define HQ_PARSE_CASE(KK) \
-        case KK: pok = parse_lane<LAT, DITHER, KK>(stage, rb, u0, lim, cbits, s, key_dither, g_lane, a2, a, upos); break;
+        case KK: pok = parse_lane<LAT, DITHER, KK>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
         HQ_PARSE_CASE(0) HQ_PARSE_CASE(1) HQ_PARSE_CASE(2) HQ_PARSE_CASE(3)
         HQ_PARSE_CASE(4) HQ_PARSE_CASE(5) HQ_PARSE_CASE(6)
-        default: pok = parse_lane<LAT, DITHER, 7>(stage, rb, u0, lim, cbits, s, key_dither, g_lane, a2, a, upos); break;
+        default: pok = parse_lane<LAT, DITHER, 7>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
 #undef HQ_PARSE_CASE
       }
       lane_ok = ok && pok;
       if (q == LPT - 1 && upos != end) lane_ok = false;      // the last one ends the tile
     }
+
     // tile-wide AND; every lane takes part in the shuffles (no short-circuit)
     int all_ok = lane_ok ? 1 : 0;
 #pragma unroll
@@ -1010,27 +1070,29 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 #pragma unroll
         for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
       }
-      fwht_tile_signed<LPT>(a, q);
-      // lane q holds (-1)^popcount(q) times the butterfly output: fold that
-      // sign into the scale; + 0.0f turns a -0 into +0 (every zero of the
-      // exact butterfly is +0), then apply the sign diagonal (on the packed
-      // bf16 pairs: rounding to nearest even commutes with a sign flip).
-      // fma(a, scale, +0) is that value in one operation, except where a
-      // nonzero product rounds to zero (then it keeps the product's sign): a
-      // second + 0.0f settles those, and is needed only for tiny steps.  The
-      // butterfly's inputs are at least 2^-26 |s| when nonzero (lattice
-      // coordinates are multiples of 1/2, dithered ones at least 2^-25 from
-      // zero), its sums stay multiples of the finest input's unit, so every
-      // nonzero output is at least 2^-50 |s|: no product underflows for
-      // |s| >= 2^-90.
+      // a +0 step: the outputs' signs (bit i for element i) from the rebuilt
+      // values' signs; the values themselves become +0
+      uint32_t zsign = 0;
+      if (__any(zero_step && lane_ok)) {
+        asm volatile("");                                   // (rare: kept out of line)
+        uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = __builtin_fmaf(a[i], lane_scale, 0.0f);
-      if (__any(!(__builtin_fabsf(as_f(sraw << 16)) >= 0x1p-90f))) {
-        asm volatile("");                                   // (a branch, not selects)
+        for (int i = 0; i < kLaneElems; i++) m |= (as_u(a[i]) >> 31) << i;
+        zsign = zero_sign_butterfly<LPT>(zero_step && lane_ok ? m : 0u, q);
+        if (zero_step) {
 #pragma unroll
-        for (int i = 0; i < kLaneElems; i++) a[i] = a[i] + 0.0f;
+          for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+        }
       }
-      const uint32_t sg = smask[q];
+      // then y = z fl(1/sqrt(n)) (already in the presigned values where it
+      // was folded there), and the sign diagonal (on the packed bf16 pairs:
+      // rounding to nearest even commutes with a sign flip)
+      fwht_tile_signed<LPT>(a, q);
+      if constexpr (!kFoldScale) {
+#pragma unroll
+        for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
+      }
+      const uint32_t sg = smask[q] ^ zsign;
       uint32_t sw[2];
       pair_sign_words(sg, sw);
       const uint64_t base = t * N + (uint64_t)q * kLaneElems;
@@ -1063,11 +1125,16 @@ using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_
                        uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t, uint32_t*, uint32_t,
                        uint32_t, uint32_t);
 
+template <int LAT, int N>
+EncFn enc_table_n(bool dither, bool bf16) {
+  if (dither) return bf16 ? encode_kernel<LAT, N, true, true> : encode_kernel<LAT, N, true, false>;
+  return bf16 ? encode_kernel<LAT, N, false, true> : encode_kernel<LAT, N, false, false>;
+}
 template <int LAT>
-EncFn enc_table(uint32_t n, bool dither) {
-  if (n == 64) return dither ? encode_kernel<LAT, 64, true> : encode_kernel<LAT, 64, false>;
-  if (n == 128) return dither ? encode_kernel<LAT, 128, true> : encode_kernel<LAT, 128, false>;
-  return dither ? encode_kernel<LAT, 256, true> : encode_kernel<LAT, 256, false>;
+EncFn enc_table(uint32_t n, bool dither, bool bf16) {
+  if (n == 64) return enc_table_n<LAT, 64>(dither, bf16);
+  if (n == 128) return enc_table_n<LAT, 128>(dither, bf16);
+  return enc_table_n<LAT, 256>(dither, bf16);
 }
 template <int LAT>
 DecFn dec_table(uint32_t n, bool dither) {
@@ -1076,10 +1143,10 @@ DecFn dec_table(uint32_t n, bool dither) {
   return dither ? decode_kernel<LAT, 256, true> : decode_kernel<LAT, 256, false>;
 }
 
-EncFn enc_fn_z(uint32_t n, bool dither);
-EncFn enc_fn_a2(uint32_t n, bool dither);
-EncFn enc_fn_d4(uint32_t n, bool dither);
-EncFn enc_fn_e8(uint32_t n, bool dither);
+EncFn enc_fn_z(uint32_t n, bool dither, bool bf16);
+EncFn enc_fn_a2(uint32_t n, bool dither, bool bf16);
+EncFn enc_fn_d4(uint32_t n, bool dither, bool bf16);
+EncFn enc_fn_e8(uint32_t n, bool dither, bool bf16);
 DecFn dec_fn_z(uint32_t n, bool dither);
 DecFn dec_fn_a2(uint32_t n, bool dither);
 DecFn dec_fn_d4(uint32_t n, bool dither);

@@ -99,12 +99,12 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
   return HQ_OK;
 }
 
-EncFn enc_fn(uint32_t lat, uint32_t n, bool dither) {
+EncFn enc_fn(uint32_t lat, uint32_t n, bool dither, bool bf16) {
   switch (lat) {
-    case HQ_Z: return enc_fn_z(n, dither);
-    case HQ_A2: return enc_fn_a2(n, dither);
-    case HQ_D4: return enc_fn_d4(n, dither);
-    default: return enc_fn_e8(n, dither);
+    case HQ_Z: return enc_fn_z(n, dither, bf16);
+    case HQ_A2: return enc_fn_a2(n, dither, bf16);
+    case HQ_D4: return enc_fn_d4(n, dither, bf16);
+    default: return enc_fn_e8(n, dither, bf16);
   }
 }
 DecFn dec_fn(uint32_t lat, uint32_t n, bool dither) {
@@ -138,7 +138,7 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   if (!x || !payload || !step || !meta || !chunk_off || !status || !ws) return HQ_EINVAL;
   if (cap < P.cap_words || ws_bytes < P.ws_bytes) return HQ_ENOSPC;
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
-  EncFn fn = enc_fn(lat, tile, kv != 0);
+  EncFn fn = enc_fn(lat, tile, kv != 0, dtype == HQ_BF16);
   const int block = kChunkTiles * (int)(tile / kLaneElems);
   // chunks staged per ticket: as many (up to kMaxGroupChunks) as fit the LDS
   // share of a workgroup at the occupancy its registers allow; the staging

@@ -139,8 +139,11 @@ void hqo_rht_inverse(const float *y, uint32_t n, uint64_t seed, float *x)
 /* ------------------------------------------------------------------------ */
 /* [M2] per-tile scale alpha.  Reading: step = bf16_rne(RMS(y) * c), where   */
 /* c is the rate constant for the target bps; the sum of squares is the     */
-/* pairwise tree ((y0^2 + y1^2) + (y2^2 + y3^2)) + ...  A step that rounds   */
-/* to zero or to a bf16 subnormal is stored as 0 (the tile decodes to 0).   */
+/* pairwise tree ((y0^2 + y1^2) + (y2^2 + y3^2)) + ...  A step below 2^-124 */
+/* (zero, a bf16 subnormal, or one of the two lowest normal binades) is     */
+/* stored as 0 and the tile decodes to zeros: a dithered coordinate can be  */
+/* as small as 2^-25, and below 2^-124 its product with the step could      */
+/* round to zero when decoded.                                              */
 /* ------------------------------------------------------------------------ */
 float hqo_tile_step(const float *y, uint32_t n, float c, int *nonfinite)
 {
@@ -156,7 +159,7 @@ float hqo_tile_step(const float *y, uint32_t n, float c, int *nonfinite)
     float r = rms * c;
     uint16_t sb = bf16_rne(r);
     if ((sb & 0x7F80u) == 0x7F80u) { *nonfinite = 1; return 0.0f; }
-    if ((sb & 0x7F80u) == 0) return 0.0f;                 /* zero or subnormal */
+    if ((sb & 0x7F80u) < 0x0180u) return 0.0f;           /* below 2^-124 */
     return bf16_to_f32(sb);
 }
 
@@ -574,12 +577,16 @@ int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t
 /* tiles' lengths, exceeds the capacity bound or holds a tile longer than   */
 /* the per-tile bound, decode to zero (+0 with                              */
 /* the sign diagonal applied, no dither) and are reported.  So does a tile  */
-/* whose step is not a finite bf16 (the encoder stores the bf16 of a finite */
-/* RMS times c, or 0).  Valid streams never meet these conditions.          */
+/* whose step is neither +0 nor a finite bf16 of at least 2^-124: the      */
+/* encoder stores the bf16 of a non-negative RMS times c > 0, with results  */
+/* below 2^-124 flushed to +0, so a negative (or -0), smaller or non-finite */
+/* step cannot come from encoding.  Valid streams never meet these          */
+/* conditions.                                                              */
 /* ------------------------------------------------------------------------ */
 
+static int step_bad(uint16_t step) { return step != 0 && (step < 0x0180u || step > 0x7F7Fu); }
+
 /* parse one tile starting at bit b (reads never reach bend); 0 = ok */
-static int step_bad(uint16_t step) { return (step & 0x7F80u) == 0x7F80u; }
 
 static int parse_tile(const uint32_t *w, uint64_t b, uint64_t bend, uint32_t len, uint32_t k,
                       uint32_t n, uint32_t nb, uint32_t *cos, uint32_t *sym)

@@ -163,6 +163,64 @@ def test_special_values():
     assert h.flags() == hq.FLAG_NONFINITE
 
 
+@pytest.mark.parametrize("lat,n,kv", [("E8", 128, False), ("E8", 256, False), ("E8", 128, True), ("E8", 64, True),
+                                      ("A2", 256, False), ("Z", 64, False), ("D4", 256, True), ("A2", 128, True)])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_decoder_step_rules(lat, n, kv, odt):
+    # Steps the encoder never writes (negative, -0, subnormal, below 2^-124)
+    # mark their tile corrupt; a +0 step over nonzero codes decodes to the
+    # butterfly's signed zeros; the smallest valid steps decode exactly.  Bit
+    # for bit against the oracle on the same stream.
+    _dev()
+    T, seed, bps = 150, 6, (2.0 if kv else 4.0)
+    print(f"[case] step rules {lat} n={n} kv={kv} out={odt}", flush=True)
+    x = workloads.gaussian(T, n, key=31)
+    c = rate_c(lat, n, bps, int(kv))
+    e = oracle.encode(x, n, lat, c, seed, dither=int(kv))
+    step = e.step.copy()
+    for t, v in {3: 0x0000, 10: 0x0180, 11: 0x01A5, 20: 0x017F, 30: 0x8000, 40: 0xC000, 50: 0x0001,
+                 64: 0x0000, 70: 0x0200, 149: 0x0000}.items():
+        step[t] = v
+    ee = oracle.Encoded(step, e.meta, e.chunk_off, e.payload, 0)
+    ref, st = oracle.decode(ee, T, n, n, lat, c, seed, oracle.F32 if odt == "f32" else oracle.BF16,
+                            dither=int(kv))
+    assert st == oracle.ECORRUPT
+    pay = e.payload.astype(np.uint32)
+    h = hq.HQTensor(torch.from_numpy(pay.view(np.int32)).to(_dev()),
+                    torch.from_numpy(step.view(np.int16)).to(_dev()),
+                    torch.from_numpy(e.meta.view(np.int16)).to(_dev()),
+                    torch.from_numpy(e.chunk_off.view(np.int32)).to(_dev()),
+                    torch.zeros(1, dtype=torch.int32, device=_dev()), (T, n),
+                    torch.float32 if odt == "f32" else torch.bfloat16, n, lat, bps, seed, kv)
+    out = hq.decode(h)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_bits(out).reshape(-1), oracle_out_bits(ref).reshape(-1))
+    assert h.flags() == hq.FLAG_CORRUPT
+
+
+@pytest.mark.parametrize("lat,n", [("E8", 128), ("E8", 64), ("A2", 128)])
+def test_kv_zero_vectors(lat, n):
+    # all-zero KV vectors (padding): their step is +0 and the dithered codes
+    # decode to signed zeros; full encode + decode parity
+    x = workloads.gaussian(64 * 3 + 5, n, key=41)
+    x[::7] = 0.0
+    x[64:70] = 0.0
+    check_full(x, n, lat, 2.0, seed=13, kv=True, dtype="bf16")
+
+
+@pytest.mark.parametrize("tile,kv", [(256, False), (128, False), (64, False), (128, True)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiny_and_huge_tiles(tile, kv, dtype):
+    # tiles whose energy estimate is out of its range (tiny or huge rows,
+    # bf16 subnormals) take the pinned sum; steps near the bottom of the
+    # valid range decode through the folded scale
+    x = workloads.gaussian(64 * 2 + 9, tile, key=43)
+    for r, sc in enumerate((2.0 ** -40, 2.0 ** -60, 2.0 ** -64, 2.0 ** -75, 2.0 ** -100, 2.0 ** -128,
+                            2.0 ** 60, 2.0 ** 100, 2.0 ** 120)):
+        x[3 * r] *= np.float32(sc)
+    check_full(x, tile, "E8", 2.0 if kv else 4.0, seed=17, kv=kv, dtype=dtype)
+
+
 def test_repeatable_and_workspace_reuse():
     # the ticket counter and look-back tags reset themselves between calls of
     # different sizes sharing one workspace

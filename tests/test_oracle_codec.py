@@ -209,16 +209,17 @@ def test_corrupt_streams_are_rejected_not_crashing():
 
 
 def test_nonfinite_step_decodes_as_corrupt_tile():
-    # the encoder stores bf16(RMS * c) or 0, never an infinity or a NaN: a tile
-    # that carries one is corrupt and decodes to zeros (the sign diagonal's
-    # signed zeros), the other tiles are untouched
+    # the encoder stores bf16(RMS * c) of at least 2^-124, or +0, never an
+    # infinity, a NaN, a negative (or -0) or a smaller step: a tile that
+    # carries one is corrupt and decodes to zeros (the sign diagonal's signed
+    # zeros), the other tiles are untouched
     x = workloads.gaussian(64, 128, key=4)
     c = rate_c("E8", 128, 4.0)
     e = oracle.encode(x, 128, "E8", c, 9)
     clean, st = oracle.decode(e, 64, 128, 128, "E8", c, 9, oracle.F32)
     assert st == oracle.OK
     sign = oracle.sign_bits(9, 128).astype(np.uint32) << np.uint32(31)
-    for bad in (0x7F80, 0xFF80, 0x7FC0, 0x7F81):
+    for bad in (0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0x8000, 0xBF80, 0x8080, 0x0001, 0x007F, 0x0080, 0x017F):
         step = e.step.copy()
         step[5] = bad
         out, st = oracle.decode(oracle.Encoded(step, e.meta, e.chunk_off, e.payload, 0), 64, 128, 128, "E8",
@@ -229,6 +230,47 @@ def test_nonfinite_step_decodes_as_corrupt_tile():
         keep = np.ones(64, bool)
         keep[5] = False
         np.testing.assert_array_equal(ob[keep], clean.view(np.uint32).reshape(-1, 128)[keep])
+
+
+def test_edge_steps_decode():
+    # the smallest and largest valid steps (2^-124 and the largest finite
+    # bf16): no corruption is reported (the largest overflows the butterfly;
+    # the smallest gives finite values)
+    x = workloads.gaussian(8, 128, key=6)
+    c = rate_c("E8", 128, 4.0)
+    e = oracle.encode(x, 128, "E8", c, 2)
+    for st_bits in (0x0180, 0x7F7F):
+        step = e.step.copy()
+        step[3] = st_bits
+        out, st = oracle.decode(oracle.Encoded(step, e.meta, e.chunk_off, e.payload, 0), 8, 128, 128, "E8",
+                                c, 2, oracle.F32)
+        assert st == oracle.OK
+        if st_bits == 0x0180:
+            assert np.all(np.isfinite(out)) and np.abs(out[3]).max() < 1e-30
+
+
+def test_zero_step_over_negative_points_keeps_ieee_zero_signs():
+    # A tile whose lattice points are all negative, decoded with a +0 step:
+    # every rebuilt value is -0.  IEEE addition gives -0 only for -0 + -0 and
+    # -0 - (+0), so the butterfly of an all -0 vector keeps -0 in element 0
+    # alone (each stage's differences become +0); the output is that, times
+    # 1/sqrt(n), through the sign diagonal.
+    n = 128
+    y = np.full((1, n), -2.2, np.float32)
+    x = oracle.rht_inverse(y[0], 11)[None, :].astype(np.float32)
+    c = rate_c("E8", n, 4.0)
+    e = oracle.encode(x, n, "E8", c, 11)
+    ref, st = oracle.decode(e, 1, n, n, "E8", c, 11, oracle.F32)
+    assert st == oracle.OK and np.all(oracle.rht_forward(ref[0], 11) < 0)   # every point negative
+    step = e.step.copy()
+    step[0] = 0
+    out, st = oracle.decode(oracle.Encoded(step, e.meta, e.chunk_off, e.payload, 0), 1, n, n, "E8",
+                            c, 11, oracle.F32)
+    assert st == oracle.OK
+    z = np.zeros(n, np.uint32)
+    z[0] = 1
+    sign = oracle.sign_bits(11, n).astype(np.uint32)
+    np.testing.assert_array_equal(out.view(np.uint32).reshape(-1), (z ^ sign) << np.uint32(31))
 
 
 def test_payload_bound_holds_on_adversarial_tiles():

@@ -130,3 +130,12 @@ def test_tile_step_special_values():
     y = np.full(n, 1e-40, np.float32)                      # bf16-subnormal step -> 0
     s, nf = oracle.tile_step(y, 0.3)
     assert s == 0 and not nf
+    # steps below 2^-124 are flushed to 0, 2^-124 itself is kept.  With y
+    # constant 2^-60 the sum of squares, its mean and root are exact powers of
+    # two (RMS = 2^-60), so RMS * c is exactly the target for these c.
+    y = np.full(n, 2.0 ** -60, np.float32)
+    for c, target, kept in ((2.0 ** -65, 2.0 ** -125, False), (1.5 * 2.0 ** -65, 1.5 * 2.0 ** -125, False),
+                            (2.0 ** -64, 2.0 ** -124, True), (1.5 * 2.0 ** -64, 1.5 * 2.0 ** -124, True)):
+        s, nf = oracle.tile_step(y, c)
+        assert not nf
+        assert (s == np.float32(target)) if kept else (s == 0)
