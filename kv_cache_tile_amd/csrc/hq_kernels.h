@@ -39,6 +39,27 @@ constexpr uint32_t kFlagAgg = 1u, kFlagIncl = 2u;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 constexpr int kLookJ = 4;                                   // look-back predecessors per lane per round
 
+// One step of a group's unary codes, built last symbol first:
+// G = ((G << 1) | 1) << (byte n of q) when `one`, else G << (byte n of q).
+// The shift takes the byte straight from q (SDWA operand select); only its
+// low 5 bits count, which is the whole quotient wherever G is kept.
+template <int n>
+__device__ __forceinline__ void unary_step(uint32_t& G, uint32_t q, bool one) {
+  if (one) asm("v_lshl_or_b32 %0, %0, 1, 1" : "+v"(G));
+  if constexpr (n == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+        : "+v"(G) : "v"(q));
+  else if constexpr (n == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+        : "+v"(G) : "v"(q));
+  else if constexpr (n == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+        : "+v"(G) : "v"(q));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+        : "+v"(G) : "v"(q));
+}
+
 // Rice fields of one lane (32 symbols, parameter K) into the staging bits of
 // its tile starting at bit t0, from the byte-packed symbols P (symbol 4j + m
 // is byte m of P[j]; every symbol of the wave is below 256).
@@ -86,16 +107,26 @@ __device__ __forceinline__ void pack_lane_bytes(uint32_t* stage, uint32_t t0, in
     }
   }
   uint32_t upos = t0 + B + (uint32_t)N * (uint32_t)K + lane_excl;
+  constexpr uint32_t qmask4 = 0x01010101u * (0xFFu >> K);
 #pragma unroll
   for (int g = 0; g < kLaneElems / 8; g++) {
-    uint32_t G = 0u, tb = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int e = 8 * g + i;
-      const uint32_t p = tb + __builtin_amdgcn_ubfe(P[e >> 2], 8 * (e & 3) + K, 8 - K);
-      G |= 1u << (p & 31u);
-      tb = p + 1u;
-    }
+    // quotients of the group's 8 symbols, 4 bytes per register; the group's
+    // code bits tb = sum (q + 1) by byte sums (G is exact when tb <= 32)
+    const uint32_t Qa = K > 0 ? (P[2 * g] >> K) & qmask4 : P[2 * g];
+    const uint32_t Qb = K > 0 ? (P[2 * g + 1] >> K) & qmask4 : P[2 * g + 1];
+    const uint32_t tb = __builtin_amdgcn_sad_u8(Qa, 0u, __builtin_amdgcn_sad_u8(Qb, 0u, 8u));
+    // the group's codes, last symbol first: each step makes room for the
+    // codes so far after a one (the next symbol's terminating one) and then
+    // shifts by that symbol's quotient (its leading zeros)
+    uint32_t G = 1u;
+    unary_step<3>(G, Qb, false);
+    unary_step<2>(G, Qb, true);
+    unary_step<1>(G, Qb, true);
+    unary_step<0>(G, Qb, true);
+    unary_step<3>(G, Qa, true);
+    unary_step<2>(G, Qa, true);
+    unary_step<1>(G, Qa, true);
+    unary_step<0>(G, Qa, true);
     if (tb <= 32u) {
       const uint32_t sh = upos & 31u, wi = upos >> 5;
       atomicOr(&stage[wi], G << sh);
