@@ -178,10 +178,14 @@ __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
 #pragma unroll
   for (int i = 0; i < 8; i++) nneg = nneg ^ c.neg[i];
   const bool oddB = oddA != nneg;
-  const float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(ad[0], ad[1]), __builtin_fmaxf(ad[2], ad[3])),
-                                   __builtin_fmaxf(__builtin_fmaxf(ad[4], ad[5]), __builtin_fmaxf(ad[6], ad[7])));
-  const float mn = __builtin_fminf(__builtin_fminf(__builtin_fminf(ad[0], ad[1]), __builtin_fminf(ad[2], ad[3])),
-                                   __builtin_fminf(__builtin_fminf(ad[4], ad[5]), __builtin_fminf(ad[6], ad[7])));
+  // (max and min are exact and order-free on these finite values: grouped
+  // for three-operand instructions)
+  const float mx = __builtin_fmaxf(
+      __builtin_fmaxf(__builtin_fmaxf(ad[0], __builtin_fmaxf(ad[1], ad[2])), __builtin_fmaxf(ad[3], __builtin_fmaxf(ad[4], ad[5]))),
+      __builtin_fmaxf(ad[6], ad[7]));
+  const float mn = __builtin_fminf(
+      __builtin_fminf(__builtin_fminf(ad[0], __builtin_fminf(ad[1], ad[2])), __builtin_fminf(ad[3], __builtin_fminf(ad[4], ad[5]))),
+      __builtin_fminf(ad[6], ad[7]));
   const float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
   float diff = sabs - 2.0f;
   if (oddA) diff = diff + (1.0f - 2.0f * mx);

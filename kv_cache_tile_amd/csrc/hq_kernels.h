@@ -128,9 +128,12 @@ __device__ __forceinline__ void pack_lane_bytes(uint32_t* stage, uint32_t t0, in
     unary_step<1>(G, Qa, true);
     unary_step<0>(G, Qa, true);
     if (tb <= 32u) {
-      const uint32_t sh = upos & 31u, wi = upos >> 5;
-      atomicOr(&stage[wi], G << sh);
-      if (sh != 0u && sh + tb > 32u) atomicOr(&stage[wi + 1], G >> (32u - sh));
+      // the group's bits at upos: the low word, and the spill into the next
+      // one, (G >> 1) >> (31 - sh), which is 0 for sh = 0 (shift counts
+      // taken mod 32 as the hardware does)
+      const uint32_t wi = upos >> 5;
+      atomicOr(&stage[wi], G << (upos & 31u));
+      atomicOr(&stage[wi + 1], (G >> 1) >> (~upos & 31u));
     } else {
       uint32_t pos = upos;
 #pragma unroll 1
