@@ -418,15 +418,19 @@ __device__ __forceinline__ int32_t code_coord(const uint32_t* seg, int e, uint32
 }
 
 // position (0..31) of the r-th set bit (r counted from 0) of w; w has > r ones
+// (otherwise the result is some position): a binary search, each level
+// counting the ones of the next half-width field at the current position
 __device__ __forceinline__ uint32_t select_bit(uint32_t w, uint32_t r) {
-  uint32_t base = 0;
+  uint32_t pos = 0;
 #pragma unroll
   for (uint32_t half = 16; half >= 1; half >>= 1) {
-    const uint32_t lo = __builtin_popcount(w & ((1u << half) - 1u));
-    if (r >= lo) { r -= lo; w >>= half; base += half; }
-    else w &= (1u << half) - 1u;
+    const uint32_t c = __builtin_popcount(__builtin_amdgcn_ubfe(w, pos, half));
+    const uint32_t d = r - c;
+    const bool up = (int32_t)d >= 0;                        // r >= c (both below 64)
+    r = up ? d : r;
+    pos = up ? pos + half : pos;
   }
-  return base;
+  return pos;
 }
 
 // Sign diagonal on packed bf16 pairs.  For a lane's 32-bit sign mask sgn

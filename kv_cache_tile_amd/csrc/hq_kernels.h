@@ -1012,8 +1012,10 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
 
     // ---- where does each lane's first unary code start?  Every codeword has
     // exactly one 1 in the unary plane: count ones word by word (physical lane
-    // p takes words p, p+LPT, ...) and mark the bit after the (32 q)-th one for
-    // logical lane q. ----
+    // p takes words p, p+LPT, ...).  The lane whose word holds the (32 q)-th
+    // one records that word's bit position and the one's rank in it for
+    // logical lane q (< 2^27 bits, rank < 32: one word), and after the barrier
+    // lane q finds the bit itself: one select per lane, not one per word. ----
     const uint32_t words = ok ? (end - ub + 31u) >> 5 : 0u;
     uint32_t carry = 0;
     for (uint32_t r = 0;; r++) {
@@ -1033,7 +1035,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       const uint32_t before = carry + inc - c, after = carry + inc;
       const uint32_t mm = before / 32u + 1u;
       if (c != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
-        ustart[tau * LPT + mm] = ub + 32u * j + select_bit(w, 32u * mm - before - 1u) + 1u;
+        ustart[tau * LPT + mm] = ((ub + 32u * j) << 5) | (32u * mm - before - 1u);
       carry += tot;
     }
     ok = ok && carry == (uint32_t)N;
@@ -1069,7 +1071,14 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       const uint32_t rb = ok ? start + B + (uint32_t)q * kLaneElems * k : 0u;
       uint32_t lt = (uint32_t)tid;
       opaque(lt);                                           // (an address recomputed, not spilled)
-      const uint32_t u0 = ok ? (q == 0 ? ub : ustart[(lt & ~(uint32_t)(LPT - 1)) + (uint32_t)q]) : 0u;
+      uint32_t u0 = ub;
+      if (q != 0) {
+        // the recorded word (bits past the tile's end cannot hold a rank
+        // below its count of ones) and the bit after its rank-th one
+        const uint32_t rec = ok ? ustart[(lt & ~(uint32_t)(LPT - 1)) + (uint32_t)q] : 0u;
+        u0 = (rec >> 5) + select_bit(lds_read32(stage, rec >> 5), rec & 31u) + 1u;
+      }
+      u0 = ok ? u0 : 0u;
       const uint32_t lim = ok ? end : 0u;
       const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
       uint32_t upos = 0;
