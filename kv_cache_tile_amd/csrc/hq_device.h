@@ -402,6 +402,26 @@ __device__ __forceinline__ uint32_t seg_bits(const uint32_t* seg, int o, int w) 
   return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(seg[j + 1], seg[j], b), 0, w);
 }
 
+// Parity of the first D - 1 coordinates of block b for K >= 2: a coordinate's
+// low bit is bit 1 xor bit 0 of its remainder field (bit 1 is the magnitude's
+// low bit, bit 0 the zigzag sign, which complements it), so the parity is that
+// of the count of those two bits over the block's first D - 1 fields (static
+// offsets; chunks of at most 31 bits).
+template <int K, int D>
+__device__ __forceinline__ uint32_t block_low_parity(const uint32_t* seg, int b) {
+  constexpr int F = 31 / K;                                 // fields per chunk
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int f0 = 0; f0 < D - 1; f0 += F) {
+    const int nf = (D - 1 - f0) < F ? (D - 1 - f0) : F;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < nf; i++) m |= 3u << (i * K);
+    cnt += __builtin_popcount(seg_bits(seg, (b * D + f0) * K, nf * K) & m);
+  }
+  return cnt & 1u;
+}
+
 // Signed coordinate of the e-th code of a lane: unzigzag((q << K) | r) with r
 // the e-th K-bit field of the remainder plane.  The zigzag sign is r's low
 // bit (as 0 / -1); the magnitude is q above r's upper K-1 bits.

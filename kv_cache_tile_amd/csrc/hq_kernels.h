@@ -811,10 +811,14 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
 #pragma unroll
       for (int i = 0; i < D; i++) d[i] = code_coord<K>(seg, b * D + i, z[bb * D + i]);
       if constexpr (LAT == 4 || LAT == 8) {
-        int32_t par = 0;
+        uint32_t par = 0;
+        if constexpr (K >= 2) {
+          par = block_low_parity<K, D>(seg, b);
+        } else {
 #pragma unroll
-        for (int i = 0; i < D - 1; i++) par ^= d[i];
-        d[D - 1] = (int32_t)(((uint32_t)d[D - 1] << 1) | ((uint32_t)par & 1u));
+          for (int i = 0; i < D - 1; i++) par ^= (uint32_t)d[i];
+        }
+        d[D - 1] = (int32_t)(((uint32_t)d[D - 1] << 1) | (par & 1u));
       }
       const uint32_t p = (cbits >> b) & 1u;
       if constexpr (LAT == 8 && !DITHER) {
@@ -1011,31 +1015,44 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
     // ---- where does each lane's first unary code start?  Every codeword has
-    // exactly one 1 in the unary plane: count ones word by word (physical lane
-    // p takes words p, p+LPT, ...).  The lane whose word holds the (32 q)-th
-    // one records that word's bit position and the one's rank in it for
-    // logical lane q (< 2^27 bits, rank < 32: one word), and after the barrier
-    // lane q finds the bit itself: one select per lane, not one per word. ----
-    const uint32_t words = ok ? (end - ub + 31u) >> 5 : 0u;
+    // exactly one 1 in the unary plane [ub, end): count ones over the aligned
+    // stage words that cover it (the first masked below ub, the last at
+    // end), kUW consecutive words per physical lane per round, so the usual
+    // tile takes one round.  The lane whose word holds the (32 q)-th one
+    // records that word's index and the one's rank in it for logical lane q
+    // (index < 2^27, rank < 32: one word), and after the barrier lane q finds
+    // the bit itself: one select per lane. ----
+    constexpr uint32_t kUW = 3;
+    const uint32_t a0 = ub >> 5;
+    const uint32_t nw = ok ? ((end - 1u) >> 5) - a0 + 1u : 0u;   // ok: end - ub >= N
+    const uint32_t lo_mask = ~0u << (ub & 31u);
+    const uint32_t hi_keep = end & 31u;                       // counted bits of the last word (0: all)
     uint32_t carry = 0;
     for (uint32_t r = 0;; r++) {
-      const bool more = r * LPT < words;
+      const bool more = r * kUW * (uint32_t)LPT < nw;
       if (!__any(more)) break;
-      const uint32_t j = r * LPT + (uint32_t)p_lane;
-      uint32_t w = 0;
-      if (j < words) {
-        const uint32_t p = ub + 32u * j;
-        w = lds_read32(stage, p);
-        const uint32_t valid = end - p;
-        if (valid < 32u) w &= (1u << valid) - 1u;
+      const uint32_t j0 = (r * (uint32_t)LPT + (uint32_t)p_lane) * kUW;
+      uint32_t c[kUW], cs = 0;
+#pragma unroll
+      for (uint32_t i = 0; i < kUW; i++) {
+        const uint32_t j = j0 + i;
+        uint32_t x = j < nw ? stage[a0 + j] : 0u;
+        if (j == 0u) x &= lo_mask;
+        if (j + 1u == nw && hi_keep != 0u) x &= (1u << hi_keep) - 1u;
+        c[i] = __builtin_popcount(x);
+        cs += c[i];
       }
-      const uint32_t c = __builtin_popcount(w);
       uint32_t inc, tot;
-      tile_scan<LPT>(c, p_lane, inc, tot);
-      const uint32_t before = carry + inc - c, after = carry + inc;
-      const uint32_t mm = before / 32u + 1u;
-      if (c != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
-        ustart[tau * LPT + mm] = ((ub + 32u * j) << 5) | (32u * mm - before - 1u);
+      tile_scan<LPT>(cs, p_lane, inc, tot);
+      uint32_t before = carry + inc - cs;
+#pragma unroll
+      for (uint32_t i = 0; i < kUW; i++) {
+        const uint32_t after = before + c[i];
+        const uint32_t mm = before / 32u + 1u;
+        if (c[i] != 0u && mm < (uint32_t)LPT && 32u * mm <= after)
+          ustart[tau * LPT + mm] = ((a0 + j0 + i) << 5) | (32u * mm - before - 1u);
+        before = after;
+      }
       carry += tot;
     }
     ok = ok && carry == (uint32_t)N;
@@ -1073,10 +1090,14 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       opaque(lt);                                           // (an address recomputed, not spilled)
       uint32_t u0 = ub;
       if (q != 0) {
-        // the recorded word (bits past the tile's end cannot hold a rank
-        // below its count of ones) and the bit after its rank-th one
+        // the recorded word, masked as when counted (bits past the tile's end
+        // cannot hold a rank below its count of ones), and the bit after its
+        // rank-th one
         const uint32_t rec = ok ? ustart[(lt & ~(uint32_t)(LPT - 1)) + (uint32_t)q] : 0u;
-        u0 = (rec >> 5) + select_bit(lds_read32(stage, rec >> 5), rec & 31u) + 1u;
+        const uint32_t wa = rec >> 5;
+        uint32_t x = stage[wa];
+        if (wa == a0) x &= lo_mask;
+        u0 = 32u * wa + select_bit(x, rec & 31u) + 1u;
       }
       u0 = ok ? u0 : 0u;
       const uint32_t lim = ok ? end : 0u;
