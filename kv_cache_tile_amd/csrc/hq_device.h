@@ -373,6 +373,24 @@ struct UnaryWindow {
     nb -= c;
     return z;
   }
+  // the next 8 codes on the fast path, read at increasing offsets into the
+  // unchanged window (each from the 32 bits at its offset), then the window
+  // advances once.  Valid only while the running max of the codes and of the
+  // offsets stays below 31 (an offset past 30 would wrap the funnel shift).
+  __device__ __forceinline__ void take8(uint32_t (&z)[8], uint32_t& zmax) {
+    uint32_t off = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      z[i] = ffbl(__builtin_amdgcn_alignbit(hi, lo, off));
+      const uint32_t m = z[i] > off ? z[i] : off;
+      zmax = zmax > m ? zmax : m;
+      off = off + z[i] + 1u;
+    }
+    const uint64_t W = (((uint64_t)hi << 32) | lo) >> (off & 63u);
+    lo = (uint32_t)W;
+    hi = (uint32_t)(W >> 32);
+    nb -= off;
+  }
   // next code, any length; returns 0xFFFFFFFF if the run reaches `limit`
   __device__ __forceinline__ uint32_t next_exact(uint32_t limit) {
     uint64_t W = ((uint64_t)hi << 32) | lo;

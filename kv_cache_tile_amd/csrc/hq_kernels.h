@@ -788,8 +788,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
     uw.refill();
     const uint32_t saved = uw.pos();                        // the group's first bit, for a re-read
     uint32_t z[8], zmax = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) z[i] = uw.take(zmax);
+    uw.take8(z, zmax);
     if (__any(zmax >= 31u)) {
       if (zmax >= 31u) {
         // rare: read the group again exactly (a rolled loop; codes shift in from the top)
