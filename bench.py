@@ -84,6 +84,100 @@ def cpu_baseline(layers_host, rows, cols, tile, bps, seed_of, c):
                       f"decode {gb / t_dec:.4f} GB/s, {t_enc + t_dec:.1f} s"}
 
 
+def config_runs():
+    """The corroborating configurations (the DiT stack is the default bench):
+    (config, tensor name, lattice, bps, tile, kv).  The MLP weight runs every
+    lattice at 3, 4 and 5 bps; K and V of the KV cache are separate tensors."""
+    runs = [(0, "W", "E8", 4.0, 128, False), (1, "W", "E8", 4.0, 128, False)]
+    runs += [(2, "W", lat, b, 128, False) for lat in ("Z", "A2", "D4", "E8") for b in (3.0, 4.0, 5.0)]
+    runs += [(3, "K", "E8", 2.0, 128, True), (3, "V", "E8", 2.0, 128, True)]
+    return runs
+
+
+def all_configs(args):
+    """One JSON line per run of config_runs(): rate, error, encode and decode
+    GB/s (median and min of timed iterations; tensors that fit the 256 MB
+    Infinity Cache are also timed with a 512 MiB write before each launch),
+    then a plain device copy as the achievable-bandwidth reference."""
+    import torch
+    from kv_cache_tile_amd import hq, workloads
+
+    dev = torch.device("cuda:0")
+    scratch = torch.empty(512 << 18, dtype=torch.int32, device=dev)      # 512 MiB
+    cache = {}
+
+    def tensor(cfg, which):
+        key = (cfg, which)
+        if key not in cache:
+            cache.clear()
+            x = torch.from_numpy(workloads.config_tensor(cfg, which=which))
+            x = x.to(dev)
+            cache[key] = x if workloads.CONFIGS[cfg]["dtype"] == "f32" else x.to(torch.bfloat16)
+        return cache[key]
+
+    def timed(fn, flush):
+        # launches queued back to back (one synchronisation at the end), an
+        # event pair around each; the host enqueues faster than these kernels run
+        evs = []
+        for i in range(args.warmup + args.steps):
+            if flush:
+                scratch.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            if i >= args.warmup:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        return ms[len(ms) // 2], ms[0]
+
+    for cfg, which, lat, bps, tile, kv in config_runs():
+        x = tensor(cfg, which)
+        x2 = x.reshape(-1, tile) if kv else x
+        seed = workloads.codec_seed(cfg, which=which)
+        h = hq.kv_encode(x2, lat, bps, seed) if kv else hq.encode(x2, tile, lat, bps, seed)
+        out = torch.empty_like(x2)
+        enc = (lambda: hq.kv_encode(x2, lat, bps, seed, out=h)) if kv else \
+              (lambda: hq.encode(x2, tile, lat, bps, seed, out=h))
+        dec = lambda: hq.decode(h, out=out)  # noqa: E731
+        numel = x2.numel()
+        esz = x2.element_size()
+        p = hq.plan(hq.BF16 if esz == 2 else hq.F32, x2.shape[0], x2.shape[1], tile, lat, bps, kv)
+        alg = numel * (esz + bps / 8.0) + 4.0 * p.tiles + 4.0 * (p.chunks + 1)
+        fits = 2 * numel * esz < (256 << 20)
+        rec = {"config": cfg, "tensor": which, "shape": list(x.shape), "dtype": str(x2.dtype).split(".")[-1],
+               "lattice": lat, "bps_target": bps, "tile": tile, "dither": kv}
+        for flush in ((False, True) if fits else (False,)):
+            e_med, e_min = timed(enc, flush)
+            d_med, d_min = timed(dec, flush)
+            tag = "flushed" if flush else "resident"
+            gb = numel * esz / 1e9
+            rec[tag] = {"encode_us": round(1000 * e_med, 2), "encode_us_min": round(1000 * e_min, 2),
+                        "decode_us": round(1000 * d_med, 2), "decode_us_min": round(1000 * d_min, 2),
+                        "encode_GBps": round(gb / (e_med / 1000), 1), "decode_GBps": round(gb / (d_med / 1000), 1),
+                        "encode_hbm_frac_input": round(gb / (e_med / 1000) / HBM_PEAK_GBPS, 4),
+                        "decode_hbm_frac_input": round(gb / (d_med / 1000) / HBM_PEAK_GBPS, 4),
+                        "encode_roofline_frac": round(alg / (e_med / 1000) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "decode_roofline_frac": round(alg / (d_med / 1000) / 1e9 / HBM_PEAK_GBPS, 4)}
+        torch.cuda.synchronize()
+        xf = x2.double()
+        rec["bps_payload"] = round(h.bits_payload() / numel, 4)
+        rec["bps_total"] = round(h.bits_total() / numel, 4)
+        rec["compression_vs_input"] = round(8.0 * esz * numel / h.bits_total(), 3)
+        rec["nmse"] = float(((out.double() - xf) ** 2).sum() / (xf ** 2).sum())
+        rec["status_flags"] = h.flags()
+        print(json.dumps(rec), flush=True)
+        del xf, out, h
+
+    cache.clear()
+    src = torch.ones(1 << 28, dtype=torch.int32, device=dev)             # 1 GiB
+    dst = torch.empty_like(src)
+    e_med, e_min = timed(lambda: dst.copy_(src), False)
+    print(json.dumps({"reference": "device copy, 1 GiB read + 1 GiB written", "us": round(1000 * e_med, 2),
+                      "GBps_read_plus_write": round(2 * 4 * (1 << 28) / 1e9 / (e_med / 1000), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,11 +188,18 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain copy kernel over this many MiB "
                          "(reference point for the HBM byte counters)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the DiT stack: one JSON line per run of the other configurations "
+                         "(weights 1024x1024 fp32, 4096x4096, 11008x4096 over all lattices, the KV cache)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the codec "
               f"shards by layer or row slab with no communication, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        all_configs(args)
+        return
 
     import numpy as np
     import torch
