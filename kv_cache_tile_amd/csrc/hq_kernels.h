@@ -436,7 +436,9 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     // the step unless it lies within 64 units in the last place of a bf16
     // rounding tie: the pinned sum and the estimate are each within 9 and 13
     // roundings of the exact sum of squares, so their two values of
-    // sqrt(ss / n) * c differ by less than 16 units in the last place.  A wave
+    // sqrt(ss / n) * c (the estimate's square root by the hardware
+    // instruction, within 1 ulp) differ by less than 16 units in the last
+    // place.  A wave
     // with such a tile, or with an estimate outside [2^-90, 2^100] (where
     // subnormal terms, overflow, a flushed or an infinite step could enter),
     // computes the pinned sum (steps below 2^-124 are stored as 0). ----
@@ -447,7 +449,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
 #pragma unroll
     for (int m = 1; m < LPT; m <<= 1) est = est + lane_xor(est, partner_xor<LPT>(m));
     if (!ydom) est = est * inv_n;                            // sum of z^2 / n (exact power-of-two scale)
-    const float r_est = sqrtf(est * inv_n) * c;
+    const float r_est = __builtin_amdgcn_sqrtf(est * inv_n) * c;   // v_sqrt_f32: within 1 ulp
     const bool near_tie = ((as_u(r_est) & 0xFFFFu) - 0x7FC0u) <= 0x80u;
     const bool in_range = est >= 0x1p-90f && est <= 0x1p100f && r_est >= 0x1p-100f && r_est <= 0x1p100f;
     bool nonfinite = false;
@@ -481,8 +483,16 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     } else {
       sbits = bf16_rne_bits(r_est);
     }
+    // fl(1 / s) from the hardware reciprocal r0 (within 1 ulp) and one
+    // correction: e = 1 - s r0 is exact (s has 8 significant bits), r0 + r0 e
+    // differs from 1 / s by e^2 / s (below 2^-22 ulp), and 1 / s = 2^-j / M
+    // (s = M 2^j, M < 256 an integer) lies at least 2^-9 ulp from every
+    // rounding midpoint, so the fused multiply-add rounds to fl(1 / s).  s is
+    // in [2^-124, 2^61 c]: r0 and 1 / s are normal.
     const float s = as_f(sbits << 16);
-    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
+    const float inv = sbits == 0u ? 0.0f : __builtin_fmaf(e, r0, r0);
     // t = y / s; with z kept, z * (inv / sqrt(n)) is the same product: both
     // scalings are exact (a finite tile energy bounds the step by
     // sqrt(FLT_MAX / n) * c < 2^61 c, far below 2^122 for the table's rate
@@ -558,7 +568,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
 #pragma unroll
       for (int j = 0; j < kLaneElems / 4; j++) R[j] = __builtin_amdgcn_perm(S2[2 * j + 1], S2[2 * j], 0x06040200u);
 #pragma unroll
-      for (int j = kLaneElems / 4; j < kLaneElems / 2; j++) R[j] = 0u;
+      for (int j = kLaneElems / 4; j < kLaneElems / 2; j++) R[j] = S2[j];   // (unread: no copies)
     } else {
 #pragma unroll
       for (int j = 0; j < kLaneElems / 2; j++) R[j] = S2[j];
@@ -572,7 +582,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
       for (int jj = 0; jj < 3; jj++) {
         // sum of (sym >> k) = (sum of sym with its low k bits cleared) >> k
         const uint32_t kk = kb + (uint32_t)jj;
-        const uint32_t bmask = 0x01010101u * ((0xFFu << kk) & 0xFFu);
+        const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
         uint32_t acc = 0;
 #pragma unroll
         for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
@@ -603,7 +613,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
       for (uint32_t kk = 0; kk < 8u; kk++) {
         uint32_t acc = 0;
         if (bytes) {
-          const uint32_t bmask = 0x01010101u * ((0xFFu << kk) & 0xFFu);
+          const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
 #pragma unroll
           for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
           acc >>= kk;

@@ -221,6 +221,21 @@ def test_tiny_and_huge_tiles(tile, kv, dtype):
     check_full(x, tile, "E8", 2.0 if kv else 4.0, seed=17, kv=kv, dtype=dtype)
 
 
+@pytest.mark.parametrize("tile,dtype", [(256, "bf16"), (128, "bf16"), (64, "f32")])
+def test_every_step_significand(tile, dtype):
+    # rows scaled by 2^(i / 256) over three octaves, and by large and small
+    # powers of two: the tiles' steps take all 128 bf16 significands, each
+    # through the encoder's reciprocal of the step
+    T = 3 * 256 + 64
+    x = workloads.gaussian(T, tile, key=47)
+    x /= np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1, keepdims=True)).astype(np.float32)
+    sc = np.exp2(np.arange(T, dtype=np.float64) / 256.0 - 1.0)
+    sc[768:] *= np.exp2(np.repeat([-100.0, -40.0, 30.0, 55.0], 16))
+    x *= sc[:, None].astype(np.float32)
+    _, e = check_full(x, tile, "E8", 4.0, seed=19, kv=False, dtype=dtype)
+    assert len(set((e.step[e.step != 0] & 0x7F).tolist())) == 128
+
+
 def test_repeatable_and_workspace_reuse():
     # the ticket counter and look-back tags reset themselves between calls of
     # different sizes sharing one workspace
