@@ -161,15 +161,35 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   const uint32_t stage_words = avail > grp_words ? (uint32_t)avail : grp_words;
   const size_t lds = (stage_words + fixed_words) * 4;
   if (lds > (size_t)max_lds) return HQ_EINVAL;
-  int grid;
-  rc = grid_for((const void*)fn, block, lds, (P.C + group - 1) / group, &grid);
+  int grid_full;
+  rc = grid_for((const void*)fn, block, lds, UINT64_MAX, &grid_full);
   if (rc) return rc;
   // a smaller grid on request (tests use it so that few chunks still give a
   // workgroup several groups, alternating between the staging halves)
   if (const char* e = getenv("HQ_ENCODE_GRID_CAP")) {
     const long v = strtol(e, nullptr, 10);
-    if (v > 0 && v < grid) grid = (int)v;
+    if (v > 0 && v < grid_full) grid_full = (int)v;
   }
+  // Chunks per group, at most the size that fits: a workgroup runs its
+  // groups' chunks one after another, so the last to finish has run about
+  // ceil(groups / grid) groups of `group` chunks.  The size that makes that
+  // shortest, the largest such (fewest look-backs) on a tie: 4096 chunks over
+  // 512 workgroups keep groups of 4, while 5504 over 1024 take groups of 3 (2
+  // rounds of 3 chunks rather than 2 of 4) and 2048 over 1024 groups of 2.
+  const uint32_t gmax = group;
+  uint64_t best = UINT64_MAX;
+  for (uint32_t g = gmax; g >= 1u; g--) {
+    const uint64_t groups = (P.C + g - 1) / g;
+    const uint64_t span = (groups + (uint64_t)grid_full - 1) / (uint64_t)grid_full * g;
+    if (span < best) { best = span; group = g; }
+  }
+  if (const char* e = getenv("HQ_ENCODE_GROUP_CHUNKS")) {   // (tests: a fixed group size)
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0 && (uint32_t)v <= gmax) group = (uint32_t)v;
+  }
+  grp_words = group * P.chunk_words + 4;
+  const uint64_t groups = (P.C + group - 1) / group;
+  const int grid = groups < (uint64_t)grid_full ? (int)groups : grid_full;
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   const float inv_n = 1.0f / (float)tile;   // exact: tile is a power of two

@@ -96,18 +96,24 @@ def test_tile_counts(T):
     check_full(x, 128, "E8", 4.0, seed=T, kv=False, dtype="bf16")
 
 
-# The encoder stages several chunks per ticket (as many as LDS allows, at
-# most 4): chunk counts of 5, 6, 8, 10 and 17 give partial last groups and
+# The encoder stages several chunks per ticket (at most 4, and no more than
+# LDS allows): chunk counts of 5, 6, 8, 10 and 17 give partial last groups and
 # several groups, at both tile sizes the configurations use.  With the full
 # grid every workgroup gets about one group; a grid capped at 2 or 3
 # workgroups gives each several, alternating between the two halves of its
 # staging area, with a group placed while the next one is in progress.
-@pytest.mark.parametrize("grid_cap", [0, 2, 3])
+#
+# The library picks the group size that shortens the busiest workgroup's
+# sequence of chunks (with the full grid these inputs get groups of one
+# chunk); a fixed size of 4 keeps the largest groups covered as well.
+@pytest.mark.parametrize("grid_cap,group", [(0, 0), (2, 0), (3, 0), (0, 4), (2, 4), (3, 4)])
 @pytest.mark.parametrize("chunks", [5, 6, 8, 10, 17])
 @pytest.mark.parametrize("tile", [128, 256])
-def test_chunk_groups(chunks, tile, grid_cap, monkeypatch):
+def test_chunk_groups(chunks, tile, grid_cap, group, monkeypatch):
     if grid_cap:
         monkeypatch.setenv("HQ_ENCODE_GRID_CAP", str(grid_cap))
+    if group:
+        monkeypatch.setenv("HQ_ENCODE_GROUP_CHUNKS", str(group))
     T = 64 * (chunks - 1) + 7
     x = workloads.gaussian(T, tile, key=1000 + chunks)
     check_full(x, tile, "E8", 4.0, seed=chunks, kv=False, dtype="bf16")
