@@ -94,6 +94,12 @@ def config_runs():
     return runs
 
 
+def closed_loop_runs():
+    """Runs repeated with closed-loop rate control (same tuple layout)."""
+    return [(1, "W", "E8", 4.0, 128, False)] + [(2, "W", "E8", b, 128, False) for b in (3.0, 4.0, 5.0)] + \
+           [(2, "W", "A2", 4.0, 128, False), (3, "K", "E8", 2.0, 128, True)]
+
+
 def all_configs(args):
     """One JSON line per run of config_runs(): rate, error, encode and decode
     GB/s (median and min of timed iterations; tensors that fit the 256 MB
@@ -167,6 +173,34 @@ def all_configs(args):
         rec["compression_vs_input"] = round(8.0 * esz * numel / h.bits_total(), 3)
         rec["nmse"] = float(((out.double() - xf) ** 2).sum() / (xf ** 2).sum())
         rec["status_flags"] = h.flags()
+        print(json.dumps(rec), flush=True)
+        del xf, out, h
+
+    # closed-loop rate: bisection on the rate constant until the stored stream
+    # is within 0.01 bps of the target, against the table's open-loop rate
+    for cfg, which, lat, bps, tile, kv in closed_loop_runs():
+        x = tensor(cfg, which)
+        x2 = x.reshape(-1, tile) if kv else x
+        seed = workloads.codec_seed(cfg, which=which)
+        numel = x2.numel()
+        h0 = hq.kv_encode(x2, lat, bps, seed) if kv else hq.encode(x2, tile, lat, bps, seed)
+        torch.cuda.synchronize()
+        open_loop = 32.0 * h0.payload_words() / numel
+        del h0
+        hq.encode_rate(x2, tile, lat, bps, seed, kv=kv)                  # warm-up (allocations)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = hq.encode_rate(x2, tile, lat, bps, seed, kv=kv)
+        t1 = time.perf_counter()
+        out = hq.decode(h)
+        torch.cuda.synchronize()
+        xf = x2.double()
+        rec = {"closed_loop": True, "config": cfg, "tensor": which, "lattice": lat, "bps_target": bps, "tile": tile,
+               "dither": kv, "stream_bps": round(h.extra["rate"], 4), "stream_bps_table_c": round(open_loop, 4),
+               "encodes": h.extra["encodes"], "search_ms": round(1000 * (t1 - t0), 2), "c": h.c,
+               "c_table": hq.plan(hq.BF16 if x2.element_size() == 2 else hq.F32, x2.shape[0], x2.shape[1], tile,
+                                  lat, bps, kv).rate_constant,
+               "nmse": float(((out.double() - xf) ** 2).sum() / (xf ** 2).sum()), "status_flags": h.flags()}
         print(json.dumps(rec), flush=True)
         del xf, out, h
 

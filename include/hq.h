@@ -73,11 +73,11 @@ typedef enum { HQ_Z = 1, HQ_A2 = 2, HQ_D4 = 4, HQ_E8 = 8 } hq_lattice;
  * the sizes of the buffers the caller must allocate.
  *   dtype    HQ_F32 or HQ_BF16 (encode input and decode output element type)
  *   rows, cols  tensor shape, cols % tile == 0, rows*cols < 2^32
- *   tile     64, 128 or 256 (the RHT size n; "tiles (e.g. size 128)",
- *            Methodology 1)
+ *   tile     64, 128 or 256 (the RHT size n; the pages' example tile is 128,
+ *            gist.science explainer of HyperQuant, Methodology section 1)
  *   lattice  HQ_Z, HQ_A2, HQ_D4, HQ_E8 (Methodology 2)
  *   bps      target payload bits per scalar on the grid 1.5, 1.75, ..., 8
- *            ("within ~0.01 bps of any target", Methodology 3)
+ *            (the realized-rate claim of Methodology section 3)
  *   kv       0 for weights (hq_encode), 1 for the dithered KV variant
  * Outputs (any may be NULL): tiles T, chunks C, payload capacity in words
  * (worst case over all inputs), workspace bytes for hq_encode / hq_kv_encode,
@@ -141,6 +141,59 @@ int hq_kv_decode(const uint32_t *payload, uint64_t payload_words, const uint16_t
                  const uint16_t *meta, const uint32_t *chunk_off,
                  uint32_t dtype, uint64_t tokens, uint32_t head_dim, uint32_t lattice,
                  float bps, uint64_t seed, void *x_out, uint32_t *status, void *stream);
+
+/*
+ * Closed-loop rate control (gist.science explainer of HyperQuant,
+ * Methodology section 3: the realized rate lands within about 0.01 bits per
+ * scalar of the target).  The table's constants c reach that on Gaussian
+ * data; these calls take an explicit c, or search for the c at which a given
+ * tensor's stored stream, 32 * chunk_off[C] / (rows * cols) bits per scalar
+ * (coset and Rice bits plus each chunk's word alignment), is within 0.01 of
+ * the target.
+ *
+ * hq_plan_c — as hq_plan, for an explicit rate constant c (finite, > 0).
+ *   Returns HQ_EINVAL where c is so small that a tile could exceed 8191 bits.
+ * hq_encode_c / hq_decode_c — as hq_encode / hq_decode (kv = 0) or
+ *   hq_kv_encode / hq_kv_decode (kv = 1, then cols == tile == head_dim), with
+ *   the step s = bf16(rms * c) of an explicit c.  A stream must be decoded
+ *   with the c it was encoded with (the decoder sizes its staging from it).
+ * hq_rate_bracket — host only.  The search interval for a target in [1, 8]
+ *   bits per scalar: K 2^-(floor(R) + 3) and K 2^-(floor(R) - 2), where
+ *   K = fl32(sqrt(2 pi e) V^(-1/d)) is the high-rate step constant of an
+ *   entropy-coded lattice quantiser (V the covolume: Z 1, A2 sqrt3/2, D4 2,
+ *   E8 1).
+ * hq_encode_rate — synchronous: bisection on c over that bracket, at the
+ *   geometric midpoint fl32(sqrt(lo * hi)); each trial is one hq_encode_c
+ *   on `stream` followed by a 4-byte read of chunk_off[C] and a stream
+ *   synchronisation.  A trial with more bits than the target raises lo,
+ *   one with fewer lowers hi.  It stops when the rate is within 0.01 of the
+ *   target, when the midpoint equals an end of the interval (fp32
+ *   resolution), or after 30 trials; the buffers then hold the last trial's
+ *   stream, encoded with *c_out (pass it to hq_decode_c), at *bps_out bits
+ *   per scalar after *encodes_out encodes (the outputs may be NULL).
+ *   Buffers are sized by hq_plan_c at the bracket's low end (its tiles are
+ *   the longest); smaller capacities give HQ_ENOSPC before any device work.
+ *   Other arguments and errors as hq_encode_c.
+ */
+int hq_plan_c(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+              float c, uint32_t kv,
+              uint64_t *tiles, uint64_t *chunks, uint64_t *payload_cap_words,
+              uint64_t *workspace_bytes, uint32_t *tile_bound_bits);
+int hq_encode_c(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                uint32_t lattice, float c, uint64_t seed, uint32_t kv,
+                uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,
+                uint32_t *chunk_off, uint32_t *status, void *workspace, uint64_t workspace_bytes,
+                void *stream);
+int hq_decode_c(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
+                const uint16_t *meta, const uint32_t *chunk_off,
+                uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+                float c, uint64_t seed, uint32_t kv, void *x_out, uint32_t *status, void *stream);
+int hq_rate_bracket(uint32_t lattice, float target_bps, float *c_lo, float *c_hi);
+int hq_encode_rate(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                   uint32_t lattice, float target_bps, uint64_t seed, uint32_t kv,
+                   uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,
+                   uint32_t *chunk_off, uint32_t *status, void *workspace, uint64_t workspace_bytes,
+                   float *c_out, double *bps_out, uint32_t *encodes_out, void *stream);
 
 /* message for a hq_status code (static storage) */
 const char *hq_strerror(int code);

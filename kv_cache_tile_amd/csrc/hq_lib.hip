@@ -78,15 +78,20 @@ struct Plan {
   float c;
 };
 
-int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat, float bps,
-              uint32_t kv, Plan* P) {
+// closed-loop rate: targets accepted, tolerance in bits per scalar, most encodes
+constexpr float kRateMin = 1.0f, kRateMax = 8.0f;
+constexpr double kRateTol = 0.01;
+constexpr uint32_t kRateIters = 30;
+
+// sizes for an explicit rate constant c (finite and positive)
+int plan_for_c(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat, float c,
+               uint32_t kv, Plan* P) {
   if (dtype != HQ_F32 && dtype != HQ_BF16) return HQ_EINVAL;
   if (tile != 64 && tile != 128 && tile != 256) return HQ_EINVAL;
   if (!lattice_dim(lat) || kv > 1) return HQ_EINVAL;
   if (rows == 0 || cols == 0 || cols % tile) return HQ_EINVAL;
   if (rows > (1ull << 32) || cols > (1ull << 32) || rows * cols >= (1ull << 32)) return HQ_EINVAL;
-  float c;
-  if (!rate_constant(lat, tile, kv, bps, &c)) return HQ_EINVAL;
+  if (!(c > 0.0f) || !(c <= 3.0e38f)) return HQ_EINVAL;
   uint32_t bound = tile_bound_bits(tile, lat, kv, c);
   if (!bound) return HQ_EINVAL;
   P->T = rows * cols / tile;
@@ -97,6 +102,14 @@ int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint3
   P->cap_words = (P->T * bound + 31) / 32 + P->C;
   P->ws_bytes = 8 + 8 * P->C;
   return HQ_OK;
+}
+
+// sizes for a target rate on the frozen table's grid
+int make_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat, float bps,
+              uint32_t kv, Plan* P) {
+  float c;
+  if (!lattice_dim(lat) || kv > 1 || !rate_constant(lat, tile, kv, bps, &c)) return HQ_EINVAL;
+  return plan_for_c(dtype, rows, cols, tile, lat, c, kv, P);
 }
 
 EncFn enc_fn(uint32_t lat, uint32_t n, bool dither, bool bf16) {
@@ -128,13 +141,10 @@ int grid_for(const void* fn, int block, size_t lds, uint64_t chunks, int* grid) 
   return HQ_OK;
 }
 
-int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lat,
-              float bps, uint64_t seed, uint32_t kv, uint32_t* payload, uint64_t cap, uint16_t* step,
-              uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* ws, uint64_t ws_bytes,
-              void* stream) {
-  Plan P;
-  int rc = make_plan(dtype, rows, cols, tile, lat, bps, kv, &P);
-  if (rc) return rc;
+int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint32_t lat, uint64_t seed,
+              uint32_t kv, uint32_t* payload, uint64_t cap, uint16_t* step, uint16_t* meta, uint32_t* chunk_off,
+              uint32_t* status, void* ws, uint64_t ws_bytes, void* stream) {
+  int rc;
   if (!x || !payload || !step || !meta || !chunk_off || !status || !ws) return HQ_EINVAL;
   if (cap < P.cap_words || ws_bytes < P.ws_bytes) return HQ_ENOSPC;
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 7)) return HQ_EINVAL;
@@ -199,12 +209,10 @@ int do_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint3
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
-int do_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
-              const uint32_t* chunk_off, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
-              uint32_t lat, float bps, uint64_t seed, uint32_t kv, void* out, uint32_t* status, void* stream) {
-  Plan P;
-  int rc = make_plan(dtype, rows, cols, tile, lat, bps, kv, &P);
-  if (rc) return rc;
+int do_decode(const Plan& P, const uint32_t* payload, uint64_t payload_words, const uint16_t* step,
+              const uint16_t* meta, const uint32_t* chunk_off, uint32_t dtype, uint32_t tile, uint32_t lat,
+              uint64_t seed, uint32_t kv, void* out, uint32_t* status, void* stream) {
+  int rc;
   if (!payload || !step || !meta || !chunk_off || !status || !out) return HQ_EINVAL;
   if (((uintptr_t)out & 15) || ((uintptr_t)payload & 15)) return HQ_EINVAL;
   DecFn fn = dec_fn(lat, tile, kv != 0);
@@ -252,34 +260,147 @@ int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_
   return HQ_OK;
 }
 
+int hq_plan_c(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice, float c,
+              uint32_t kv, uint64_t* tiles, uint64_t* chunks, uint64_t* payload_cap_words,
+              uint64_t* workspace_bytes, uint32_t* tile_bound) {
+  Plan P;
+  int rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &P);
+  if (rc) return rc;
+  if (tiles) *tiles = P.T;
+  if (chunks) *chunks = P.C;
+  if (payload_cap_words) *payload_cap_words = P.cap_words;
+  if (workspace_bytes) *workspace_bytes = P.ws_bytes;
+  if (tile_bound) *tile_bound = P.bound;
+  return HQ_OK;
+}
+
 int hq_encode(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
               float bps, uint64_t seed, uint32_t* payload, uint64_t payload_cap_words, uint16_t* step,
               uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* workspace,
               uint64_t workspace_bytes, void* stream) {
-  return do_encode(x, dtype, rows, cols, tile, lattice, bps, seed, 0, payload, payload_cap_words, step, meta,
-                   chunk_off, status, workspace, workspace_bytes, stream);
+  Plan P;
+  int rc = make_plan(dtype, rows, cols, tile, lattice, bps, 0, &P);
+  if (rc) return rc;
+  return do_encode(P, x, dtype, tile, lattice, seed, 0, payload, payload_cap_words, step, meta, chunk_off, status,
+                   workspace, workspace_bytes, stream);
 }
 
 int hq_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
               const uint32_t* chunk_off, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
               uint32_t lattice, float bps, uint64_t seed, void* x_out, uint32_t* status, void* stream) {
-  return do_decode(payload, payload_words, step, meta, chunk_off, dtype, rows, cols, tile, lattice, bps, seed,
-                   0, x_out, status, stream);
+  Plan P;
+  int rc = make_plan(dtype, rows, cols, tile, lattice, bps, 0, &P);
+  if (rc) return rc;
+  return do_decode(P, payload, payload_words, step, meta, chunk_off, dtype, tile, lattice, seed, 0, x_out,
+                   status, stream);
 }
 
 int hq_kv_encode(const void* x, uint32_t dtype, uint64_t tokens, uint32_t head_dim, uint32_t lattice,
                  float bps, uint64_t seed, uint32_t* payload, uint64_t payload_cap_words, uint16_t* step,
                  uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* workspace,
                  uint64_t workspace_bytes, void* stream) {
-  return do_encode(x, dtype, tokens, head_dim, head_dim, lattice, bps, seed, 1, payload, payload_cap_words,
-                   step, meta, chunk_off, status, workspace, workspace_bytes, stream);
+  Plan P;
+  int rc = make_plan(dtype, tokens, head_dim, head_dim, lattice, bps, 1, &P);
+  if (rc) return rc;
+  return do_encode(P, x, dtype, head_dim, lattice, seed, 1, payload, payload_cap_words, step, meta, chunk_off,
+                   status, workspace, workspace_bytes, stream);
 }
 
 int hq_kv_decode(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
                  const uint32_t* chunk_off, uint32_t dtype, uint64_t tokens, uint32_t head_dim,
                  uint32_t lattice, float bps, uint64_t seed, void* x_out, uint32_t* status, void* stream) {
-  return do_decode(payload, payload_words, step, meta, chunk_off, dtype, tokens, head_dim, head_dim, lattice,
-                   bps, seed, 1, x_out, status, stream);
+  Plan P;
+  int rc = make_plan(dtype, tokens, head_dim, head_dim, lattice, bps, 1, &P);
+  if (rc) return rc;
+  return do_decode(P, payload, payload_words, step, meta, chunk_off, dtype, head_dim, lattice, seed, 1, x_out,
+                   status, stream);
+}
+
+int hq_encode_c(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+                float c, uint64_t seed, uint32_t kv, uint32_t* payload, uint64_t payload_cap_words,
+                uint16_t* step, uint16_t* meta, uint32_t* chunk_off, uint32_t* status, void* workspace,
+                uint64_t workspace_bytes, void* stream) {
+  Plan P;
+  int rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &P);
+  if (rc) return rc;
+  if (kv && cols != tile) return HQ_EINVAL;
+  return do_encode(P, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off,
+                   status, workspace, workspace_bytes, stream);
+}
+
+int hq_decode_c(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
+                const uint32_t* chunk_off, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                uint32_t lattice, float c, uint64_t seed, uint32_t kv, void* x_out, uint32_t* status,
+                void* stream) {
+  Plan P;
+  int rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &P);
+  if (rc) return rc;
+  if (kv && cols != tile) return HQ_EINVAL;
+  return do_decode(P, payload, payload_words, step, meta, chunk_off, dtype, tile, lattice, seed, kv, x_out,
+                   status, stream);
+}
+
+int hq_rate_bracket(uint32_t lattice, float target_bps, float* c_lo, float* c_hi) {
+  // fl32(sqrt(2 pi e) V^(-1/d)), V the lattice's covolume (Z 1, A2 sqrt3/2,
+  // D4 2, E8 1): the high-rate step constant of an entropy-coded lattice
+  // quantiser is that times 2^-R
+  uint32_t kb;
+  switch (lattice) {
+    case HQ_Z: kb = 0x40843F56u; break;
+    case HQ_A2: kb = 0x408E1BEDu; break;
+    case HQ_D4: kb = 0x405E69A9u; break;
+    case HQ_E8: kb = 0x40843F56u; break;
+    default: return HQ_EINVAL;
+  }
+  if (!(target_bps >= kRateMin && target_bps <= kRateMax) || !c_lo || !c_hi) return HQ_EINVAL;
+  float k;
+  memcpy(&k, &kb, 4);
+  const int e = (int)floorf(target_bps);
+  *c_lo = ldexpf(k, -e - 3);
+  *c_hi = ldexpf(k, -e + 2);
+  return HQ_OK;
+}
+
+int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                   uint32_t lattice, float target_bps, uint64_t seed, uint32_t kv, uint32_t* payload,
+                   uint64_t payload_cap_words, uint16_t* step, uint16_t* meta, uint32_t* chunk_off,
+                   uint32_t* status, void* workspace, uint64_t workspace_bytes, float* c_out, double* bps_out,
+                   uint32_t* encodes_out, void* stream) {
+  float lo, hi;
+  int rc = hq_rate_bracket(lattice, target_bps, &lo, &hi);
+  if (rc) return rc;
+  if (kv && cols != tile) return HQ_EINVAL;
+  // the lowest constant has the longest tiles: its plan bounds every trial
+  Plan P;
+  rc = plan_for_c(dtype, rows, cols, tile, lattice, lo, kv, &P);
+  if (rc) return rc;
+  if (payload_cap_words < P.cap_words || workspace_bytes < P.ws_bytes) return HQ_ENOSPC;
+  const double numel = (double)rows * (double)cols;
+  float c = lo;
+  double r = 0.0;
+  uint32_t it = 0;
+  while (it < kRateIters) {
+    c = (float)sqrt((double)lo * (double)hi);        // geometric midpoint (the product is exact)
+    Plan Q;
+    rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &Q);
+    if (rc) return rc;
+    rc = do_encode(Q, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off,
+                   status, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    uint32_t words = 0;
+    if (hipMemcpyAsync(&words, chunk_off + P.C, 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+        hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+      return HQ_EHIP;
+    it++;
+    r = 32.0 * (double)words / numel;
+    if (fabs(r - (double)target_bps) <= kRateTol || c == lo || c == hi) break;
+    if (r > (double)target_bps) lo = c;              // too many bits: a larger step
+    else hi = c;
+  }
+  if (c_out) *c_out = c;
+  if (bps_out) *bps_out = r;
+  if (encodes_out) *encodes_out = it;
+  return HQ_OK;
 }
 
 const char* hq_strerror(int code) {

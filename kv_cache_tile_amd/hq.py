@@ -23,7 +23,7 @@ FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE = 1, 2, 4
 CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
-           "hq_version")
+           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate")
 
 
 class HQError(RuntimeError):
@@ -53,6 +53,17 @@ def lib() -> ctypes.CDLL:
         L.hq_decode.restype = ctypes.c_int
         L.hq_kv_decode.argtypes = [vp, u64, vp, vp, vp, u32, u64, u32, u32, f32, u64, vp, vp, vp]
         L.hq_kv_decode.restype = ctypes.c_int
+        L.hq_plan_c.argtypes = [u32, u64, u64, u32, u32, f32, u32, P(u64), P(u64), P(u64), P(u64), P(u32)]
+        L.hq_plan_c.restype = ctypes.c_int
+        L.hq_encode_c.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64, vp]
+        L.hq_encode_c.restype = ctypes.c_int
+        L.hq_decode_c.argtypes = [vp, u64, vp, vp, vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, vp, vp]
+        L.hq_decode_c.restype = ctypes.c_int
+        L.hq_rate_bracket.argtypes = [u32, f32, P(f32), P(f32)]
+        L.hq_rate_bracket.restype = ctypes.c_int
+        L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
+                                     P(f32), P(ctypes.c_double), P(u32), vp]
+        L.hq_encode_rate.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_version.argtypes = []
@@ -128,6 +139,7 @@ class HQTensor:
     seed: int
     kv: bool = False
     extra: dict = field(default_factory=dict)
+    c: float | None = None    # explicit rate constant (closed-loop or hq_encode_c streams)
 
     def payload_words(self) -> int:
         return int(self.chunk_off[-1].item())
@@ -186,6 +198,11 @@ def decode(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     if out is None:
         out = torch.empty(h.shape, dtype=h.dtype, device=h.payload.device)
     dt = _dtype_code(h.dtype)
+    if h.c is not None:
+        _check(lib().hq_decode_c(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
+                                 h.chunk_off.data_ptr(), dt, rows, cols, h.tile, LATTICES[h.lattice], h.c, h.seed,
+                                 int(h.kv), out.data_ptr(), h.status.data_ptr(), _stream(out.device)))
+        return out
     fn = lib().hq_kv_decode if h.kv else lib().hq_decode
     if h.kv:
         rc = fn(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
@@ -227,3 +244,59 @@ def kv_decode(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     if not h.kv:
         raise HQError("not a KV tensor")
     return decode(h, out)
+
+
+# ---------------------------------------------------------------- explicit constant, closed-loop rate
+def plan_c(dtype: int, rows: int, cols: int, tile: int, lattice: str, c: float, kv: bool = False) -> Plan:
+    vals = [ctypes.c_uint64() for _ in range(4)]
+    tb = ctypes.c_uint32()
+    _check(lib().hq_plan_c(dtype, rows, cols, tile, LATTICES[lattice], float(c), int(kv),
+                           *[ctypes.byref(v) for v in vals], ctypes.byref(tb)))
+    return Plan(vals[0].value, vals[1].value, vals[2].value, vals[3].value, tb.value, float(c))
+
+
+def rate_bracket(lattice: str, target_bps: float) -> tuple:
+    lo, hi = ctypes.c_float(), ctypes.c_float()
+    _check(lib().hq_rate_bracket(LATTICES[lattice], float(target_bps), ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def _rows_cols(x: torch.Tensor, tile: int, kv: bool):
+    if not x.is_cuda:
+        raise HQError("needs a GPU tensor")
+    x2 = x.reshape(-1, tile if kv else x.shape[-1]).contiguous()
+    return x2, x2.shape[0], x2.shape[1]
+
+
+def encode_c(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int = 0, kv: bool = False) -> HQTensor:
+    """Encode with an explicit rate constant c (step = bf16(rms * c)); KV: tile = head_dim."""
+    x2, rows, cols = _rows_cols(x, tile, kv)
+    dt = _dtype_code(x2.dtype)
+    p = plan_c(dt, rows, cols, tile, lattice, c, kv)
+    payload, step, meta, off, status = _alloc(p, x.device)
+    ws = workspace(x.device, p.workspace_bytes)
+    _check(lib().hq_encode_c(x2.data_ptr(), dt, rows, cols, tile, LATTICES[lattice], float(c), seed, int(kv),
+                             payload.data_ptr(), payload.numel(), step.data_ptr(), meta.data_ptr(), off.data_ptr(),
+                             status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float("nan"), seed,
+                    kv, c=float(c))
+
+
+def encode_rate(x: torch.Tensor, tile: int, lattice: str, target_bps: float, seed: int = 0,
+                kv: bool = False) -> HQTensor:
+    """Closed-loop rate: the library bisects on c until the stored stream is
+    within 0.01 bits per scalar of target_bps (synchronous).  The result
+    records c, the rate reached and the number of encodes in `extra`."""
+    x2, rows, cols = _rows_cols(x, tile, kv)
+    dt = _dtype_code(x2.dtype)
+    lo, _ = rate_bracket(lattice, target_bps)
+    p = plan_c(dt, rows, cols, tile, lattice, lo, kv)
+    payload, step, meta, off, status = _alloc(p, x.device)
+    ws = workspace(x.device, p.workspace_bytes)
+    c, r, n = ctypes.c_float(), ctypes.c_double(), ctypes.c_uint32()
+    _check(lib().hq_encode_rate(x2.data_ptr(), dt, rows, cols, tile, LATTICES[lattice], float(target_bps), seed,
+                                int(kv), payload.data_ptr(), payload.numel(), step.data_ptr(), meta.data_ptr(),
+                                off.data_ptr(), status.data_ptr(), ws.data_ptr(), ws.numel(), ctypes.byref(c),
+                                ctypes.byref(r), ctypes.byref(n), _stream(x.device)))
+    return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float(target_bps),
+                    seed, kv, extra=dict(rate=r.value, encodes=n.value), c=c.value)

@@ -6,7 +6,7 @@ the fp32 constant c such that the oracle's payload rate (coset bits + Rice
 bits, averaged over the tensor) on 2^18 seeded N(0,1) scalars equals R.
 
 Why a table: the per-tile step is RMS * c; the pages state that the realized
-rate lands within ~0.01 bps of any target (gist.science explainer of
+rate lands within about a hundredth of a bit per scalar of the target (gist.science explainer of
 HyperQuant, Methodology section 3, "Bit-Stripping and Rice Coding") and that
 the pipeline is data-free (Significance section, "Practical Deployment"), so c
 is fixed per (lattice, tile, rate) from synthetic Gaussians, which is what the

@@ -98,7 +98,7 @@ static uint32_t coset_bits_per_block(uint32_t lat) { return (lat == HQO_E8 || la
 
 /* ------------------------------------------------------------------------ */
 /* [M1] RHT_n(x) = H_n D x, scaled by 1/sqrt(n) so that it is orthogonal     */
-/* ("The transform is orthogonal").  H_n is the Sylvester-ordered           */
+/* (the pages call the transform orthogonal).  H_n is the Sylvester-ordered */
 /* Walsh-Hadamard matrix, H_ij = (-1)^popcount(i & j), applied by the fast   */
 /* butterfly with strides h = 1, 2, 4, ..., n/2 in that order.              */
 /* ------------------------------------------------------------------------ */

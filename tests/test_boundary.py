@@ -30,6 +30,12 @@ def lib():
     L.hq_decode.argtypes = [vp, u64, vp, vp, vp, u32, u64, u64, u32, u32, f32, u64, vp, vp, vp]
     L.hq_kv_encode.argtypes = [vp, u32, u64, u32, u32, f32, u64, vp, u64, vp, vp, vp, vp, vp, u64, vp]
     L.hq_kv_decode.argtypes = [vp, u64, vp, vp, vp, u32, u64, u32, u32, f32, u64, vp, vp, vp]
+    L.hq_plan_c.argtypes = [u32, u64, u64, u32, u32, f32, u32, P(u64), P(u64), P(u64), P(u64), P(u32)]
+    L.hq_encode_c.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64, vp]
+    L.hq_decode_c.argtypes = [vp, u64, vp, vp, vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, vp, vp]
+    L.hq_rate_bracket.argtypes = [u32, f32, P(f32), P(f32)]
+    L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
+                                 P(f32), P(ctypes.c_double), P(u32), vp]
     L.hq_strerror.argtypes = [ctypes.c_int]
     L.hq_strerror.restype = ctypes.c_char_p
     L.hq_version.restype = u32
@@ -113,3 +119,60 @@ def test_calls_reject_bad_pointers_before_device_work(lib):
     assert dec(pay=A + 4) == EINVAL                # payload not 16-byte aligned
     assert lib.hq_kv_encode(A, BF16, 100, 96, E8, 2.0, 1, A, 1 << 20, A, A, A, A, A, 1 << 20, None) == EINVAL
     assert lib.hq_kv_decode(A, 100, A, A, A, BF16, 100, 96, E8, 2.0, 1, A, A, None) == EINVAL
+
+
+# ---------------------------------------------------------------- closed-loop rate (host side)
+def plan_c(lib, c, dtype=BF16, rows=4096, cols=16384, tile=256, lat=E8, kv=0):
+    T, C, cap, ws = (ctypes.c_uint64() for _ in range(4))
+    bound = ctypes.c_uint32()
+    rc = lib.hq_plan_c(dtype, rows, cols, tile, lat, c, kv, ctypes.byref(T), ctypes.byref(C), ctypes.byref(cap),
+                       ctypes.byref(ws), ctypes.byref(bound))
+    return rc, T.value, C.value, cap.value, ws.value, bound.value
+
+
+def test_plan_c_matches_the_table_plan_and_shrinks_with_c(lib):
+    rc, T, C, cap, ws, bound, c = plan(lib)
+    assert plan_c(lib, c) == (OK, T, C, cap, ws, bound)
+    bounds = [plan_c(lib, c * f)[5] for f in (0.25, 0.5, 1.0, 2.0, 4.0)]
+    assert all(a > b for a, b in zip(bounds, bounds[1:]))
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-4):   # 1e-4: tiles could pass 8191 bits
+        assert plan_c(lib, bad)[0] == EINVAL
+
+
+def test_rate_bracket_matches_the_oracle(lib):
+    import numpy as np
+
+    import oracle
+    lo, hi = ctypes.c_float(), ctypes.c_float()
+    for name, code in (("Z", Z), ("A2", A2), ("D4", D4), ("E8", E8)):
+        for R in (1.0, 2.0, 3.3, 4.0, 5.75, 7.99, 8.0):
+            assert lib.hq_rate_bracket(code, R, ctypes.byref(lo), ctypes.byref(hi)) == OK
+            assert (lo.value, hi.value) == oracle.rate_bracket(name, float(np.float32(R)))
+    for R in (0.5, 8.5, float("nan")):
+        assert lib.hq_rate_bracket(E8, R, ctypes.byref(lo), ctypes.byref(hi)) == EINVAL
+    assert lib.hq_rate_bracket(3, 4.0, ctypes.byref(lo), ctypes.byref(hi)) == EINVAL
+
+
+def test_rate_calls_reject_before_device_work(lib):
+    A = 1 << 40
+    lo, hi = ctypes.c_float(), ctypes.c_float()
+    lib.hq_rate_bracket(E8, 4.0, ctypes.byref(lo), ctypes.byref(hi))
+    rc, T, C, cap, ws, bound = plan_c(lib, lo.value, rows=64, cols=1024, tile=128)
+    assert rc == OK
+    c_out, r_out, n_out = ctypes.c_float(), ctypes.c_double(), ctypes.c_uint32()
+
+    def rate(**kw):
+        a = dict(x=A, pay=A, cap=cap, ws=ws, R=4.0, kv=0, cols=1024, tile=128)
+        a.update(kw)
+        return lib.hq_encode_rate(a["x"], BF16, 64, a["cols"], a["tile"], E8, a["R"], 1, a["kv"], a["pay"],
+                                  a["cap"], A, A, A, A, A, a["ws"], ctypes.byref(c_out), ctypes.byref(r_out),
+                                  ctypes.byref(n_out), None)
+
+    assert rate(cap=cap - 1) == ENOSPC and rate(ws=ws - 8) == ENOSPC   # sized at the bracket's low end
+    assert rate(R=0.5) == EINVAL and rate(R=9.0) == EINVAL
+    assert rate(kv=1) == EINVAL                                        # KV needs cols == tile
+    assert rate(x=None) == EINVAL and rate(pay=None) == EINVAL          # the first trial's checks
+    assert lib.hq_encode_c(A, BF16, 64, 1024, 128, E8, 0.0, 1, 0, A, cap, A, A, A, A, A, ws, None) == EINVAL
+    assert lib.hq_encode_c(None, BF16, 64, 1024, 128, E8, 0.3, 1, 0, A, cap, A, A, A, A, A, ws, None) == EINVAL
+    assert lib.hq_decode_c(A, 100, A, A, A, BF16, 64, 1024, 128, E8, -1.0, 1, 0, A, A, None) == EINVAL
+    assert lib.hq_decode_c(A, 100, A, A, A, BF16, 64, 1024, 128, E8, 0.3, 1, 1, A, A, None) == EINVAL

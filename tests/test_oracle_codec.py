@@ -88,7 +88,7 @@ def test_long_unary_runs_cross_words():
 @pytest.mark.parametrize("lat", ["Z", "A2", "D4", "E8"])
 @pytest.mark.parametrize("bps", [2.0, 3.0, 4.0, 5.0])
 def test_realized_rate_within_001_bps_on_fresh_gaussians(lat, bps):
-    # Methodology section 3: realized rate within ~0.01 bps of any target
+    # Methodology section 3: the realized rate is within about 0.01 bps of the target
     x = workloads.gaussian(1024, 128, key=777)
     c = rate_c(lat, 128, bps)
     e = oracle.encode(x, 128, lat, c, seed=12345)
