@@ -101,6 +101,11 @@ int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_
  *              before its first use; the kernels leave it ready for the next
  *              call.  Calls that overlap in time must not share a workspace.
  * The bit stream is a pure function of (x, shape, tile, lattice, bps, seed).
+ * The encode grid is persistent: its workgroups wait for one another's chunk
+ * offsets, and the grid is sized (cus x occupancy) to be resident at once.
+ * Do not run two encodes concurrently on one device (on different streams),
+ * nor alongside a kernel that never finishes: either could keep part of the
+ * grid from starting while the rest waits for it.
  */
 int hq_encode(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
               uint32_t lattice, float bps, uint64_t seed,
