@@ -144,3 +144,14 @@ def dit_layer_device(rows: int, cols: int, layer: int, device, std: float = 0.02
     t = z / torch.sqrt(chi / nu)
     w = torch.where(mask, t, w)
     return w.to(torch.bfloat16)
+
+
+def haar_orthogonal(d: int, key: int) -> np.ndarray:
+    """A Haar-uniform d x d orthogonal matrix (the KV path's per-layer
+    rotation is drawn by the caller): QR of an fp64 Gaussian matrix with the
+    signs of R's diagonal moved into Q (Mezzadri's correction), rounded to
+    fp32, row-major."""
+    g = _rng(7, key).standard_normal((d, d))
+    q, r = np.linalg.qr(g)
+    q = q * np.sign(np.diag(r))[None, :]
+    return np.ascontiguousarray(q, dtype=np.float32)

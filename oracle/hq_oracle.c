@@ -695,3 +695,37 @@ int hqo_decode_tiles(const uint16_t *step, const uint16_t *meta, const uint32_t 
     }
     return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* [M4] The per-layer rotation of KV vectors by a Haar-uniform orthogonal   */
+/* matrix, the alternative to the sign diagonal (gist.science explainer of  */
+/* HyperQuant, Methodology section 4, "Bias Correction for KV Cache").      */
+/* Reading: the vector is rotated, y = Q x, before the codec's own per-tile */
+/* RHT; H D Q is Haar-uniform whenever Q is, so the composite is the pages' */
+/* Haar rotation.  Decode applies Q^T after the codec's inverse.  Q is an   */
+/* input (the caller draws it).  Each output is one fused multiply-add      */
+/* chain over j = 0 .. d-1 in ascending order, starting from +0:            */
+/*   y_i = fma(M_i,d-1, x_d-1, ... fma(M_i,1, x_1, fma(M_i,0, x_0, 0))),     */
+/* with M = Q (transpose = 0) or Q^T (transpose = 1), Q row-major [d][d].   */
+/* x and y are [rows][d], fp32 or bf16 bits (y rounded to nearest even).    */
+/* ------------------------------------------------------------------------ */
+void hqo_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uint32_t x_dtype,
+                uint64_t rows, void *y, uint32_t y_dtype)
+{
+    float *xv = (float *)malloc(sizeof(float) * d);
+    for (uint64_t r = 0; r < rows; r++) {
+        for (uint32_t j = 0; j < d; j++)
+            xv[j] = x_dtype == HQO_BF16 ? bf16_to_f32(((const uint16_t *)x)[r * d + j])
+                                        : ((const float *)x)[r * d + j];
+        for (uint32_t i = 0; i < d; i++) {
+            float acc = 0.0f;
+            for (uint32_t j = 0; j < d; j++) {
+                const float m = transpose ? Q[(uint64_t)j * d + i] : Q[(uint64_t)i * d + j];
+                acc = fmaf(m, xv[j], acc);
+            }
+            if (y_dtype == HQO_BF16) ((uint16_t *)y)[r * d + i] = bf16_rne(acc);
+            else ((float *)y)[r * d + i] = acc;
+        }
+    }
+    free(xv);
+}

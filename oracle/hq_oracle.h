@@ -85,6 +85,11 @@ int hqo_decode_tiles(const uint16_t *step, const uint16_t *meta, const uint32_t 
 int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t1,
                      uint16_t *step, uint16_t *meta, uint32_t *bits, uint64_t bits_cap_words);
 
+/* KV rotation y = Q x (transpose = 0) or Q^T x per d-vector, one ascending
+ * fused multiply-add chain per output; x, y fp32 or bf16 bits, [rows][d] */
+void hqo_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uint32_t x_dtype,
+                uint64_t rows, void *y, uint32_t y_dtype);
+
 #ifdef __cplusplus
 }
 #endif

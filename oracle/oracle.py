@@ -86,6 +86,9 @@ def lib():
         L.hqo_encode_tiles.restype = ctypes.c_int
         L.hqo_decode_tiles.argtypes = [vp, vp, vp, ctypes.c_uint64, P(_Params), ctypes.c_uint64, ctypes.c_uint64, vp]
         L.hqo_decode_tiles.restype = ctypes.c_int
+        L.hqo_rotate.argtypes = [vp, ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_uint32, ctypes.c_uint64, vp,
+                                 ctypes.c_uint32]
+        L.hqo_rotate.restype = None
         _lib = L
     return _lib
 
@@ -320,3 +323,17 @@ def rate_search(x: np.ndarray, tile: int, lattice: str, target: float, seed: int
         else:
             hi = c
     return c, r, it, e
+
+
+# ---------------------------------------------------------------- KV rotation
+def rotate(Q: np.ndarray, x: np.ndarray, transpose: bool = False, out_dtype: int = F32) -> np.ndarray:
+    """y = Q x (or Q^T x) for every d-vector row of x (float32, or uint16 bf16
+    bits); Q float32 [d][d].  Returns float32, or uint16 bf16 bits."""
+    Q = np.ascontiguousarray(Q, np.float32)
+    d = Q.shape[0]
+    assert Q.shape == (d, d) and x.shape[-1] == d
+    xdt = F32 if x.dtype == np.float32 else BF16
+    x = _as_input(x.reshape(-1, d), xdt)
+    y = np.zeros(x.shape, np.float32 if out_dtype == F32 else np.uint16)
+    lib().hqo_rotate(_ptr(Q), d, int(transpose), _ptr(x), xdt, x.shape[0], _ptr(y), out_dtype)
+    return y
