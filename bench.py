@@ -204,6 +204,45 @@ def all_configs(args):
         print(json.dumps(rec), flush=True)
         del xf, out, h
 
+    # the KV cache with the per-layer Haar rotation (rotation kernel, then the
+    # dithered codec on the fp32 rotated vectors; decode, then the transposed
+    # rotation back to bf16)
+    for which in ("K", "V"):
+        x = tensor(3, which)
+        x2 = x.reshape(-1, 128)
+        seed = workloads.codec_seed(3, which=which)
+        Q = torch.from_numpy(workloads.haar_orthogonal(128, 3)).to(dev)
+        y = hq.rotate(Q, x2, out_dtype=torch.float32)
+        h = hq.kv_encode(y, "E8", 2.0, seed)
+        out = torch.empty_like(x2)
+        yd = torch.empty_like(y)
+
+        def enc():
+            hq.rotate(Q, x2, out=y)
+            hq.kv_encode(y, "E8", 2.0, seed, out=h)
+
+        def dec():
+            hq.decode(h, out=yd)
+            hq.rotate(Q, yd, transpose=True, out=out)
+
+        rot_med, rot_min = timed(lambda: hq.rotate(Q, x2, out=y), False)
+        e_med, e_min = timed(enc, False)
+        d_med, d_min = timed(dec, False)
+        torch.cuda.synchronize()
+        numel = x2.numel()
+        xf = x2.double()
+        gb = numel * 2 / 1e9
+        flops = 2.0 * numel * 128
+        rec = {"haar_rotation": True, "config": 3, "tensor": which, "lattice": "E8", "bps_target": 2.0, "tile": 128,
+               "dither": True, "rotate_us": round(1000 * rot_med, 2),
+               "rotate_TFLOPs": round(flops / (rot_med / 1000) / 1e12, 2),
+               "encode_us": round(1000 * e_med, 2), "decode_us": round(1000 * d_med, 2),
+               "encode_GBps": round(gb / (e_med / 1000), 1), "decode_GBps": round(gb / (d_med / 1000), 1),
+               "bps_payload": round(h.bits_payload() / numel, 4),
+               "nmse": float(((out.double() - xf) ** 2).sum() / (xf ** 2).sum()), "status_flags": h.flags()}
+        print(json.dumps(rec), flush=True)
+        del xf, out, h, y, yd
+
     cache.clear()
     src = torch.ones(1 << 28, dtype=torch.int32, device=dev)             # 1 GiB
     dst = torch.empty_like(src)

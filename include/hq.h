@@ -200,6 +200,25 @@ int hq_encode_rate(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, 
                    uint32_t *chunk_off, uint32_t *status, void *workspace, uint64_t workspace_bytes,
                    float *c_out, double *bps_out, uint32_t *encodes_out, void *stream);
 
+/*
+ * hq_rotate — the KV path's per-layer Haar rotation (gist.science explainer
+ * of HyperQuant, Methodology section 4, "Bias Correction for KV Cache": a
+ * Haar-uniform rotation as the alternative to the sign diagonal).  For each
+ * of `rows` d-vectors (d = 64 or 128), y = Q x (transpose = 0) or Q^T x
+ * (transpose = 1), each output one fused multiply-add chain over j = 0 ..
+ * d-1 in ascending order from +0 (bf16 output: that value rounded to nearest
+ * even).  The rotation runs before hq_kv_encode (whose RHT then applies
+ * H D; H D Q is Haar-uniform whenever Q is) and, transposed, after
+ * hq_kv_decode.
+ *   Q   device, [d][d] fp32 row-major, 4-byte aligned, drawn by the caller
+ *   x   device, [rows][d] of x_dtype (HQ_F32 or HQ_BF16), 16-byte aligned
+ *   y   device, [rows][d] of y_dtype, 16-byte aligned, not overlapping x
+ * Asynchronous on `stream`; HQ_EINVAL for another d, a bad dtype, a NULL or
+ * misaligned pointer, or rows >= 2^32 (before any device work).
+ */
+int hq_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uint32_t x_dtype,
+              uint64_t rows, void *y, uint32_t y_dtype, void *stream);
+
 /* message for a hq_status code (static storage) */
 const char *hq_strerror(int code);
 /* (major << 16) | minor of the library; the stream layout above is version 1 */

@@ -16,6 +16,13 @@
 #include "hq.h"
 #include "hq_kernels.h"
 
+namespace hq {
+// hq_kern_rot.hip: the rotation kernel for (d, input, output dtype), its LDS
+// bytes, threads and rows per workgroup pass (null for an unsupported d)
+const void* rot_mfma_fn(uint32_t d, bool xbf16, bool ybf16, size_t* lds, uint32_t* threads,
+                        uint32_t* rows_per_block);
+}  // namespace hq
+
 using namespace hq;
 
 namespace {
@@ -401,6 +408,24 @@ int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, 
   if (bps_out) *bps_out = r;
   if (encodes_out) *encodes_out = it;
   return HQ_OK;
+}
+
+int hq_rotate(const float* Q, uint32_t d, uint32_t transpose, const void* x, uint32_t x_dtype, uint64_t rows,
+              void* y, uint32_t y_dtype, void* stream) {
+  if ((x_dtype != HQ_F32 && x_dtype != HQ_BF16) || (y_dtype != HQ_F32 && y_dtype != HQ_BF16) || transpose > 1)
+    return HQ_EINVAL;
+  size_t lds = 0;
+  uint32_t rb = 0, threads = 0;
+  const void* fn = rot_mfma_fn(d, x_dtype == HQ_BF16, y_dtype == HQ_BF16, &lds, &threads, &rb);
+  if (!fn || !Q || !x || !y || rows >= (1ull << 32)) return HQ_EINVAL;
+  if (((uintptr_t)x & 15) || ((uintptr_t)y & 15) || ((uintptr_t)Q & 3)) return HQ_EINVAL;
+  if (rows == 0) return HQ_OK;
+  int grid;
+  int rc = grid_for(fn, (int)threads, lds, (rows + rb - 1) / rb, &grid);
+  if (rc) return rc;
+  hipLaunchKernelGGL((void (*)(const float*, uint32_t, const void*, uint64_t, void*))fn, dim3(grid), dim3(threads),
+                     lds, (hipStream_t)stream, Q, transpose, x, rows, y);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
 const char* hq_strerror(int code) {

@@ -23,7 +23,7 @@ FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE = 1, 2, 4
 CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
-           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate")
+           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate")
 
 
 class HQError(RuntimeError):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
                                      P(f32), P(ctypes.c_double), P(u32), vp]
         L.hq_encode_rate.restype = ctypes.c_int
+        L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
+        L.hq_rotate.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_version.argtypes = []
@@ -300,3 +302,37 @@ def encode_rate(x: torch.Tensor, tile: int, lattice: str, target_bps: float, see
                                 ctypes.byref(r), ctypes.byref(n), _stream(x.device)))
     return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float(target_bps),
                     seed, kv, extra=dict(rate=r.value, encodes=n.value), c=c.value)
+
+
+# ---------------------------------------------------------------- KV Haar rotation
+def rotate(Q: torch.Tensor, x: torch.Tensor, transpose: bool = False, out_dtype: torch.dtype | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = Q x (or Q^T x) for every d-vector (last dim) of x; Q fp32 [d][d] on
+    the same GPU, d = 64 or 128."""
+    if not x.is_cuda or not Q.is_cuda or Q.dtype != torch.float32:
+        raise HQError("rotate needs GPU tensors and an fp32 Q")
+    d = Q.shape[0]
+    x2 = x.reshape(-1, d).contiguous()
+    Qc = Q.contiguous()
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().hq_rotate(Qc.data_ptr(), d, int(transpose), x2.data_ptr(), _dtype_code(x2.dtype), x2.shape[0],
+                           out.data_ptr(), _dtype_code(out.dtype), _stream(x.device)))
+    return out
+
+
+def kv_encode_haar(x: torch.Tensor, Q: torch.Tensor, lattice: str = "E8", bps: float = 2.0,
+                   seed: int = 0) -> HQTensor:
+    """KV vectors rotated by the caller's Haar matrix Q (fp32, rotated values
+    kept in fp32), then coded by the dithered KV path; decode with
+    kv_decode_haar."""
+    y = rotate(Q, x, out_dtype=torch.float32)
+    h = kv_encode(y, lattice, bps, seed)
+    h.extra["haar_Q"] = Q
+    h.extra["haar_out_dtype"] = x.dtype
+    return h
+
+
+def kv_decode_haar(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    y = kv_decode(h)
+    return rotate(h.extra["haar_Q"], y, transpose=True, out_dtype=h.extra["haar_out_dtype"], out=out)

@@ -36,6 +36,7 @@ def lib():
     L.hq_rate_bracket.argtypes = [u32, f32, P(f32), P(f32)]
     L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
                                  P(f32), P(ctypes.c_double), P(u32), vp]
+    L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
     L.hq_strerror.argtypes = [ctypes.c_int]
     L.hq_strerror.restype = ctypes.c_char_p
     L.hq_version.restype = u32
@@ -176,3 +177,24 @@ def test_rate_calls_reject_before_device_work(lib):
     assert lib.hq_encode_c(None, BF16, 64, 1024, 128, E8, 0.3, 1, 0, A, cap, A, A, A, A, A, ws, None) == EINVAL
     assert lib.hq_decode_c(A, 100, A, A, A, BF16, 64, 1024, 128, E8, -1.0, 1, 0, A, A, None) == EINVAL
     assert lib.hq_decode_c(A, 100, A, A, A, BF16, 64, 1024, 128, E8, 0.3, 1, 1, A, A, None) == EINVAL
+
+
+def test_rotate_rejects_before_device_work(lib):
+    A = 1 << 40
+    assert lib.hq_rotate(A, 96, 0, A, BF16, 10, A, F32, None) == EINVAL           # d is 64 or 128
+    assert lib.hq_rotate(A, 128, 2, A, BF16, 10, A, F32, None) == EINVAL
+    assert lib.hq_rotate(A, 128, 0, A, 3, 10, A, F32, None) == EINVAL
+    assert lib.hq_rotate(None, 128, 0, A, BF16, 10, A, F32, None) == EINVAL
+    assert lib.hq_rotate(A, 128, 0, A + 8, BF16, 10, A, F32, None) == EINVAL      # x not 16-byte aligned
+    assert lib.hq_rotate(A, 128, 0, A, BF16, 10, A + 4, F32, None) == EINVAL
+    assert lib.hq_rotate(A, 128, 0, A, BF16, 1 << 32, A, F32, None) == EINVAL
+    assert lib.hq_rotate(A, 128, 0, A, BF16, 0, A, F32, None) == OK               # nothing to do
+
+
+def test_library_has_no_undefined_internal_symbols():
+    # every function the library calls is defined in it or in a system/ROCm
+    # library: none of its own namespaces may be left undefined
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", LIB], capture_output=True, text=True).stdout
+    bad = [l for l in out.splitlines() if "_GLOBAL__N" in l or "_ZN2hq" in l]
+    assert not bad, bad
