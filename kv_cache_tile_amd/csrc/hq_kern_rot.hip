@@ -21,21 +21,23 @@ namespace hq {
 // blocks per instruction, rounded once like a fused multiply-add (bit-equal
 // to fmaf over normal, subnormal and cancelling operands, and pinned by the
 // parity tests against the oracle's chains), so issuing it for j = 0 .. D-1
-// in order gives each output exactly the ascending chain.  A wave owns 64
-// rows (block b: lanes 32b .. 32b+31 supply the x of rows 32b + lane % 32 of
-// its slab) and all D outputs: D / 32 instructions per j, each over a
-// 32-output slice of the matrix that both blocks share.  x streams from
-// global memory 8 values at a time (the next 8 in flight); the matrix sits in
-// LDS as Mt[j][i].  Output layout of a block: register r of lane l holds row
-// (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
+// in order gives each output exactly the ascending chain.  A wave owns 32
+// rows and all D outputs: both blocks take the same 32 rows (lanes l and
+// l + 32 supply the x of row l % 32 of the wave's slab) and instruction t
+// covers outputs 64 t .. 64 t + 63 (block b the 32 from 64 t + 32 b), D / 64
+// instructions per j.  That keeps 64 accumulators per lane for D = 128, so
+// several waves share a SIMD.  x streams from global memory 8 values at a
+// time (the next 8 in flight); the matrix sits in LDS as Mt[j][i].  Output
+// layout of a block: register r of lane l holds row (r / 4) 8 + (l / 32) 4 +
+// r % 4, column l % 32.
 typedef float rot_f32x32 __attribute__((ext_vector_type(32)));
-constexpr int kRotMfmaWaves = 4;
+constexpr int kRotMfmaWaves = 8;
 
 template <int D, bool XBF16, bool YBF16>
 __global__ void __launch_bounds__(64 * kRotMfmaWaves)
 rotate_mfma_kernel(const float* __restrict__ Q, uint32_t transpose, const void* __restrict__ x, uint64_t rows,
                    void* __restrict__ y) {
-  constexpr int IT = D / 32;
+  constexpr int IT = D / 64;
   extern __shared__ float rsm[];
   float* Mt = rsm;                       // [D][D]
   const int tid = threadIdx.x;
@@ -47,10 +49,10 @@ rotate_mfma_kernel(const float* __restrict__ Q, uint32_t transpose, const void* 
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
-  const uint64_t nblk = (rows + 63) / 64;                  // 64-row slabs, one per wave at a time
+  const uint64_t nblk = (rows + 31) / 32;                  // 32-row slabs, one per wave at a time
   for (uint64_t blk = (uint64_t)blockIdx.x * kRotMfmaWaves + wave; blk < nblk;
        blk += (uint64_t)gridDim.x * kRotMfmaWaves) {
-    const uint64_t row = blk * 64 + (uint64_t)lane;
+    const uint64_t row = blk * 32 + (uint64_t)(lane & 31);
     const bool live = row < rows;
     rot_f32x32 acc[IT];
 #pragma unroll
@@ -74,6 +76,7 @@ rotate_mfma_kernel(const float* __restrict__ Q, uint32_t transpose, const void* 
     };
     uint32_t wn[8];
     load8(0, wn);
+#pragma unroll 1
     for (int j0 = 0; j0 < D; j0 += 8) {
       uint32_t w[8];
 #pragma unroll
@@ -92,19 +95,19 @@ rotate_mfma_kernel(const float* __restrict__ Q, uint32_t transpose, const void* 
       }
 #pragma unroll
       for (int jj = 0; jj < 8; jj++) {
-        const float* mrow = Mt + (j0 + jj) * D + (lane & 31);
+        const float* mrow = Mt + (j0 + jj) * D + lane;
 #pragma unroll
         for (int t = 0; t < IT; t++)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(xv[jj], mrow[32 * t], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(xv[jj], mrow[64 * t], acc[t], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int t = 0; t < IT; t++) {
-      const int col = 32 * t + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 32; r++) {
         const int b = r >> 4, rr = r & 15;
-        const uint64_t orow = blk * 64 + (uint64_t)(32 * b + (rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3));
+        const int col = 64 * t + 32 * b + (lane & 31);
+        const uint64_t orow = blk * 32 + (uint64_t)((rr >> 2) * 8 + (lane >> 5) * 4 + (rr & 3));
         if (orow < rows) {
           if (YBF16) {
             const uint32_t h = bf16x2_rne(acc[t][r], 0.0f) & 0xFFFFu;
@@ -130,7 +133,7 @@ RotFn rot_mfma_table_d(bool xbf16, bool ybf16) {
 // threads and rows per workgroup pass; null for an unsupported d
 const void* rot_mfma_fn(uint32_t d, bool xbf16, bool ybf16, size_t* lds, uint32_t* threads, uint32_t* rows_per_block) {
   *threads = 64 * kRotMfmaWaves;
-  *rows_per_block = 64 * kRotMfmaWaves;
+  *rows_per_block = 32 * kRotMfmaWaves;
   if (d == 64) { *lds = 64 * 64 * 4; return (const void*)rot_mfma_table_d<64>(xbf16, ybf16); }
   if (d == 128) { *lds = 128 * 128 * 4; return (const void*)rot_mfma_table_d<128>(xbf16, ybf16); }
   return nullptr;
