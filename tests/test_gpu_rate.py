@@ -100,3 +100,27 @@ def test_rate_search_llama_projection_full():
     assert abs(r - 4.0) <= 0.01
     torch.cuda.synchronize()
     np.testing.assert_array_equal(h.payload[:h.payload_words()].cpu().numpy().view(np.uint32), e.payload)
+
+
+@pytest.mark.parametrize("kind", ["zeros", "nan_row"])
+def test_rate_search_degenerate_inputs(kind):
+    # an all-zero tensor cannot reach the target (every tile costs its coset
+    # bits and one unary bit a symbol): the search runs down to the bracket's
+    # end; a non-finite row is coded as zero and flagged.  Both sides take the
+    # same steps either way.
+    x = np.zeros((256, 512), np.float32) if kind == "zeros" else workloads.gaussian(256, 512, key=8)
+    if kind == "nan_row":
+        x[17, 100] = np.nan
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    xo = workloads.bf16_bits(t)
+    print(f"[case] rate search degenerate {kind}", flush=True)
+    h = hq.encode_rate(t.to(_dev()), 128, "E8", 4.0, seed=3)
+    c, r, n, e = oracle.rate_search(xo, 128, "E8", 4.0, 3)
+    assert (h.c, h.extra["rate"], h.extra["encodes"]) == (c, r, n)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(h.payload[:h.payload_words()].cpu().numpy().view(np.uint32), e.payload)
+    np.testing.assert_array_equal(h.step.cpu().numpy().view(np.uint16), e.step)
+    if kind == "zeros":
+        assert r < 1.2 and n > 5           # 144 bits per 128-scalar tile, far below the target
+    else:
+        assert h.flags() == hq.FLAG_NONFINITE and e.status == oracle.ENONFINITE
