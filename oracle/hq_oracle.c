@@ -729,3 +729,102 @@ void hqo_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, u
     }
     free(xv);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode into integer codes for an int8 matrix product (the pages name     */
+/* int8 matrix-core paths on the post-RHT lattice output, the lattice's     */
+/* integer embedding fitting 8 bits; gist.science explainer of HyperQuant,  */
+/* Key Contributions, "Hardware Integration", and Methodology section 2).   */
+/* Reading: a tile's codes are 2 P (P its lattice point, so 2 P is an       */
+/* integer vector for Z, D4 and E8), saturated to [-127, 127] (flagged);    */
+/* its weights are then D H (s P) / sqrt(n), so a row of the weight matrix  */
+/* times an activation x is sum over tiles of s_t <P_t, RHT(x)_t>.  The     */
+/* activation's RHT is quantized per tile to int8 with scale a_t =          */
+/* fl(max|RHT(x)_t| / 127), q = rint(fl(RHT(x)_i / a_t)), and              */
+/*   y[b][r] = 0.5 * (fma chain over tiles t ascending, from +0, of          */
+/*             (float) I_t * fl(s_t * a_t)),  I_t = <codes_t, q_t> (exact).  */
+/* ------------------------------------------------------------------------ */
+int hqo_decode_codes(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk_off,
+                     const uint32_t *payload, uint64_t payload_words, const hqo_params *p, int8_t *codes,
+                     uint32_t *range_flag)
+{
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (p->dither || p->lattice == HQO_A2) return HQO_EINVAL;
+    uint32_t n = p->tile, d = lattice_dim(p->lattice);
+    uint32_t nb = (n / d) * coset_bits_per_block(p->lattice);
+    uint64_t T = p->rows * p->cols / n;
+    uint64_t C = (T + HQO_CHUNK_TILES - 1) / HQO_CHUNK_TILES;
+    uint64_t chunk_cap = ((uint64_t)HQO_CHUNK_TILES * hqo_tile_bound_bits(p) + 31) / 32;
+    int status = HQO_OK;
+    uint32_t cos[256], sym[256], zero[8] = {0};
+    *range_flag = 0;
+    for (uint64_t c = 0; c < C; c++) {
+        uint64_t w0 = chunk_off[c], w1 = chunk_off[c + 1];
+        uint64_t t0 = c * HQO_CHUNK_TILES, t1 = t0 + HQO_CHUNK_TILES;
+        if (t1 > T) t1 = T;
+        uint64_t total = 0;
+        int too_long = 0;
+        for (uint64_t t = t0; t < t1; t++) {
+            total += meta[t] >> 3;
+            if ((uint32_t)(meta[t] >> 3) > hqo_tile_bound_bits(p)) too_long = 1;
+        }
+        int chunk_bad = !(w1 >= w0 && w1 <= payload_words && w1 - w0 <= chunk_cap)
+                        || too_long || (total + 31) / 32 != w1 - w0;
+        uint64_t b = w0 * 32, bend = w1 * 32;
+        for (uint64_t t = t0; t < t1; t++) {
+            uint32_t len = meta[t] >> 3, k = meta[t] & 7u;
+            int bad = chunk_bad || step_bad(step[t]) || parse_tile(payload, b, bend, len, k, n, nb, cos, sym);
+            if (bad) status = HQO_ECORRUPT;
+            for (uint32_t blk = 0; blk < n / d; blk++) {
+                float pt[8];
+                uint32_t pc = (coset_bits_per_block(p->lattice) && !bad) ? cos[blk] : 0;
+                block_point(p->lattice, pc, bad ? zero : sym + blk * d, pt);
+                for (uint32_t i = 0; i < d; i++) {
+                    long v = lrintf(2.0f * pt[i]);
+                    if (v > 127) { v = 127; *range_flag = 1; }
+                    if (v < -127) { v = -127; *range_flag = 1; }
+                    codes[t * n + blk * d + i] = (int8_t)v;
+                }
+            }
+            b += len;
+        }
+    }
+    return status;
+}
+
+void hqo_act_quant(const float *x, uint64_t batch, uint64_t cols, uint32_t n, uint64_t seed, int8_t *q,
+                   float *scale)
+{
+    float y[256];
+    for (uint64_t b = 0; b < batch; b++)
+        for (uint64_t t = 0; t < cols / n; t++) {
+            hqo_rht_forward(x + b * cols + t * n, n, seed, y);
+            float m = 0.0f;
+            for (uint32_t i = 0; i < n; i++) m = fabsf(y[i]) > m ? fabsf(y[i]) : m;
+            float a = m / 127.0f;
+            scale[b * (cols / n) + t] = a;
+            for (uint32_t i = 0; i < n; i++) {
+                long v = a == 0.0f ? 0 : lrintf(y[i] / a);
+                q[b * cols + t * n + i] = (int8_t)(v > 127 ? 127 : (v < -127 ? -127 : v));
+            }
+        }
+}
+
+void hqo_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols, uint32_t n,
+                      const int8_t *q, const float *scale, uint64_t batch, float *y)
+{
+    uint64_t tr = cols / n;
+    for (uint64_t b = 0; b < batch; b++)
+        for (uint64_t r = 0; r < rows; r++) {
+            float acc = 0.0f;
+            for (uint64_t t = 0; t < tr; t++) {
+                int32_t I = 0;
+                for (uint32_t i = 0; i < n; i++)
+                    I += (int32_t)codes[r * cols + t * n + i] * (int32_t)q[b * cols + t * n + i];
+                float w = bf16_to_f32(step[r * tr + t]) * scale[b * tr + t];
+                acc = fmaf((float)I, w, acc);
+            }
+            y[b * rows + r] = 0.5f * acc;
+        }
+}

@@ -90,6 +90,18 @@ int hqo_encode_tiles(const void *x, const hqo_params *p, uint64_t t0, uint64_t t
 void hqo_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uint32_t x_dtype,
                 uint64_t rows, void *y, uint32_t y_dtype);
 
+/* int8 product path: a stream's codes 2P (Z, D4, E8 without dither; int8,
+ * saturated, *range_flag set if any was), the activation's per-tile RHT in
+ * int8 with fp32 scales, and y[b][r] = 0.5 * (ascending fma chain over the
+ * row's tiles of (float)<codes, q> * fl(step * scale)) */
+int hqo_decode_codes(const uint16_t *step, const uint16_t *meta, const uint32_t *chunk_off,
+                     const uint32_t *payload, uint64_t payload_words, const hqo_params *p, int8_t *codes,
+                     uint32_t *range_flag);
+void hqo_act_quant(const float *x, uint64_t batch, uint64_t cols, uint32_t n, uint64_t seed, int8_t *q,
+                   float *scale);
+void hqo_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols, uint32_t n,
+                      const int8_t *q, const float *scale, uint64_t batch, float *y);
+
 #ifdef __cplusplus
 }
 #endif

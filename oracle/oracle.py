@@ -89,6 +89,13 @@ def lib():
         L.hqo_rotate.argtypes = [vp, ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_uint32, ctypes.c_uint64, vp,
                                  ctypes.c_uint32]
         L.hqo_rotate.restype = None
+        L.hqo_decode_codes.argtypes = [vp, vp, vp, vp, ctypes.c_uint64, P(_Params), vp, P(ctypes.c_uint32)]
+        L.hqo_decode_codes.restype = ctypes.c_int
+        L.hqo_act_quant.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, vp, vp]
+        L.hqo_act_quant.restype = None
+        L.hqo_codes_matmul.argtypes = [vp, vp, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, vp, vp,
+                                       ctypes.c_uint64, vp]
+        L.hqo_codes_matmul.restype = None
         _lib = L
     return _lib
 
@@ -336,4 +343,40 @@ def rotate(Q: np.ndarray, x: np.ndarray, transpose: bool = False, out_dtype: int
     x = _as_input(x.reshape(-1, d), xdt)
     y = np.zeros(x.shape, np.float32 if out_dtype == F32 else np.uint16)
     lib().hqo_rotate(_ptr(Q), d, int(transpose), _ptr(x), xdt, x.shape[0], _ptr(y), out_dtype)
+    return y
+
+
+# ---------------------------------------------------------------- int8 product path
+def decode_codes(e: Encoded, rows: int, cols: int, tile: int, lattice, c: float, seed: int):
+    """A stream's integer codes 2P as int8 [rows][cols]: (codes, status, range_flag)."""
+    p = params(rows, cols, tile, lattice, c, seed, F32, 0)
+    codes = np.zeros((rows, cols), np.int8)
+    pay = np.ascontiguousarray(e.payload, dtype=np.uint32)
+    if pay.size == 0:
+        pay = np.zeros(1, np.uint32)
+    flag = ctypes.c_uint32(0)
+    st = lib().hqo_decode_codes(_ptr(np.ascontiguousarray(e.step)), _ptr(np.ascontiguousarray(e.meta)),
+                                _ptr(np.ascontiguousarray(e.chunk_off)), _ptr(pay), e.payload.size,
+                                ctypes.byref(p), _ptr(codes), ctypes.byref(flag))
+    return codes, st, flag.value
+
+
+def act_quant(x: np.ndarray, tile: int, seed: int):
+    """Per-tile RHT of activations x [batch][cols] (fp32) in int8 with fp32 scales."""
+    x = np.ascontiguousarray(x, np.float32)
+    B, cols = x.shape
+    q = np.zeros((B, cols), np.int8)
+    sc = np.zeros((B, cols // tile), np.float32)
+    lib().hqo_act_quant(_ptr(x), B, cols, tile, seed, _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def codes_matmul(codes: np.ndarray, step: np.ndarray, tile: int, q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """y [batch][rows] from the weight codes [rows][cols], tile steps and int8 activations."""
+    rows, cols = codes.shape
+    B = q.shape[0]
+    y = np.zeros((B, rows), np.float32)
+    lib().hqo_codes_matmul(_ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(step, np.uint16)), rows,
+                           cols, tile, _ptr(np.ascontiguousarray(q)), _ptr(np.ascontiguousarray(scale, np.float32)),
+                           B, _ptr(y))
     return y
