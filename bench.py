@@ -243,6 +243,31 @@ def all_configs(args):
         print(json.dumps(rec), flush=True)
         del xf, out, h, y, yd
 
+    # the int8 product path on one DiT layer (4096 x 16384 bf16, E8, 4 bps,
+    # n = 256) times 32 activations: codes from the decoder, the activations'
+    # int8 RHT, the int8 matrix-core product
+    cache.clear()
+    w = torch.from_numpy(workloads.dit_layer(4096, 16384, key=4, layer=0)).to(dev).to(torch.bfloat16)
+    seed = workloads.codec_seed(4, 0)
+    h = hq.encode(w, 256, "E8", 4.0, seed)
+    xa = torch.from_numpy(workloads.gaussian(32, 16384, key=77)).to(dev)
+    codes = hq.decode_codes(h)
+    q, sc = hq.act_quant(xa, 256, seed)
+    yv = hq.codes_matmul(codes, h.step, 256, q, sc)
+    d_med, _ = timed(lambda: hq.decode_codes(h, out=codes), False)
+    a_med, _ = timed(lambda: hq.act_quant(xa, 256, seed), False)
+    m_med, _ = timed(lambda: hq.codes_matmul(codes, h.step, 256, q, sc, out=yv), False)
+    torch.cuda.synchronize()
+    ref = xa.double() @ hq.decode(h).double().t()
+    rec = {"int8_product": True, "config": 4, "tensor": "DiT layer 0 x 32 activations", "lattice": "E8",
+           "bps_target": 4.0, "tile": 256, "decode_codes_us": round(1000 * d_med, 2),
+           "act_quant_us": round(1000 * a_med, 2), "codes_matmul_us": round(1000 * m_med, 2),
+           "matmul_TOPs": round(2.0 * 4096 * 16384 * 32 / (m_med / 1000) / 1e12, 2),
+           "rel_err_vs_decoded_fp64": float(((yv.double() - ref).norm() / ref.norm()).item()),
+           "status_flags": h.flags()}
+    print(json.dumps(rec), flush=True)
+    del w, h, xa, codes, q, sc, yv, ref
+
     cache.clear()
     src = torch.ones(1 << 28, dtype=torch.int32, device=dev)             # 1 GiB
     dst = torch.empty_like(src)

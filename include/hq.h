@@ -64,6 +64,7 @@ typedef enum {
 #define HQ_FLAG_NONFINITE 1u   /* encode: a tile had a non-finite energy; it was coded as zero */
 #define HQ_FLAG_CORRUPT   2u   /* decode: a tile's parsed length disagreed with meta (tile -> 0) */
 #define HQ_FLAG_NOSPACE   4u   /* encode: payload capacity exceeded (nothing written past it) */
+#define HQ_FLAG_RANGE     8u   /* decode to codes: a code 2P beyond [-127, 127] (saturated) */
 
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 typedef enum { HQ_Z = 1, HQ_A2 = 2, HQ_D4 = 4, HQ_E8 = 8 } hq_lattice;
@@ -218,6 +219,40 @@ int hq_encode_rate(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, 
  */
 int hq_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uint32_t x_dtype,
               uint64_t rows, void *y, uint32_t y_dtype, void *stream);
+
+/*
+ * int8 product path (gist.science explainer of HyperQuant, Key Contributions,
+ * "Hardware Integration": int8 matrix-core products on the post-RHT lattice
+ * output; Methodology section 2: the lattice's integer embedding).  A weight
+ * tile decodes to D H (s P) / sqrt(n), so a weight row times an activation x
+ * is the sum over tiles of s_t <P_t, RHT(x)_t>; these calls compute it with
+ * int8 operands.
+ *
+ * hq_decode_codes — as hq_decode_c (weights, kv = 0) but writes each tile's
+ *   integer codes 2P, int8 [rows][cols] (device, 16-byte aligned), for Z, D4
+ *   and E8 only (HQ_EINVAL otherwise).  Codes beyond [-127, 127] are
+ *   saturated and HQ_FLAG_RANGE is OR-ed into *status; a corrupt tile's codes
+ *   are 0 (HQ_FLAG_CORRUPT).  The tile steps stay in `step`.
+ * hq_act_quant — activations x [batch][cols] (HQ_F32 or HQ_BF16, device):
+ *   per tile of n (the weights' tile size and seed), y = the codec's RHT of
+ *   the tile, a = fl(max |y| / 127), q = rint(fl(y / a)) (0 where a = 0),
+ *   clamped to [-127, 127]; q int8 [batch][cols], a fp32 [batch][cols / n].
+ * hq_codes_matmul — y[b][r] = 0.5 * (fma chain over the row's tiles t in
+ *   ascending order, from +0, of (float) I * fl(s_t * a_bt)), I the exact
+ *   int32 <codes tile, q tile> (matrix cores).  codes and q 8-byte aligned;
+ *   y fp32 [batch][rows].
+ * All three are asynchronous on `stream`; argument errors return HQ_EINVAL
+ * before any device work.
+ */
+int hq_decode_codes(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
+                    const uint16_t *meta, const uint32_t *chunk_off, uint64_t rows, uint64_t cols,
+                    uint32_t tile, uint32_t lattice, float c, uint64_t seed, int8_t *codes,
+                    uint32_t *status, void *stream);
+int hq_act_quant(const void *x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile,
+                 uint64_t seed, int8_t *q, float *scale, void *stream);
+int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols,
+                    uint32_t tile, const int8_t *q, const float *scale, uint64_t batch, float *y,
+                    void *stream);
 
 /* message for a hq_status code (static storage) */
 const char *hq_strerror(int code);

@@ -6,4 +6,5 @@
 namespace hq {
 EncFn enc_fn_e8(uint32_t n, bool dither, bool bf16) { return enc_table<8>(n, dither, bf16); }
 DecFn dec_fn_e8(uint32_t n, bool dither) { return dec_table<8>(n, dither); }
+DecFn dec_codes_fn_e8(uint32_t n) { return dec_codes_table<8>(n); }
 }  // namespace hq

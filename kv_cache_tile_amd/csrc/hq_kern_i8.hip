@@ -1,0 +1,129 @@
+// hq_kern_i8.hip — the int8 product path on the matrix cores (gist.science
+// explainer of HyperQuant, Key Contributions, "Hardware Integration": int8
+// matrix-core products on the post-RHT lattice output; Methodology section 2:
+// the lattice's integer embedding fits 8 bits).
+//
+// A weight tile decodes to D H (s P) / sqrt(n), so a weight row times an
+// activation x is the sum over the row's tiles of s_t <P_t, RHT(x)_t>.  The
+// decoder writes the integer codes 2P (int8); act_quant_kernel rotates each
+// activation tile with the codec's RHT and quantizes it to int8 with scale
+// a_t = fl(max |RHT(x)_t| / 127); codes_matmul_kernel forms the exact int32
+// tile products on the matrix cores and accumulates
+//   y[b][r] = 0.5 * fma chain over tiles t ascending, from +0, of
+//             (float) I_t * fl(s_t * a_t)
+// in that order, so every output is bit-exact against a plain loop.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hq_device.h"
+
+namespace hq {
+
+// One workgroup of N / 2 threads per activation tile: sign diagonal (the
+// codec's sign bits of positions 0 .. n-1), the butterfly with strides 1, 2,
+// ..., n/2 in LDS, the scale fl(1/sqrt(n)), then max |y| and the int8 codes.
+template <int N>
+__global__ void __launch_bounds__(N / 2)
+act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_row, uint32_t key_sign,
+                 float inv_sqrtn, int8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float y[N];
+  __shared__ float red[N / 2];
+  const int k = threadIdx.x;
+  const uint64_t tile = blockIdx.x;                         // (b, t) row-major: tile index in the activations
+  const uint64_t base = tile * N;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int i = k + h * (N / 2);
+    float v = xbf16 ? as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] << 16)
+                    : reinterpret_cast<const float*>(x)[base + i];
+    if (pcg_hash(key_sign + (uint32_t)i) >> 31) v = -v;
+    y[i] = v;
+  }
+  __syncthreads();
+  for (int h = 1; h < N; h <<= 1) {
+    const int j = (k / h) * 2 * h + (k % h);
+    const float lo = y[j], hi = y[j + h];
+    __syncthreads();
+    y[j] = lo + hi;
+    y[j + h] = lo - hi;
+    __syncthreads();
+  }
+  const float v0 = y[k] * inv_sqrtn, v1 = y[k + N / 2] * inv_sqrtn;
+  red[k] = fmaxf(fabsf(v0), fabsf(v1));
+  __syncthreads();
+  for (int m = N / 4; m > 0; m >>= 1) {
+    if (k < m) red[k] = fmaxf(red[k], red[k + m]);
+    __syncthreads();
+  }
+  const float a = red[0] / 127.0f;
+  auto code = [&](float v) -> int8_t {
+    if (a == 0.0f) return 0;
+    float r = rintf(v / a);
+    r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+    return (int8_t)(int)r;
+  };
+  q[base + k] = code(v0);
+  q[base + k + N / 2] = code(v1);
+  if (k == 0) scale[tile] = a;
+  (void)tiles_per_row;
+}
+
+// One wave per 32 rows x 32 activations.  v_mfma_i32_32x32x16_i8 takes 8
+// codes per lane from each operand (lane l: row / activation l % 32, the
+// 8-byte half l / 32 of the 16-code step; both operands use the same split,
+// so every product is summed once), exact in int32.  Output layout: register
+// r of lane l holds row (r / 4) 8 + (l / 32) 4 + r % 4, activation l % 32.
+typedef int i8_i32x16 __attribute__((ext_vector_type(16)));
+
+template <int N>
+__global__ void __launch_bounds__(64)
+codes_matmul_kernel(const int8_t* __restrict__ codes, const uint16_t* __restrict__ step, uint64_t rows,
+                    uint64_t cols, const int8_t* __restrict__ q, const float* __restrict__ scale, uint64_t batch,
+                    float* __restrict__ y) {
+  const int lane = threadIdx.x;
+  const uint64_t r0 = (uint64_t)blockIdx.x * 32, b0 = (uint64_t)blockIdx.y * 32;
+  const uint64_t tr = cols / N;
+  const uint64_t arow = r0 + (uint64_t)(lane & 31), bcol = b0 + (uint64_t)(lane & 31);
+  const bool alive = arow < rows, blive = bcol < batch;
+  const int half = (lane >> 5) * 8;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+  for (uint64_t t = 0; t < tr; t++) {
+    i8_i32x16 I = {};
+#pragma unroll 4
+    for (int ks = 0; ks < N / 16; ks++) {
+      const uint64_t col = t * N + (uint64_t)(16 * ks + half);
+      const long av = alive ? *reinterpret_cast<const long*>(codes + arow * cols + col) : 0l;
+      const long bv = blive ? *reinterpret_cast<const long*>(q + bcol * cols + col) : 0l;
+      I = __builtin_amdgcn_mfma_i32_32x32x16_i8(av, bv, I, 0, 0, 0);
+    }
+    const float a = blive ? scale[bcol * tr + t] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const uint64_t row = r0 + (uint64_t)((i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
+      const float s = row < rows ? as_f((uint32_t)step[row * tr + t] << 16) : 0.0f;
+      acc[i] = __builtin_fmaf((float)I[i], s * a, acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const uint64_t row = r0 + (uint64_t)((i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
+    if (row < rows && blive) y[bcol * rows + row] = 0.5f * acc[i];
+  }
+}
+
+const void* act_quant_fn(uint32_t n) {
+  if (n == 64) return (const void*)act_quant_kernel<64>;
+  if (n == 128) return (const void*)act_quant_kernel<128>;
+  if (n == 256) return (const void*)act_quant_kernel<256>;
+  return nullptr;
+}
+const void* codes_matmul_fn(uint32_t n) {
+  if (n == 64) return (const void*)codes_matmul_kernel<64>;
+  if (n == 128) return (const void*)codes_matmul_kernel<128>;
+  if (n == 256) return (const void*)codes_matmul_kernel<256>;
+  return nullptr;
+}
+
+}  // namespace hq

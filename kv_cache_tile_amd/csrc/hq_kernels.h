@@ -857,7 +857,11 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
 }
 
 // Occupancy target: 7 waves per SIMD (72 VGPRs) without dither, 5 with it.
-template <int LAT, int N, bool DITHER>
+// CODES: write each tile's integer codes 2P (int8, saturated to [-127, 127]
+// with HQ_FLAG_RANGE) instead of the reconstruction, for an int8 product
+// (Z, D4, E8 without dither): the rebuild takes the step 2, and the inverse
+// RHT and the store below are skipped.
+template <int LAT, int N, bool DITHER, bool CODES = false>
 __global__ void __launch_bounds__(DecodeGeom<N>::THREADS) __attribute__((amdgpu_waves_per_eu(DITHER ? 5 : 7)))
 decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
               const uint16_t* __restrict__ step, const uint16_t* __restrict__ meta,
@@ -1085,7 +1089,8 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     //  - a +0 step: every value is a signed zero.  The rebuild takes the step
     //    1 to see each value's sign, and the signs go through the butterfly's
     //    rules for zeros (at the store). ----
-    constexpr bool kFoldScale = kPow2Scale<N> && LAT != 2 && !DITHER;
+    static_assert(!CODES || (!DITHER && LAT != 2), "integer codes: Z, D4 or E8 without dither");
+    constexpr bool kFoldScale = kPow2Scale<N> && LAT != 2 && !DITHER && !CODES;
     float a[kLaneElems];
     bool lane_ok;
     const bool zero_step = sraw == 0u;
@@ -1093,7 +1098,8 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       const float s = as_f(sraw << 16);
       uint32_t cbits = 0;
       if constexpr (CB_LANE > 0) cbits = lds_read32(stage, ok ? start + (uint32_t)q * CB_LANE : 0u);
-      const float s_lane = zero_step ? 1.0f : (lane_sign_odd(q) ? -s : s) * (kFoldScale ? inv_sqrtn : 1.0f);
+      const float s_lane = CODES ? 2.0f
+                                 : zero_step ? 1.0f : (lane_sign_odd(q) ? -s : s) * (kFoldScale ? inv_sqrtn : 1.0f);
       const uint32_t rb = ok ? start + B + (uint32_t)q * kLaneElems * k : 0u;
       uint32_t lt = (uint32_t)tid;
       opaque(lt);                                           // (an address recomputed, not spilled)
@@ -1136,6 +1142,31 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     // order: the next wait needs no store to finish)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    if constexpr (CODES) {
+      // 2P is an exact integer; an invalid tile's codes are zeros
+      if (active) {
+        if (!lane_ok && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
+        uint32_t w[8];
+        bool over = false;
+#pragma unroll
+        for (int v = 0; v < 8; v++) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int h = 0; h < 4; h++) {
+            int c = lane_ok ? (int)a[4 * v + h] : 0;
+            over = over | (c > 127) | (c < -127);
+            c = c > 127 ? 127 : (c < -127 ? -127 : c);
+            pk |= ((uint32_t)c & 0xFFu) << (8 * h);
+          }
+          w[v] = pk;
+        }
+        if (over) atomicOr(status, HQ_FLAG_RANGE);
+        uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(out) + t * N + (uint64_t)q * kLaneElems);
+        p[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        p[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      continue;
+    }
     // ---- inverse RHT and store (an invalid tile decodes to zeros) ----
     if (active) {
       if (!lane_ok) {
@@ -1210,6 +1241,12 @@ EncFn enc_table(uint32_t n, bool dither, bool bf16) {
   return enc_table_n<LAT, 256>(dither, bf16);
 }
 template <int LAT>
+DecFn dec_codes_table(uint32_t n) {
+  if (n == 64) return decode_kernel<LAT, 64, false, true>;
+  if (n == 128) return decode_kernel<LAT, 128, false, true>;
+  return decode_kernel<LAT, 256, false, true>;
+}
+template <int LAT>
 DecFn dec_table(uint32_t n, bool dither) {
   if (n == 64) return dither ? decode_kernel<LAT, 64, true> : decode_kernel<LAT, 64, false>;
   if (n == 128) return dither ? decode_kernel<LAT, 128, true> : decode_kernel<LAT, 128, false>;
@@ -1224,5 +1261,8 @@ DecFn dec_fn_z(uint32_t n, bool dither);
 DecFn dec_fn_a2(uint32_t n, bool dither);
 DecFn dec_fn_d4(uint32_t n, bool dither);
 DecFn dec_fn_e8(uint32_t n, bool dither);
+DecFn dec_codes_fn_z(uint32_t n);
+DecFn dec_codes_fn_d4(uint32_t n);
+DecFn dec_codes_fn_e8(uint32_t n);
 
 }  // namespace hq

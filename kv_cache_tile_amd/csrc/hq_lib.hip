@@ -21,6 +21,9 @@ namespace hq {
 // bytes, threads and rows per workgroup pass (null for an unsupported d)
 const void* rot_mfma_fn(uint32_t d, bool xbf16, bool ybf16, size_t* lds, uint32_t* threads,
                         uint32_t* rows_per_block);
+// hq_kern_i8.hip: the int8 product path's kernels for tile size n (null otherwise)
+const void* act_quant_fn(uint32_t n);
+const void* codes_matmul_fn(uint32_t n);
 }  // namespace hq
 
 using namespace hq;
@@ -218,11 +221,11 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
 
 int do_decode(const Plan& P, const uint32_t* payload, uint64_t payload_words, const uint16_t* step,
               const uint16_t* meta, const uint32_t* chunk_off, uint32_t dtype, uint32_t tile, uint32_t lat,
-              uint64_t seed, uint32_t kv, void* out, uint32_t* status, void* stream) {
+              uint64_t seed, uint32_t kv, void* out, uint32_t* status, void* stream, DecFn kernel = nullptr) {
   int rc;
   if (!payload || !step || !meta || !chunk_off || !status || !out) return HQ_EINVAL;
   if (((uintptr_t)out & 15) || ((uintptr_t)payload & 15)) return HQ_EINVAL;
-  DecFn fn = dec_fn(lat, tile, kv != 0);
+  DecFn fn = kernel ? kernel : dec_fn(lat, tile, kv != 0);
   const uint32_t lpt = tile / kLaneElems;
   const uint32_t tpw = (256 / lpt) < (uint32_t)kChunkTiles ? 256 / lpt : (uint32_t)kChunkTiles;
   const int block = (int)(tpw * lpt);
@@ -425,6 +428,47 @@ int hq_rotate(const float* Q, uint32_t d, uint32_t transpose, const void* x, uin
   if (rc) return rc;
   hipLaunchKernelGGL((void (*)(const float*, uint32_t, const void*, uint64_t, void*))fn, dim3(grid), dim3(threads),
                      lds, (hipStream_t)stream, Q, transpose, x, rows, y);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+int hq_decode_codes(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,
+                    const uint32_t* chunk_off, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
+                    float c, uint64_t seed, int8_t* codes, uint32_t* status, void* stream) {
+  Plan P;
+  int rc = plan_for_c(HQ_F32, rows, cols, tile, lattice, c, 0, &P);
+  if (rc) return rc;
+  DecFn fn = lattice == HQ_E8 ? dec_codes_fn_e8(tile) : lattice == HQ_D4 ? dec_codes_fn_d4(tile)
+                             : lattice == HQ_Z ? dec_codes_fn_z(tile) : nullptr;
+  if (!fn) return HQ_EINVAL;
+  return do_decode(P, payload, payload_words, step, meta, chunk_off, HQ_F32, tile, lattice, seed, 0, codes, status,
+                   stream, fn);
+}
+
+int hq_act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile, uint64_t seed,
+                 int8_t* q, float* scale, void* stream) {
+  const void* fn = act_quant_fn(tile);
+  if (!fn || (x_dtype != HQ_F32 && x_dtype != HQ_BF16) || !x || !q || !scale || cols % tile ||
+      batch * cols >= (1ull << 32))
+    return HQ_EINVAL;
+  const uint64_t tiles = batch * (cols / tile);
+  if (tiles == 0) return HQ_OK;
+  hipLaunchKernelGGL((void (*)(const void*, uint32_t, uint64_t, uint32_t, float, int8_t*, float*))fn,
+                     dim3((uint32_t)tiles), dim3(tile / 2), 0, (hipStream_t)stream, x, (uint32_t)(x_dtype == HQ_BF16),
+                     cols / tile, derive_key(seed, 0x5349474Eu), (float)(1.0 / sqrt((double)tile)), q, scale);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+int hq_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t tile,
+                    const int8_t* q, const float* scale, uint64_t batch, float* y, void* stream) {
+  const void* fn = codes_matmul_fn(tile);
+  if (!fn || !codes || !step || !q || !scale || !y || cols % tile || rows * cols >= (1ull << 32) ||
+      batch * cols >= (1ull << 32) || ((uintptr_t)codes & 7) || ((uintptr_t)q & 7))
+    return HQ_EINVAL;
+  if (rows == 0 || batch == 0) return HQ_OK;
+  hipLaunchKernelGGL((void (*)(const int8_t*, const uint16_t*, uint64_t, uint64_t, const int8_t*, const float*,
+                               uint64_t, float*))fn,
+                     dim3((uint32_t)((rows + 31) / 32), (uint32_t)((batch + 31) / 32)), dim3(64), 0,
+                     (hipStream_t)stream, codes, step, rows, cols, q, scale, batch, y);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 

@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(HERE, "libhq.so")
 
 LATTICES = {"Z": 1, "A2": 2, "D4": 4, "E8": 8}
 F32, BF16 = 0, 1
-FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE = 1, 2, 4
+FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE, FLAG_RANGE = 1, 2, 4, 8
 CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
-           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate")
+           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
+           "hq_codes_matmul")
 
 
 class HQError(RuntimeError):
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.hq_encode_rate.restype = ctypes.c_int
         L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
         L.hq_rotate.restype = ctypes.c_int
+        L.hq_decode_codes.argtypes = [vp, u64, vp, vp, vp, u64, u64, u32, u32, f32, u64, vp, vp, vp]
+        L.hq_decode_codes.restype = ctypes.c_int
+        L.hq_act_quant.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
+        L.hq_act_quant.restype = ctypes.c_int
+        L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp]
+        L.hq_codes_matmul.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_version.argtypes = []
@@ -336,3 +343,51 @@ def kv_encode_haar(x: torch.Tensor, Q: torch.Tensor, lattice: str = "E8", bps: f
 def kv_decode_haar(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     y = kv_decode(h)
     return rotate(h.extra["haar_Q"], y, transpose=True, out_dtype=h.extra["haar_out_dtype"], out=out)
+
+
+# ---------------------------------------------------------------- int8 product path
+def decode_codes(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The weights' integer codes 2P (int8 [rows][cols]) for hq_codes_matmul."""
+    if h.kv:
+        raise HQError("integer codes: weights only (the KV path is dithered)")
+    rows = 1
+    for s_ in h.shape[:-1]:
+        rows *= s_
+    cols = h.shape[-1]
+    c = h.c if h.c is not None else plan(_dtype_code(h.dtype), rows, cols, h.tile, h.lattice, h.bps).rate_constant
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.int8, device=h.payload.device)
+    _check(lib().hq_decode_codes(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
+                                 h.chunk_off.data_ptr(), rows, cols, h.tile, LATTICES[h.lattice], c, h.seed,
+                                 out.data_ptr(), h.status.data_ptr(), _stream(out.device)))
+    return out
+
+
+def act_quant(x: torch.Tensor, tile: int, seed: int) -> tuple:
+    """Per-tile RHT of activations x [batch][cols] in int8, with fp32 scales."""
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
+    B, cols = x2.shape
+    q = torch.empty((B, cols), dtype=torch.int8, device=x.device)
+    sc = torch.empty((B, cols // tile), dtype=torch.float32, device=x.device)
+    _check(lib().hq_act_quant(x2.data_ptr(), _dtype_code(x2.dtype), B, cols, tile, seed, q.data_ptr(),
+                              sc.data_ptr(), _stream(x.device)))
+    return q, sc
+
+
+def codes_matmul(codes: torch.Tensor, step: torch.Tensor, tile: int, q: torch.Tensor, scale: torch.Tensor,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [batch][rows] from int8 weight codes, their tile steps and int8 activations."""
+    rows, cols = codes.shape
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, rows), dtype=torch.float32, device=codes.device)
+    _check(lib().hq_codes_matmul(codes.data_ptr(), step.data_ptr(), rows, cols, tile, q.data_ptr(),
+                                 scale.data_ptr(), B, out.data_ptr(), _stream(codes.device)))
+    return out
+
+
+def matmul_compressed(h: HQTensor, x: torch.Tensor) -> torch.Tensor:
+    """x @ W_hat^T for compressed weights h, through the int8 product path."""
+    codes = decode_codes(h)
+    q, sc = act_quant(x, h.tile, h.seed)
+    return codes_matmul(codes, h.step, h.tile, q, sc)
