@@ -256,7 +256,8 @@ def all_configs(args):
     yv = hq.codes_matmul(codes, h.step, 256, q, sc)
     d_med, _ = timed(lambda: hq.decode_codes(h, out=codes), False)
     a_med, _ = timed(lambda: hq.act_quant(xa, 256, seed), False)
-    m_med, _ = timed(lambda: hq.codes_matmul(codes, h.step, 256, q, sc, out=yv), False)
+    wk = torch.empty(32 * 4096 * 64, dtype=torch.int32, device=dev)
+    m_med, _ = timed(lambda: hq.codes_matmul(codes, h.step, 256, q, sc, out=yv, work=wk), False)
     torch.cuda.synchronize()
     ref = xa.double() @ hq.decode(h).double().t()
     rec = {"int8_product": True, "config": 4, "tensor": "DiT layer 0 x 32 activations", "lattice": "E8",
@@ -266,7 +267,7 @@ def all_configs(args):
            "rel_err_vs_decoded_fp64": float(((yv.double() - ref).norm() / ref.norm()).item()),
            "status_flags": h.flags()}
     print(json.dumps(rec), flush=True)
-    del w, h, xa, codes, q, sc, yv, ref
+    del w, h, xa, codes, q, sc, yv, ref, wk
 
     cache.clear()
     src = torch.ones(1 << 28, dtype=torch.int32, device=dev)             # 1 GiB

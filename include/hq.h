@@ -239,8 +239,10 @@ int hq_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uin
  *   clamped to [-127, 127]; q int8 [batch][cols], a fp32 [batch][cols / n].
  * hq_codes_matmul — y[b][r] = 0.5 * (fma chain over the row's tiles t in
  *   ascending order, from +0, of (float) I * fl(s_t * a_bt)), I the exact
- *   int32 <codes tile, q tile> (matrix cores).  codes and q 8-byte aligned;
- *   y fp32 [batch][rows].
+ *   int32 <codes tile, q tile> (matrix cores, all tiles in parallel; the
+ *   chain in a second pass).  codes and q 8-byte aligned; y fp32
+ *   [batch][rows]; work: device int32 scratch of at least
+ *   4 * batch * rows * (cols / n) bytes (HQ_ENOSPC otherwise).
  * All three are asynchronous on `stream`; argument errors return HQ_EINVAL
  * before any device work.
  */
@@ -252,7 +254,7 @@ int hq_act_quant(const void *x, uint32_t x_dtype, uint64_t batch, uint64_t cols,
                  uint64_t seed, int8_t *q, float *scale, void *stream);
 int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols,
                     uint32_t tile, const int8_t *q, const float *scale, uint64_t batch, float *y,
-                    void *stream);
+                    int32_t *work, uint64_t work_bytes, void *stream);
 
 /* message for a hq_status code (static storage) */
 const char *hq_strerror(int code);

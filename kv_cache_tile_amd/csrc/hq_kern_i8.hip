@@ -7,8 +7,8 @@
 // activation x is the sum over the row's tiles of s_t <P_t, RHT(x)_t>.  The
 // decoder writes the integer codes 2P (int8); act_quant_kernel rotates each
 // activation tile with the codec's RHT and quantizes it to int8 with scale
-// a_t = fl(max |RHT(x)_t| / 127); codes_matmul_kernel forms the exact int32
-// tile products on the matrix cores and accumulates
+// a_t = fl(max |RHT(x)_t| / 127); the product forms the exact int32 tile
+// products on the matrix cores and accumulates
 //   y[b][r] = 0.5 * fma chain over tiles t ascending, from +0, of
 //             (float) I_t * fl(s_t * a_t)
 // in that order, so every output is bit-exact against a plain loop.
@@ -68,49 +68,58 @@ act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_
   (void)tiles_per_row;
 }
 
-// One wave per 32 rows x 32 activations.  v_mfma_i32_32x32x16_i8 takes 8
-// codes per lane from each operand (lane l: row / activation l % 32, the
-// 8-byte half l / 32 of the 16-code step; both operands use the same split,
-// so every product is summed once), exact in int32.  Output layout: register
-// r of lane l holds row (r / 4) 8 + (l / 32) 4 + r % 4, activation l % 32.
+// The product in two passes, so that the tiles' exact int32 products run in
+// parallel and only the fp32 chain is sequential.
+// Pass 1: one wave per (32 rows, one tile, 32 activations).
+// v_mfma_i32_32x32x16_i8 takes 8 codes per lane from each operand (lane l:
+// row / activation l % 32, the 8-byte half l / 32 of the 16-code step; both
+// operands use the same split, so every product is summed once), exact in
+// int32.  Output layout: register r of lane l holds row
+// (r / 4) 8 + (l / 32) 4 + r % 4, activation l % 32.  I goes to
+// work[t][r][b] (a store of one register is two 128-byte runs).
 typedef int i8_i32x16 __attribute__((ext_vector_type(16)));
 
 template <int N>
 __global__ void __launch_bounds__(64)
-codes_matmul_kernel(const int8_t* __restrict__ codes, const uint16_t* __restrict__ step, uint64_t rows,
-                    uint64_t cols, const int8_t* __restrict__ q, const float* __restrict__ scale, uint64_t batch,
-                    float* __restrict__ y) {
+codes_tile_products_kernel(const int8_t* __restrict__ codes, uint64_t rows, uint64_t cols,
+                           const int8_t* __restrict__ q, uint64_t batch, int32_t* __restrict__ work) {
   const int lane = threadIdx.x;
-  const uint64_t r0 = (uint64_t)blockIdx.x * 32, b0 = (uint64_t)blockIdx.y * 32;
+  const uint64_t r0 = (uint64_t)blockIdx.x * 32, t = blockIdx.y, b0 = (uint64_t)blockIdx.z * 32;
   const uint64_t tr = cols / N;
   const uint64_t arow = r0 + (uint64_t)(lane & 31), bcol = b0 + (uint64_t)(lane & 31);
   const bool alive = arow < rows, blive = bcol < batch;
   const int half = (lane >> 5) * 8;
-  float acc[16];
+  i8_i32x16 I = {};
 #pragma unroll
-  for (int i = 0; i < 16; i++) acc[i] = 0.0f;
-  for (uint64_t t = 0; t < tr; t++) {
-    i8_i32x16 I = {};
-#pragma unroll 4
-    for (int ks = 0; ks < N / 16; ks++) {
-      const uint64_t col = t * N + (uint64_t)(16 * ks + half);
-      const long av = alive ? *reinterpret_cast<const long*>(codes + arow * cols + col) : 0l;
-      const long bv = blive ? *reinterpret_cast<const long*>(q + bcol * cols + col) : 0l;
-      I = __builtin_amdgcn_mfma_i32_32x32x16_i8(av, bv, I, 0, 0, 0);
-    }
-    const float a = blive ? scale[bcol * tr + t] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const uint64_t row = r0 + (uint64_t)((i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
-      const float s = row < rows ? as_f((uint32_t)step[row * tr + t] << 16) : 0.0f;
-      acc[i] = __builtin_fmaf((float)I[i], s * a, acc[i]);
-    }
+  for (int ks = 0; ks < N / 16; ks++) {
+    const uint64_t col = t * N + (uint64_t)(16 * ks + half);
+    const long av = alive ? *reinterpret_cast<const long*>(codes + arow * cols + col) : 0l;
+    const long bv = blive ? *reinterpret_cast<const long*>(q + bcol * cols + col) : 0l;
+    I = __builtin_amdgcn_mfma_i32_32x32x16_i8(av, bv, I, 0, 0, 0);
   }
+  if (!blive) return;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const uint64_t row = r0 + (uint64_t)((i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
-    if (row < rows && blive) y[bcol * rows + row] = 0.5f * acc[i];
+    if (row < rows) work[(t * rows + row) * batch + bcol] = I[i];
   }
+}
+
+// Pass 2: one thread per output (activation index fastest, so each tile's
+// reads are contiguous), the fp32 chain over the row's tiles in ascending
+// order.
+__global__ void __launch_bounds__(256)
+codes_chain_kernel(const int32_t* __restrict__ work, const uint16_t* __restrict__ step, uint64_t rows, uint64_t tr,
+                   const float* __restrict__ scale, uint64_t batch, float* __restrict__ y) {
+  const uint64_t o = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= rows * batch) return;
+  const uint64_t r = o / batch, b = o % batch;
+  float acc = 0.0f;
+  for (uint64_t t = 0; t < tr; t++) {
+    const float w = as_f((uint32_t)step[r * tr + t] << 16) * scale[b * tr + t];
+    acc = __builtin_fmaf((float)work[(t * rows + r) * batch + b], w, acc);
+  }
+  y[b * rows + r] = 0.5f * acc;
 }
 
 const void* act_quant_fn(uint32_t n) {
@@ -119,11 +128,12 @@ const void* act_quant_fn(uint32_t n) {
   if (n == 256) return (const void*)act_quant_kernel<256>;
   return nullptr;
 }
-const void* codes_matmul_fn(uint32_t n) {
-  if (n == 64) return (const void*)codes_matmul_kernel<64>;
-  if (n == 128) return (const void*)codes_matmul_kernel<128>;
-  if (n == 256) return (const void*)codes_matmul_kernel<256>;
+const void* codes_products_fn(uint32_t n) {
+  if (n == 64) return (const void*)codes_tile_products_kernel<64>;
+  if (n == 128) return (const void*)codes_tile_products_kernel<128>;
+  if (n == 256) return (const void*)codes_tile_products_kernel<256>;
   return nullptr;
 }
+const void* codes_chain_fn() { return (const void*)codes_chain_kernel; }
 
 }  // namespace hq

@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.hq_decode_codes.restype = ctypes.c_int
         L.hq_act_quant.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
         L.hq_act_quant.restype = ctypes.c_int
-        L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp]
+        L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp, u64, vp]
         L.hq_codes_matmul.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
@@ -375,14 +375,17 @@ def act_quant(x: torch.Tensor, tile: int, seed: int) -> tuple:
 
 
 def codes_matmul(codes: torch.Tensor, step: torch.Tensor, tile: int, q: torch.Tensor, scale: torch.Tensor,
-                 out: torch.Tensor | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
     """y [batch][rows] from int8 weight codes, their tile steps and int8 activations."""
     rows, cols = codes.shape
     B = q.shape[0]
     if out is None:
         out = torch.empty((B, rows), dtype=torch.float32, device=codes.device)
+    if work is None:
+        work = torch.empty(B * rows * (cols // tile), dtype=torch.int32, device=codes.device)
     _check(lib().hq_codes_matmul(codes.data_ptr(), step.data_ptr(), rows, cols, tile, q.data_ptr(),
-                                 scale.data_ptr(), B, out.data_ptr(), _stream(codes.device)))
+                                 scale.data_ptr(), B, out.data_ptr(), work.data_ptr(), 4 * work.numel(),
+                                 _stream(codes.device)))
     return out
 
 
