@@ -240,7 +240,7 @@ int hq_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uin
  * hq_codes_matmul — y[b][r] = 0.5 * (fma chain over the row's tiles t in
  *   ascending order, from +0, of (float) I * fl(s_t * a_bt)), I the exact
  *   int32 <codes tile, q tile> (matrix cores, all tiles in parallel; the
- *   chain in a second pass).  codes and q 8-byte aligned; y fp32
+ *   chain in a second pass).  codes and q 16-byte aligned; y fp32
  *   [batch][rows]; work: device int32 scratch of at least
  *   4 * batch * rows * (cols / n) bytes (HQ_ENOSPC otherwise).
  * All three are asynchronous on `stream`; argument errors return HQ_EINVAL

@@ -71,13 +71,14 @@ act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_
 // The product in two passes, so that the tiles' exact int32 products run in
 // parallel and only the fp32 chain is sequential.
 // Pass 1: one wave per (32 rows, one tile, 32 activations).
-// v_mfma_i32_32x32x16_i8 takes 8 codes per lane from each operand (lane l:
-// row / activation l % 32, the 8-byte half l / 32 of the 16-code step; both
-// operands use the same split, so every product is summed once), exact in
-// int32.  Output layout: register r of lane l holds row
+// v_mfma_i32_32x32x32_i8 takes 16 codes per lane from each operand (lane
+// l: row / activation l % 32, the 16-byte half l / 32 of the 32-code step;
+// both operands use the same split, so every product is summed once), exact
+// in int32.  Output layout: register r of lane l holds row
 // (r / 4) 8 + (l / 32) 4 + r % 4, activation l % 32.  I goes to
 // work[t][r][b] (a store of one register is two 128-byte runs).
 typedef int i8_i32x16 __attribute__((ext_vector_type(16)));
+typedef int i8_i32x4 __attribute__((ext_vector_type(4)));
 
 template <int N>
 __global__ void __launch_bounds__(64)
@@ -88,14 +89,15 @@ codes_tile_products_kernel(const int8_t* __restrict__ codes, uint64_t rows, uint
   const uint64_t tr = cols / N;
   const uint64_t arow = r0 + (uint64_t)(lane & 31), bcol = b0 + (uint64_t)(lane & 31);
   const bool alive = arow < rows, blive = bcol < batch;
-  const int half = (lane >> 5) * 8;
+  const int half = (lane >> 5) * 16;
   i8_i32x16 I = {};
+  const i8_i32x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
-  for (int ks = 0; ks < N / 16; ks++) {
-    const uint64_t col = t * N + (uint64_t)(16 * ks + half);
-    const long av = alive ? *reinterpret_cast<const long*>(codes + arow * cols + col) : 0l;
-    const long bv = blive ? *reinterpret_cast<const long*>(q + bcol * cols + col) : 0l;
-    I = __builtin_amdgcn_mfma_i32_32x32x16_i8(av, bv, I, 0, 0, 0);
+  for (int ks = 0; ks < N / 32; ks++) {
+    const uint64_t col = t * N + (uint64_t)(32 * ks + half);
+    const i8_i32x4 av = alive ? *reinterpret_cast<const i8_i32x4*>(codes + arow * cols + col) : zero4;
+    const i8_i32x4 bv = blive ? *reinterpret_cast<const i8_i32x4*>(q + bcol * cols + col) : zero4;
+    I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, I, 0, 0, 0);
   }
   if (!blive) return;
 #pragma unroll

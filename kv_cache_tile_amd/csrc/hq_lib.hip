@@ -464,7 +464,7 @@ int hq_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, ui
                     uint64_t work_bytes, void* stream) {
   const void* fn = codes_products_fn(tile);
   if (!fn || !codes || !step || !q || !scale || !y || !work || cols % tile || rows * cols >= (1ull << 32) ||
-      batch * cols >= (1ull << 32) || ((uintptr_t)codes & 7) || ((uintptr_t)q & 7) || ((uintptr_t)work & 3))
+      batch * cols >= (1ull << 32) || ((uintptr_t)codes & 15) || ((uintptr_t)q & 15) || ((uintptr_t)work & 3))
     return HQ_EINVAL;
   const uint64_t tr = cols / tile;
   if (work_bytes < 4 * batch * rows * tr) return HQ_ENOSPC;
