@@ -117,6 +117,8 @@ codes_chain_kernel(const int32_t* __restrict__ work, const uint16_t* __restrict_
   if (o >= rows * batch) return;
   const uint64_t r = o / batch, b = o % batch;
   float acc = 0.0f;
+  // (the loads of 8 tiles issued ahead of their chain steps)
+#pragma unroll 8
   for (uint64_t t = 0; t < tr; t++) {
     const float w = as_f((uint32_t)step[r * tr + t] << 16) * scale[b * tr + t];
     acc = __builtin_fmaf((float)work[(t * rows + r) * batch + b], w, acc);
