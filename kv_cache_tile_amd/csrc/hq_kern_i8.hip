@@ -70,7 +70,8 @@ act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_
 
 // The product in two passes, so that the tiles' exact int32 products run in
 // parallel and only the fp32 chain is sequential.
-// Pass 1: one wave per (32 rows, one tile, 32 activations).
+// Pass 1: one wave per (32 rows, one tile, 32 activations), four waves to a
+// workgroup.
 // v_mfma_i32_32x32x32_i8 takes 16 codes per lane from each operand (lane
 // l: row / activation l % 32, the 16-byte half l / 32 of the 32-code step;
 // both operands use the same split, so every product is summed once), exact
@@ -81,29 +82,49 @@ typedef int i8_i32x16 __attribute__((ext_vector_type(16)));
 typedef int i8_i32x4 __attribute__((ext_vector_type(4)));
 
 template <int N>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 codes_tile_products_kernel(const int8_t* __restrict__ codes, uint64_t rows, uint64_t cols,
                            const int8_t* __restrict__ q, uint64_t batch, int32_t* __restrict__ work) {
-  const int lane = threadIdx.x;
-  const uint64_t r0 = (uint64_t)blockIdx.x * 32, t = blockIdx.y, b0 = (uint64_t)blockIdx.z * 32;
+  // a workgroup: 128 rows (a wave per 32) x one tile x 32 activations; the
+  // tile's codes and activation codes are staged in LDS with coalesced
+  // 16-byte loads (rows padded by 16 bytes against bank conflicts), the
+  // activations once for the four waves
+  constexpr int RS = N + 16;                                // LDS row stride in bytes
+  __shared__ __attribute__((aligned(16))) int8_t sa[128 * RS];
+  __shared__ __attribute__((aligned(16))) int8_t sb[32 * RS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t r0 = (uint64_t)blockIdx.x * 128, t = blockIdx.y, b0 = (uint64_t)blockIdx.z * 32;
   const uint64_t tr = cols / N;
-  const uint64_t arow = r0 + (uint64_t)(lane & 31), bcol = b0 + (uint64_t)(lane & 31);
-  const bool alive = arow < rows, blive = bcol < batch;
+  constexpr int CH = N / 16;                                // 16-byte chunks per row
+  const i8_i32x4 zero4 = {0, 0, 0, 0};
+  for (int e = tid; e < 128 * CH; e += 256) {
+    const int r = e / CH, ch = e % CH;
+    const uint64_t row = r0 + (uint64_t)r;
+    *reinterpret_cast<i8_i32x4*>(sa + r * RS + 16 * ch) =
+        row < rows ? *reinterpret_cast<const i8_i32x4*>(codes + row * cols + t * N + 16 * ch) : zero4;
+  }
+  for (int e = tid; e < 32 * CH; e += 256) {
+    const int r = e / CH, ch = e % CH;
+    const uint64_t bb = b0 + (uint64_t)r;
+    *reinterpret_cast<i8_i32x4*>(sb + r * RS + 16 * ch) =
+        bb < batch ? *reinterpret_cast<const i8_i32x4*>(q + bb * cols + t * N + 16 * ch) : zero4;
+  }
+  __syncthreads();
+  const int arow = 32 * wave + (lane & 31), bcol = lane & 31;
   const int half = (lane >> 5) * 16;
   i8_i32x16 I = {};
-  const i8_i32x4 zero4 = {0, 0, 0, 0};
 #pragma unroll
   for (int ks = 0; ks < N / 32; ks++) {
-    const uint64_t col = t * N + (uint64_t)(32 * ks + half);
-    const i8_i32x4 av = alive ? *reinterpret_cast<const i8_i32x4*>(codes + arow * cols + col) : zero4;
-    const i8_i32x4 bv = blive ? *reinterpret_cast<const i8_i32x4*>(q + bcol * cols + col) : zero4;
+    const i8_i32x4 av = *reinterpret_cast<const i8_i32x4*>(sa + arow * RS + 32 * ks + half);
+    const i8_i32x4 bv = *reinterpret_cast<const i8_i32x4*>(sb + bcol * RS + 32 * ks + half);
     I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, I, 0, 0, 0);
   }
-  if (!blive) return;
+  const uint64_t bg = b0 + (uint64_t)bcol;
+  if (bg >= batch) return;
 #pragma unroll
   for (int i = 0; i < 16; i++) {
-    const uint64_t row = r0 + (uint64_t)((i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
-    if (row < rows) work[(t * rows + row) * batch + bcol] = I[i];
+    const uint64_t row = r0 + (uint64_t)(32 * wave + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3));
+    if (row < rows) work[(t * rows + row) * batch + bg] = I[i];
   }
 }
 
@@ -132,12 +153,19 @@ const void* act_quant_fn(uint32_t n) {
   if (n == 256) return (const void*)act_quant_kernel<256>;
   return nullptr;
 }
-const void* codes_products_fn(uint32_t n) {
-  if (n == 64) return (const void*)codes_tile_products_kernel<64>;
-  if (n == 128) return (const void*)codes_tile_products_kernel<128>;
-  if (n == 256) return (const void*)codes_tile_products_kernel<256>;
-  return nullptr;
+// both passes on `stream` (shapes checked by the caller); false on a launch error
+bool launch_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t n,
+                         const int8_t* q, const float* scale, uint64_t batch, float* y, int32_t* work,
+                         hipStream_t stream) {
+  const uint64_t tr = cols / n;
+  const dim3 grid((uint32_t)((rows + 127) / 128), (uint32_t)tr, (uint32_t)((batch + 31) / 32));
+  if (n == 64) hipLaunchKernelGGL(codes_tile_products_kernel<64>, grid, dim3(256), 0, stream, codes, rows, cols, q, batch, work);
+  else if (n == 128) hipLaunchKernelGGL(codes_tile_products_kernel<128>, grid, dim3(256), 0, stream, codes, rows, cols, q, batch, work);
+  else hipLaunchKernelGGL(codes_tile_products_kernel<256>, grid, dim3(256), 0, stream, codes, rows, cols, q, batch, work);
+  if (hipGetLastError() != hipSuccess) return false;
+  hipLaunchKernelGGL(codes_chain_kernel, dim3((uint32_t)((rows * batch + 255) / 256)), dim3(256), 0, stream, work,
+                     step, rows, tr, scale, batch, y);
+  return hipGetLastError() == hipSuccess;
 }
-const void* codes_chain_fn() { return (const void*)codes_chain_kernel; }
 
 }  // namespace hq

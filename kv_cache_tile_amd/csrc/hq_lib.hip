@@ -23,8 +23,9 @@ const void* rot_mfma_fn(uint32_t d, bool xbf16, bool ybf16, size_t* lds, uint32_
                         uint32_t* rows_per_block);
 // hq_kern_i8.hip: the int8 product path's kernels for tile size n (null otherwise)
 const void* act_quant_fn(uint32_t n);
-const void* codes_products_fn(uint32_t n);
-const void* codes_chain_fn();
+bool launch_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t n,
+                         const int8_t* q, const float* scale, uint64_t batch, float* y, int32_t* work,
+                         hipStream_t stream);
 }  // namespace hq
 
 using namespace hq;
@@ -462,23 +463,16 @@ int hq_act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols,
 int hq_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t tile,
                     const int8_t* q, const float* scale, uint64_t batch, float* y, int32_t* work,
                     uint64_t work_bytes, void* stream) {
-  const void* fn = codes_products_fn(tile);
-  if (!fn || !codes || !step || !q || !scale || !y || !work || cols % tile || rows * cols >= (1ull << 32) ||
-      batch * cols >= (1ull << 32) || ((uintptr_t)codes & 15) || ((uintptr_t)q & 15) || ((uintptr_t)work & 3))
+  if ((tile != 64 && tile != 128 && tile != 256) || !codes || !step || !q || !scale || !y || !work || cols % tile ||
+      rows * cols >= (1ull << 32) || batch * cols >= (1ull << 32) || ((uintptr_t)codes & 15) ||
+      ((uintptr_t)q & 15) || ((uintptr_t)work & 3))
     return HQ_EINVAL;
   const uint64_t tr = cols / tile;
   if (work_bytes < 4 * batch * rows * tr) return HQ_ENOSPC;
   if (rows == 0 || batch == 0) return HQ_OK;
-  if ((rows + 31) / 32 > 0x7FFFFFFFull || tr > 65535 || (batch + 31) / 32 > 65535) return HQ_EINVAL;
-  hipLaunchKernelGGL((void (*)(const int8_t*, uint64_t, uint64_t, const int8_t*, uint64_t, int32_t*))fn,
-                     dim3((uint32_t)((rows + 31) / 32), (uint32_t)tr, (uint32_t)((batch + 31) / 32)), dim3(64), 0,
-                     (hipStream_t)stream, codes, rows, cols, q, batch, work);
-  if (hipGetLastError() != hipSuccess) return HQ_EHIP;
-  hipLaunchKernelGGL((void (*)(const int32_t*, const uint16_t*, uint64_t, uint64_t, const float*, uint64_t,
-                               float*))codes_chain_fn(),
-                     dim3((uint32_t)((rows * batch + 255) / 256)), dim3(256), 0, (hipStream_t)stream, work, step,
-                     rows, tr, scale, batch, y);
-  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+  if ((rows + 127) / 128 > 0x7FFFFFFFull || tr > 65535 || (batch + 31) / 32 > 65535) return HQ_EINVAL;
+  return launch_codes_matmul(codes, step, rows, cols, tile, q, scale, batch, y, work, (hipStream_t)stream) ? HQ_OK
+                                                                                                           : HQ_EHIP;
 }
 
 const char* hq_strerror(int code) {
