@@ -21,7 +21,8 @@
  *  - All tensor/buffer pointers are DEVICE pointers (hipMalloc'd or
  *    torch-owned); descriptors and sizes are host values.  `stream` is a
  *    hipStream_t passed as void* (NULL = default stream).  Every compute call
- *    is asynchronous on `stream`; buffers must stay alive until it is
+ *    but hq_encode_rate (which synchronises `stream` after each trial) is
+ *    asynchronous on `stream`; buffers must stay alive until it is
  *    synchronised.  The library allocates no device memory and keeps no
  *    pointer after returning.
  *  - Return value: 0 (HQ_OK) or a negative hq_status for argument errors
