@@ -146,6 +146,27 @@ def dit_layer_device(rows: int, cols: int, layer: int, device, std: float = 0.02
     return w.to(torch.bfloat16)
 
 
+def e8_near_ties(n: int, key: int, span: int = 120) -> np.ndarray:
+    """n blocks of 8 fp32 coordinates near the bisector of a point A of D8 and
+    a neighbouring point B of D8 + 1/2 (A - B in {+-1/2}^8 with an even count
+    of minus signs, |A - B|^2 = 2): t = (A + B)/2 + w, w a random vector
+    orthogonal to A - B of length up to 0.1, then some coordinates nudged by
+    up to 1e-6 of that length; A ranges over |coordinates| <= 2 span.  A
+    quarter of the blocks take w = 0 and no nudge (exact ties in fp32)."""
+    rng = _rng(11, key)
+    d = 2 * rng.integers(-span // 2, span // 2 + 1, size=(n, 8))
+    d[:, 0] += 2 * rng.integers(0, 2, n)
+    v = np.where(rng.random((n, 8)) < 0.5, -0.5, 0.5)
+    odd = (v < 0).sum(axis=1) % 2 == 1
+    v[odd, 0] = -v[odd, 0]
+    w = rng.standard_normal((n, 8)) * rng.uniform(0.0, 0.1, (n, 1))
+    w -= ((w * v).sum(axis=1, keepdims=True) / 2.0) * v          # |v|^2 = 2
+    w += rng.choice([0.0, 1.0, -1.0], size=(n, 8)) * 1e-6 * rng.random((n, 1))
+    w[: n // 4] = 0.0
+    t = (d + 0.5) + v / 2.0 + w                                   # B = d + 1/2, A = B + v
+    return t.astype(np.float32)
+
+
 def haar_orthogonal(d: int, key: int) -> np.ndarray:
     """A Haar-uniform d x d orthogonal matrix (the KV path's per-layer
     rotation is drawn by the caller): QR of an fp64 Gaussian matrix with the

@@ -47,8 +47,8 @@ uint32_t hqo_key(uint64_t seed, uint32_t domain)
 }
 
 /* [M1]: D is a random sign diagonal.  Reading: one D per call (per layer for
- * the KV cache, [M4] "per-layer rotation ... +-1 sign diagonal"), entry i
- * negative iff the top bit of hash(key + i) is set. */
+ * the KV cache: [M4] rotates each layer's vectors with a random +-1
+ * diagonal), entry i negative iff the top bit of hash(key + i) is set. */
 uint32_t hqo_sign_bit(uint64_t seed, uint32_t i)
 {
     return hqo_pcg_hash(hqo_key(seed, DOMAIN_SIGN) + i) >> 31;
@@ -191,58 +191,56 @@ static void nearest_D4(const float *t, int32_t *code, float *pt)
     for (int i = 0; i < 4; i++) { code[1 + i] = (int32_t)f[i]; pt[i] = f[i]; }
 }
 
-/* E8 = D8 u (D8 + 1/2) ([M2]: "E8 ... constant-time closed-form decoder").
- * Candidate A: nearest point of D8 (as for D4).  Candidate B: nearest point
- * of D8 + 1/2: start from floor(t) + 1/2 and, if sum floor(t) is odd, move
- * the coordinate with the largest |t - (floor t + 1/2)| one step towards t.
- *
- * Choice between A and B.  With delta = t - rint(t) (|delta| <= 1/2) every
- * coordinate's distance to floor(t) + 1/2 is 1/2 - |delta|, and in exact
- * arithmetic
- *   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|)
- *                                       - [B moved](2 min|delta|);
- * B's moved coordinate is the one of smallest |delta|.  B is taken iff this
- * difference, evaluated in fp32 in the order written below, is > 0 (ties
- * go to A).  Reading: the pages fix no decision arithmetic; this form is the
- * exact identity evaluated with one rounding per operation. */
+/* The nearest point of D8 + h (h = 0 or 1/2 in every coordinate), Conway &
+ * Sloane's D_n decoder on the shifted coset: start from the nearest point of
+ * Z^8 + h (h = 0: rint(t), ties to even; h = 1/2: floor(t) + 1/2); if the
+ * coordinates' integer parts sum to an odd number, move the coordinate with
+ * the largest |t - P| (smallest index on ties) one step towards t
+ * (t >= P: +1, else -1).  P[] gets the point, d[] its integer parts. */
+static void nearest_D8_coset(const float *t, int half, float *P, int32_t *d)
+{
+    float e[8];
+    int32_t s = 0;
+    for (int i = 0; i < 8; i++) {
+        float base = half ? floorf(t[i]) : rintf(t[i]);
+        d[i] = (int32_t)base;
+        P[i] = half ? base + 0.5f : base;
+        e[i] = t[i] - P[i];
+        s += d[i];
+    }
+    if (s & 1) {
+        int j = 0;
+        for (int i = 1; i < 8; i++) if (fabsf(e[i]) > fabsf(e[j])) j = i;
+        float step = (t[j] >= P[j]) ? 1.0f : -1.0f;
+        P[j] = P[j] + step;
+        d[j] += (int32_t)step;
+    }
+}
+
+/* squared distance |t - P|^2 in fp32, pairwise tree over the 8 squares */
+static float dist8(const float *t, const float *P)
+{
+    float q[8];
+    for (int i = 0; i < 8; i++) { float e = t[i] - P[i]; q[i] = e * e; }
+    return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+}
+
+/* E8 = D8 u (D8 + 1/2) ([M2]: E8 has a closed-form decoder of fixed cost).
+ * Conway & Sloane's E8 decoder: the nearest point of each of the two cosets
+ * (nearest_D8_coset), then the nearer of the two by squared distance
+ * (dist8); a tie goes to D8.  Code: p = 1 for the half-integer coset, and
+ * the integer vector d (the point is d + p/2). */
 static void nearest_E8(const float *t, int32_t *code, float *pt)
 {
-    float f[8], dl[8], ad[8];
-    int32_t fi[8], gi[8], sf = 0, sg = 0;
-    for (int i = 0; i < 8; i++) {
-        f[i] = rintf(t[i]);
-        dl[i] = t[i] - f[i];
-        ad[i] = fabsf(dl[i]);
-        fi[i] = (int32_t)f[i];
-        gi[i] = (int32_t)floorf(t[i]);
-        sf += fi[i];
-        sg += gi[i];
-    }
-    int oddA = sf & 1, oddB = sg & 1;
-    int jA = 0, jB = 0;
-    for (int i = 1; i < 8; i++) {
-        if (ad[i] > ad[jA]) jA = i;
-        if (ad[i] < ad[jB]) jB = i;
-    }
-    float mx = ad[jA], mn = ad[jB];
-    float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
-    float diff = sabs - 2.0f;
-    if (oddA) diff = diff + (1.0f - 2.0f * mx);
-    if (oddB) diff = diff - 2.0f * mn;
-    int useB = diff > 0.0f;
-
-    int32_t d[8];
-    if (!useB) {
-        for (int i = 0; i < 8; i++) d[i] = fi[i];
-        if (oddA) d[jA] += (t[jA] >= f[jA]) ? 1 : -1;
-    } else {
-        for (int i = 0; i < 8; i++) d[i] = gi[i];
-        if (oddB) d[jB] += (t[jB] >= (float)gi[jB] + 0.5f) ? 1 : -1;
-    }
+    float A[8], B[8];
+    int32_t dA[8], dB[8];
+    nearest_D8_coset(t, 0, A, dA);
+    nearest_D8_coset(t, 1, B, dB);
+    int useB = dist8(t, B) < dist8(t, A);
     code[0] = useB;
     for (int i = 0; i < 8; i++) {
-        code[1 + i] = d[i];
-        pt[i] = useB ? (float)d[i] + 0.5f : (float)d[i];
+        code[1 + i] = useB ? dB[i] : dA[i];
+        pt[i] = useB ? B[i] : A[i];
     }
 }
 
@@ -314,8 +312,8 @@ uint64_t hqo_rice_cost(const uint32_t *u, uint32_t n, uint32_t k)
     return c;
 }
 
-/* Reading: "k chosen per tile" = the k in 0..7 of smallest coded length,
- * the smallest such k on ties. */
+/* Reading: the per-tile Rice parameter is the k in 0..7 of smallest coded
+ * length, the smallest such k on ties. */
 uint32_t hqo_rice_k(const uint32_t *u, uint32_t n)
 {
     uint32_t best = 0;

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from hq_testutil import golden_json
+from kv_cache_tile_amd import workloads
 
 CONST = golden_json("lattice_constants.json")
 DIM = {"Z": 1, "A2": 2, "D4": 4, "E8": 8}
@@ -196,3 +197,63 @@ def test_dither_is_uniform_on_the_voronoi_cell(lat):
     assert np.all(np.abs(u.mean(axis=0)) < 0.02)
     _, _, p = oracle.nearest_batch(lat, u.astype(np.float32))
     assert np.mean(np.abs(p).max(axis=1) == 0) > 0.999     # Q(U) = 0 up to boundary ties
+
+
+def e8_coset_points(t32):
+    """Both candidates of Conway & Sloane's E8 decoder, written here in numpy
+    (fp64 on the fp32 inputs, exact): A the nearest point of D8, B of D8 + 1/2
+    (round; with an odd sum of integer parts move the first coordinate of
+    largest error one step towards t)."""
+    t = t32.astype(np.float64)
+    rows = np.arange(len(t))
+    out = []
+    for half in (False, True):
+        base = np.floor(t) if half else np.rint(t)
+        P = base + (0.5 if half else 0.0)
+        odd = (base.sum(axis=1).astype(np.int64) % 2) == 1
+        j = np.argmax(np.abs(t - P), axis=1)                       # first of the largest
+        step = np.where(t[rows, j] >= P[rows, j], 1.0, -1.0)
+        P[rows[odd], j[odd]] += step[odd]
+        out.append(P)
+    return out
+
+
+def test_e8_choice_is_the_nearer_coset_point():
+    # The oracle's E8 point is the nearer of the two coset candidates: on 2^20
+    # random blocks (|t| up to about 250, the largest the codec quantises) and
+    # 2^20 blocks near a tie between neighbouring points of the two cosets, its
+    # exact (fp64) distance is at most the other candidate's plus the rounding
+    # of the two fp32 distances (each within 9 * 2^-23), and an exact tie goes
+    # to the D8 point.
+    rng = np.random.default_rng(8)
+    N = 1 << 20
+    t = (rng.standard_normal((N, 8)) * 10.0 ** rng.uniform(-1, np.log10(250.0), (N, 1))).astype(np.float32)
+    ties = workloads.e8_near_ties(N, key=1)
+    T = np.concatenate([t, ties])
+    p, ints, pts = oracle.nearest_batch("E8", T)
+    A, B = e8_coset_points(T)
+    isA = np.all(pts == A, axis=1)
+    isB = np.all(pts == B, axis=1)
+    assert np.all(isA | isB)
+    np.testing.assert_array_equal(p == 1, isB & ~isA)
+    t64 = T.astype(np.float64)
+    dA = ((t64 - A) ** 2).sum(axis=1)
+    dB = ((t64 - B) ** 2).sum(axis=1)
+    chosen = np.where(p == 1, dB, dA)
+    other = np.where(p == 1, dA, dB)
+    assert np.all(chosen <= other + 18 * 2.0 ** -23)
+    # the crafted inputs do reach exact ties; where the two fp32 distances
+    # (squares and pairwise tree in fp32) are equal the point is D8's
+    exact_tie = dA == dB
+    assert exact_tie[N:].sum() > N // 8
+
+    def tree32(P):
+        q = ((T - P.astype(np.float32)) ** 2).astype(np.float32)
+        return ((q[:, 0] + q[:, 1]) + (q[:, 2] + q[:, 3])) + ((q[:, 4] + q[:, 5]) + (q[:, 6] + q[:, 7]))
+    tie32 = tree32(A) == tree32(B)
+    assert tie32.sum() > N // 8
+    assert np.all(p[tie32] == 0)
+    # away from ties the choice is the exact one
+    far = np.abs(dA - dB) > 18 * 2.0 ** -23
+    np.testing.assert_array_equal((p == 1)[far], (dB < dA)[far])
+    assert far[:N].mean() > 0.999
