@@ -291,3 +291,16 @@ def test_payload_bound_holds_on_adversarial_tiles():
             bound = oracle.tile_bound_bits(p)
             e = oracle.encode(x, n, lat, c, 0, dith)
             assert int((e.meta >> 3).max()) <= bound
+
+
+@pytest.mark.parametrize("lat", ["Z", "A2", "D4", "E8"])
+def test_reader_generator_matches_oracle_steps(lat):
+    # the reader regenerates the sign diagonal and the dither itself; the
+    # oracle's own sign bits and dither blocks agree with it (the dither up to
+    # the fp32 rounding of the A2 coordinate)
+    for seed in (0, 3, (4 << 32) | 7, 2 ** 64 - 1):
+        np.testing.assert_array_equal(hq1_reader.signs(seed, 256) < 0, oracle.sign_bits(seed, 256) == 1)
+        d = hq1_reader.DIM[lat]
+        u = hq1_reader.dither_values(lat, seed, 1000, 256)
+        ref = np.concatenate([oracle.dither_block(lat, seed, 1000 + b) for b in range(0, 256, d)])
+        np.testing.assert_allclose(u, ref, rtol=0, atol=1e-7 if lat == "A2" else 0)
