@@ -192,44 +192,53 @@ static void nearest_D4(const float *t, int32_t *code, float *pt)
 }
 
 /* The nearest point of D8 + h (h = 0 or 1/2 in every coordinate), Conway &
- * Sloane's D_n decoder on the shifted coset: start from the nearest point of
- * Z^8 + h (h = 0: rint(t), ties to even; h = 1/2: floor(t) + 1/2); if the
- * coordinates' integer parts sum to an odd number, move the coordinate with
- * the largest |t - P| (smallest index on ties) one step towards t
- * (t >= P: +1, else -1).  P[] gets the point, d[] its integer parts. */
+ * Sloane's D_n decoder on the shifted coset.  Start from the nearest point of
+ * Z^8 + h: rint(t) (ties to even) or floor(t) + 1/2.  If the coordinates'
+ * integer parts sum to an odd number, move the coordinate farthest from that
+ * start, smallest index on ties, one step towards t (t >= P: +1, else -1).
+ * Distances are compared exactly: with delta = t - rint(t) (exact in fp32),
+ * |t - rint t| = |delta| and |t - (floor t + 1/2)| = 1/2 - |delta|, so the
+ * farthest coordinate is the one of largest |delta| for h = 0 and of
+ * smallest |delta| for h = 1/2 (t - (floor t + 1/2) itself can round in fp32
+ * when |t| < 1/4).  P[] gets the point, d[] its integer parts. */
 static void nearest_D8_coset(const float *t, int half, float *P, int32_t *d)
 {
-    float e[8];
+    float ad[8];
     int32_t s = 0;
     for (int i = 0; i < 8; i++) {
-        float base = half ? floorf(t[i]) : rintf(t[i]);
+        float f = rintf(t[i]);
+        ad[i] = fabsf(t[i] - f);
+        float base = half ? floorf(t[i]) : f;
         d[i] = (int32_t)base;
         P[i] = half ? base + 0.5f : base;
-        e[i] = t[i] - P[i];
         s += d[i];
     }
     if (s & 1) {
         int j = 0;
-        for (int i = 1; i < 8; i++) if (fabsf(e[i]) > fabsf(e[j])) j = i;
+        for (int i = 1; i < 8; i++)
+            if (half ? ad[i] < ad[j] : ad[i] > ad[j]) j = i;
         float step = (t[j] >= P[j]) ? 1.0f : -1.0f;
         P[j] = P[j] + step;
         d[j] += (int32_t)step;
     }
 }
 
-/* squared distance |t - P|^2 in fp32, pairwise tree over the 8 squares */
-static float dist8(const float *t, const float *P)
+/* squared distance |t - P|^2 in fp64 (each coordinate's error and square
+ * computed in fp64 from the fp32 values; pairwise tree over the 8 squares) */
+static double dist8(const float *t, const float *P)
 {
-    float q[8];
-    for (int i = 0; i < 8; i++) { float e = t[i] - P[i]; q[i] = e * e; }
+    double q[8];
+    for (int i = 0; i < 8; i++) { double e = (double)t[i] - (double)P[i]; q[i] = e * e; }
     return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
 }
 
 /* E8 = D8 u (D8 + 1/2) ([M2]: E8 has a closed-form decoder of fixed cost).
  * Conway & Sloane's E8 decoder: the nearest point of each of the two cosets
  * (nearest_D8_coset), then the nearer of the two by squared distance
- * (dist8); a tie goes to D8.  Code: p = 1 for the half-integer coset, and
- * the integer vector d (the point is d + p/2). */
+ * (dist8); a tie goes to D8.  Reading: the pages fix no arithmetic for the
+ * comparison; fp64 keeps it exact up to a relative 2^-50 or so, far below
+ * any difference fp32 inputs produce away from an exact tie.  Code: p = 1
+ * for the half-integer coset, and the integer vector d (point d + p/2). */
 static void nearest_E8(const float *t, int32_t *code, float *pt)
 {
     float A[8], B[8];

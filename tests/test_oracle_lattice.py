@@ -201,17 +201,20 @@ def test_dither_is_uniform_on_the_voronoi_cell(lat):
 
 def e8_coset_points(t32):
     """Both candidates of Conway & Sloane's E8 decoder, written here in numpy
-    (fp64 on the fp32 inputs, exact): A the nearest point of D8, B of D8 + 1/2
-    (round; with an odd sum of integer parts move the first coordinate of
-    largest error one step towards t)."""
+    (fp64 on the fp32 inputs): A the nearest point of D8, B of D8 + 1/2
+    (round; with an odd sum of integer parts move the coordinate farthest from
+    the rounded point, the first on ties, one step towards t).  Distances to
+    the rounded point are exact here through |t - rint t|: for B the farthest
+    coordinate is the one nearest an integer."""
     t = t32.astype(np.float64)
     rows = np.arange(len(t))
+    ad = np.abs(t - np.rint(t))
     out = []
     for half in (False, True):
         base = np.floor(t) if half else np.rint(t)
         P = base + (0.5 if half else 0.0)
         odd = (base.sum(axis=1).astype(np.int64) % 2) == 1
-        j = np.argmax(np.abs(t - P), axis=1)                       # first of the largest
+        j = np.argmin(ad, axis=1) if half else np.argmax(ad, axis=1)   # the first of them
         step = np.where(t[rows, j] >= P[rows, j], 1.0, -1.0)
         P[rows[odd], j[odd]] += step[odd]
         out.append(P)
@@ -221,10 +224,9 @@ def e8_coset_points(t32):
 def test_e8_choice_is_the_nearer_coset_point():
     # The oracle's E8 point is the nearer of the two coset candidates: on 2^20
     # random blocks (|t| up to about 250, the largest the codec quantises) and
-    # 2^20 blocks near a tie between neighbouring points of the two cosets, its
-    # exact (fp64) distance is at most the other candidate's plus the rounding
-    # of the two fp32 distances (each within 9 * 2^-23), and an exact tie goes
-    # to the D8 point.
+    # 2^20 blocks near a tie between neighbouring points of the two cosets, it
+    # is one of the two candidates, its distance is at most the other's (up to
+    # fp64 rounding), and a tie goes to the D8 point.
     rng = np.random.default_rng(8)
     N = 1 << 20
     t = (rng.standard_normal((N, 8)) * 10.0 ** rng.uniform(-1, np.log10(250.0), (N, 1))).astype(np.float32)
@@ -241,19 +243,9 @@ def test_e8_choice_is_the_nearer_coset_point():
     dB = ((t64 - B) ** 2).sum(axis=1)
     chosen = np.where(p == 1, dB, dA)
     other = np.where(p == 1, dA, dB)
-    assert np.all(chosen <= other + 18 * 2.0 ** -23)
-    # the crafted inputs do reach exact ties; where the two fp32 distances
-    # (squares and pairwise tree in fp32) are equal the point is D8's
-    exact_tie = dA == dB
-    assert exact_tie[N:].sum() > N // 8
-
-    def tree32(P):
-        q = ((T - P.astype(np.float32)) ** 2).astype(np.float32)
-        return ((q[:, 0] + q[:, 1]) + (q[:, 2] + q[:, 3])) + ((q[:, 4] + q[:, 5]) + (q[:, 6] + q[:, 7]))
-    tie32 = tree32(A) == tree32(B)
-    assert tie32.sum() > N // 8
-    assert np.all(p[tie32] == 0)
-    # away from ties the choice is the exact one
-    far = np.abs(dA - dB) > 18 * 2.0 ** -23
-    np.testing.assert_array_equal((p == 1)[far], (dB < dA)[far])
-    assert far[:N].mean() > 0.999
+    assert np.all(chosen <= other + 1e-12)
+    # the crafted inputs reach exact ties, which go to D8
+    tie = np.abs(dA - dB) <= 1e-12
+    assert tie[N:].sum() > N // 8
+    assert np.all(p[tie] == 0)
+    np.testing.assert_array_equal((p == 1)[~tie], (dB < dA)[~tie])
