@@ -66,6 +66,9 @@ typedef enum {
 #define HQ_FLAG_CORRUPT   2u   /* decode: a tile's parsed length disagreed with meta (tile -> 0) */
 #define HQ_FLAG_NOSPACE   4u   /* encode: payload capacity exceeded (nothing written past it) */
 #define HQ_FLAG_RANGE     8u   /* decode to codes: a code 2P beyond [-127, 127] (saturated) */
+#define HQ_FLAG_STALL    16u   /* encode: a chunk-offset look-back gave up waiting (about a
+                                  second); the stream is not valid.  Not reached unless the
+                                  device stops running the encode's workgroups. */
 
 typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 typedef enum { HQ_Z = 1, HQ_A2 = 2, HQ_D4 = 4, HQ_E8 = 8 } hq_lattice;
@@ -99,15 +102,18 @@ int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_
  *   step, meta device, T uint16 each
  *   chunk_off  device, C+1 uint32
  *   status     device, one uint32 (flags OR-ed in)
- *   workspace  device, 8-byte aligned, workspace_bytes (>= hq_plan's) zero-filled ONCE
- *              before its first use; the kernels leave it ready for the next
- *              call.  Calls that overlap in time must not share a workspace.
+ *   workspace  device, 8-byte aligned, workspace_bytes (>= hq_plan's: 16 + 8 C)
+ *              zero-filled ONCE before its first use; the kernels leave it
+ *              ready for the next call.  Calls that overlap in time must not
+ *              share a workspace.
  * The bit stream is a pure function of (x, shape, tile, lattice, bps, seed).
- * The encode grid is persistent: its workgroups wait for one another's chunk
- * offsets, and the grid is sized (cus x occupancy) to be resident at once.
- * Do not run two encodes concurrently on one device (on different streams),
- * nor alongside a kernel that never finishes: either could keep part of the
- * grid from starting while the rest waits for it.
+ * The encode's workgroups take groups of chunks in order (a first one each,
+ * then from a counter in the workspace once all have started), and each
+ * waits only for the chunk offsets of groups taken before its own, by
+ * workgroups already running: it needs no part of its grid to be resident
+ * at once, and may run next to any other kernel, other encodes included
+ * (each with its own workspace).  A wait that lasts past about a second gives
+ * up and sets HQ_FLAG_STALL.
  */
 int hq_encode(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
               uint32_t lattice, float bps, uint64_t seed,
@@ -256,6 +262,20 @@ int hq_act_quant(const void *x, uint32_t x_dtype, uint64_t batch, uint64_t cols,
 int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols,
                     uint32_t tile, const int8_t *q, const float *scale, uint64_t batch, float *y,
                     int32_t *work, uint64_t work_bytes, void *stream);
+
+/*
+ * hq_nearest — the lattice quantiser alone (gist.science explainer of
+ * HyperQuant, Methodology section 2): for each of nblocks blocks of d = 1,
+ * 2, 4 or 8 coordinates (Z, A2, D4, E8) of t (device, fp32, [nblocks][d]),
+ * the nearest lattice point, with the encoder's own decision and tie rules
+ * (round half to even; a D_n candidate moves its first coordinate of largest
+ * rounding error towards t; E8 and A2 take the second coset only when it is
+ * strictly nearer), written as fp32 to points (device, [nblocks][d]; E8:
+ * d + p/2, A2: (m + p/2, sqrt3 (n' + p/2))).  Asynchronous on `stream`;
+ * HQ_EINVAL for another lattice, a NULL or misaligned pointer, or nblocks >=
+ * 2^40.
+ */
+int hq_nearest(uint32_t lattice, const float *t, uint64_t nblocks, float *points, void *stream);
 
 /* message for a hq_status code (static storage) */
 const char *hq_strerror(int code);

@@ -99,47 +99,55 @@ __device__ __forceinline__ void nearest_d4(const float* t, int32_t* d, uint32_t&
   p = 0;
 }
 
-// E8 = D8 u (D8 + 1/2).  With delta = t - rint(t):
-//   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|) - [B moved](2 min|delta|)
-// (exact identity; B's moved coordinate is the one of smallest |delta|),
-// evaluated in fp32 in this order; B iff > 0.
-__device__ __forceinline__ void nearest_e8(const float* t, int32_t* d, uint32_t& p) {
-  float f[8], ad[8];
-  int32_t g[8], sf = 0, sg = 0;
+// Squared distance from t to the nearest point of the coset D8 + h (h = 0,
+// or 1/2 in every coordinate: Conway & Sloane's decoder on the shifted
+// coset), in fp64 with the pairwise tree over the 8 squares.  Start from
+// rint(t) (h = 0) or floor(t) + 1/2; if the integer parts sum to an odd
+// number, move the first coordinate farthest from that start one step
+// towards t: the first of largest |t - rint t| for h = 0, of smallest for
+// h = 1/2 (|t - rint t| is exact in fp32, and the distance to floor(t) + 1/2
+// is 1/2 minus it).
+__device__ __forceinline__ double e8_coset_dist(const float* t, bool half) {
+  float P[8], ad[8], tgt = half ? 1.0f : 0.0f;
+  int32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    f[i] = __builtin_rintf(t[i]);
-    ad[i] = __builtin_fabsf(t[i] - f[i]);
-    g[i] = (int32_t)__builtin_floorf(t[i]);
-    sf += (int32_t)f[i];
-    sg += g[i];
+    const float f = __builtin_rintf(t[i]);
+    ad[i] = __builtin_fabsf(t[i] - f);
+    const float base = half ? __builtin_floorf(t[i]) : f;
+    sum += (int32_t)base;
+    P[i] = half ? base + 0.5f : base;
+    tgt = half ? __builtin_fminf(tgt, ad[i]) : __builtin_fmaxf(tgt, ad[i]);
   }
-  int jA = 0, jB = 0;
-  float mx = ad[0], mn = ad[0];
-#pragma unroll
-  for (int i = 1; i < 8; i++) {
-    if (ad[i] > mx) { mx = ad[i]; jA = i; }
-    if (ad[i] < mn) { mn = ad[i]; jB = i; }
-  }
-  float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
-  float diff = sabs - 2.0f;
-  if (sf & 1) diff = diff + (1.0f - 2.0f * mx);
-  if (sg & 1) diff = diff - 2.0f * mn;
-  const bool useB = diff > 0.0f;
+  bool seen = false;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    int32_t a = (int32_t)f[i];
-    if ((sf & 1) && i == jA) a += (t[i] >= f[i]) ? 1 : -1;
-    int32_t b = g[i];
-    if ((sg & 1) && i == jB) b += (t[i] >= (float)g[i] + 0.5f) ? 1 : -1;
-    d[i] = useB ? b : a;
+    const bool first = (sum & 1) && !seen && ad[i] == tgt;
+    seen = seen || first;
+    if (first) P[i] = P[i] + (t[i] >= P[i] ? 1.0f : -1.0f);
   }
-  p = useB ? 1u : 0u;
+  double q[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const double e = (double)t[i] - (double)P[i];
+    q[i] = e * e;
+  }
+  return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
 }
 
-// E8 straight to Rice symbols, for the encoder's quantiser: the same choice
-// and tie rules as nearest_e8 followed by block_symbols, arranged for fewer
-// operations.  With f = rint(t) and delta = t - f:
+// E8 = D8 u (D8 + 1/2) (Methodology 2): the nearer of the two cosets' nearest
+// points by squared distance in fp64 (e8_coset_dist), a tie going to D8.
+// The fast path decides through an identity instead: with delta = t - rint(t),
+//   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|) - [B moved] 2 min|delta|
+// (exact in the reals; B's moved coordinate is the one of smallest |delta|),
+// evaluated in fp32 as diff.  Every delta is exact in fp32, so diff is within
+// 10 * 2^-23 of the exact difference, and the fp64 distances are within a
+// relative 2^-50 or so of theirs: wherever |diff| > 2^-16 the two distances
+// compare as diff says.  A lane with |diff| <= 2^-16 (a near tie; rare)
+// computes the two distances themselves.
+//
+// The encoder goes straight to Rice symbols (nearest_e8_symbols), arranged
+// for fewer operations.  With f = rint(t) and delta = t - f:
 //  - floor(t) = f - [delta < 0], so the half-integer candidate's coset parity
 //    is f's parity flipped by the number of negative deltas;
 //  - the moved coordinate is the first one whose |delta| equals the max (A)
@@ -191,6 +199,11 @@ __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
   if (oddA) diff = diff + (1.0f - 2.0f * mx);
   if (oddB) diff = diff - 2.0f * mn;
   c.useB = diff > 0.0f;
+  const bool near_tie = __builtin_fabsf(diff) <= 0x1p-16f;
+  if (__any(near_tie)) {
+    asm volatile("");                                       // (rare: stays a branch)
+    if (near_tie) c.useB = e8_coset_dist(t, true) < e8_coset_dist(t, false);
+  }
   const float target = c.useB ? mn : mx;
   // (bitwise operators on the conditions: they stay lane masks)
   bool seen = false, negj = false;
@@ -260,12 +273,13 @@ __device__ __forceinline__ void nearest_a2(const float* t, int32_t* d, uint32_t&
   p = useB ? 1u : 0u;
 }
 
+// Z, A2 and D4 (E8 goes through e8_choose)
 template <int LAT>
 __device__ __forceinline__ void nearest(const float* t, int32_t* d, uint32_t& p, A2Consts k) {
+  static_assert(LAT != 8, "E8: nearest_e8_symbols / nearest_e8_point");
   if constexpr (LAT == 1) nearest_z(t, d, p);
   else if constexpr (LAT == 2) nearest_a2(t, d, p, k);
-  else if constexpr (LAT == 4) nearest_d4(t, d, p);
-  else nearest_e8(t, d, p);
+  else nearest_d4(t, d, p);
 }
 
 // lattice point (as floats) of a code (used for the dither reduction)

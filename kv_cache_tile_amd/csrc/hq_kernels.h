@@ -175,17 +175,41 @@ __device__ __forceinline__ void pack_lane_pairs(uint32_t* stage, uint32_t t0, in
   }
 }
 
-// Draw a group ticket from the counter (the first group of each workgroup is
-// its own index; the counter numbers the groups after those); the holder of
-// the last draw resets the counter and moves the epoch on, leaving the
-// workspace ready for the next call.
-__device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint32_t last_draw, uint32_t epoch) {
-  const uint32_t v = __hip_atomic_fetch_add(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (v == last_draw) {
-    __hip_atomic_store(&ws[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws[1], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Group tickets.  Workspace (32-bit words): [0..1] the event word (low
+// half: draws, high half: early exits), [2] the epoch, [64..128) and
+// [128..192) two bit arrays of started workgroups (a call of epoch e uses
+// array e & 1), then the look-back words.  Workgroup b's first group is
+// group b, with no contended atomic at start-up: it only sets its bit in the
+// started array (32 workgroups share a word).  After its first group a
+// workgroup checks the array (loaded ahead, during its group's last chunk):
+// if every workgroup of the grid has started, it draws the following groups
+// from the counter (draw v is group grid + v); if not, it leaves (an early
+// exit), so that the workgroups still waiting for room can start.  Either
+// way every group is held by a workgroup that is running, and a look-back
+// waits only for groups numbered below its own: the encode progresses
+// whatever part of the grid is resident, and next to any other kernel.
+// Each workgroup ends with exactly one terminal event, a failing draw or an
+// early exit, so the event whose result makes (exits + failing draws) equal
+// to the grid is the last use of the workspace in this call: its holder
+// resets the event word, clears the other started array for the next call
+// and moves the epoch on.  Returns the group, or 0xFFFFFFFF when the
+// workgroup is done.
+constexpr uint32_t kStartedWords = 64;                      // bits for up to 2048 workgroups
+constexpr uint32_t kStartedBase = 64, kLookBase = 192;      // word offsets in the workspace
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint64_t CG, uint32_t epoch, bool all_started) {
+  const uint32_t grid = gridDim.x;
+  const uint64_t dyn = CG - grid;                            // groups handed out by draws
+  const uint64_t add = all_started ? 1ull : (1ull << 32);
+  uint64_t* evw = reinterpret_cast<uint64_t*>(ws);
+  const uint64_t post = __hip_atomic_fetch_add(evw, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+  const uint64_t draws = (uint32_t)post, exits = post >> 32;
+  if (exits + (draws > dyn ? draws - dyn : 0ull) == grid) {
+    __hip_atomic_store(evw, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* other = ws + kStartedBase + ((epoch + 1u) & 1u) * kStartedWords;
+    for (uint32_t i = 0; i < kStartedWords; i++) __hip_atomic_store(&other[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws[2], (epoch + 1u) & kEpochMask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  return gridDim.x + v;
+  return (all_started && draws - 1 < dyn) ? grid + (uint32_t)(draws - 1) : 0xFFFFFFFFu;
 }
 
 // Sign diagonal (Methodology 1): bit i of lane q's mask is the sign of tile
@@ -213,7 +237,8 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
               uint32_t* __restrict__ payload, uint64_t cap_words,
               uint16_t* __restrict__ step_out, uint16_t* __restrict__ meta_out,
               uint32_t* __restrict__ chunk_off, uint32_t* __restrict__ status,
-              uint32_t* __restrict__ ws, uint32_t stage_words, uint32_t grp_words, uint32_t group_chunks) {
+              uint32_t* __restrict__ ws, uint32_t stage_words, uint32_t grp_words, uint32_t group_chunks,
+              uint32_t spin_limit) {
   constexpr int LPT = N / kLaneElems;                       // lanes per tile
   constexpr int D = LatticeTraits<LAT>::dim;
   constexpr int BPL = kLaneElems / D;                       // lattice blocks per lane
@@ -233,31 +258,28 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   const int tau = tid / LPT;
   const int p_lane = tid % LPT;                            // physical lane in the tile
   const int q = tile_lane<LPT>(p_lane);                     // logical lane
-  uint64_t* look = reinterpret_cast<uint64_t*>(ws + 2);     // one word per group
+  uint64_t* look = reinterpret_cast<uint64_t*>(ws + kLookBase);   // one word per group
+
+  // Tickets number groups of group_chunks consecutive chunks (take_ticket).
+  const uint64_t CG = (C + group_chunks - 1) / group_chunks;
+  if (tid == 0)
+    misc[2] = __hip_atomic_load(&ws[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
 
   // sign diagonal entries of this lane's 32 positions (Methodology 1), with
-  // the butterfly's lane sign folded in (inputs presigned per lane)
+  // the butterfly's lane sign folded in (inputs presigned per lane); the
+  // barrier inside also publishes the epoch
   const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q) ^ (lane_sign_odd(q) ? 0xFFFFFFFFu : 0u);
   uint32_t sgnw[2];
   pair_sign_words(sgn, sgnw);
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
-
-  // Tickets number groups of group_chunks consecutive chunks.  Workgroup b's
-  // first group is group b (the grid is at most the group count: no
-  // contended atomic at start-up); after that a workgroup draws tickets
-  // grid + 0, 1, 2, ... from the counter until it gets one >= the group
-  // count, and one look-back places a whole group.  The draws number exactly
-  // groups (grid - groups succeed, each workgroup's last fails), every
-  // workgroup reads the epoch before its first draw, so the holder of the
-  // very last draw (groups - 1) can reset the counter and bump the epoch for
-  // the next call.
-  const uint64_t CG = (C + group_chunks - 1) / group_chunks;
-  const uint32_t last_draw = (uint32_t)(CG - 1);
-  if (tid == 0)
-    misc[2] = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
+  const uint32_t epoch = misc[2];
+  uint32_t* started = ws + kStartedBase + (epoch & 1u) * kStartedWords;
+  // with no group left to draw (a grid as large as the group count) every
+  // draw fails: no started bits are set or read
+  bool checked = CG == gridDim.x, all_started = false;      // wave 1: the started array was read, and its verdict
+  uint32_t started_word = 0;                                // (lane i: word i, loaded ahead)
   for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
-  const uint32_t epoch = misc[2];
   uint64_t grp = blockIdx.x;
   uint64_t chunk = grp * group_chunks;
   uint32_t gi = 0, gw = 0;                                  // chunk of the group, group words staged so far
@@ -281,6 +303,11 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     }
   };
   prefetch(chunk);
+  // this workgroup has started (after the loads above, so that waiting for
+  // them does not wait for this contended atomic)
+  if (tid == 64 && !checked)
+    (void)__hip_atomic_fetch_or(&started[blockIdx.x >> 5], 1u << (blockIdx.x & 31u), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 
   // The staging area holds two group areas of grp_words (a group's worst
   // case), at 0 and at stage_words - grp_words; consecutive groups of a
@@ -301,11 +328,16 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   // predecessors per lane at once (distance d = 64 jj + lane, all loads in
   // flight together), waits until each has published, and sums the values up
   // to the nearest inclusive prefix.  Then the group's inclusive prefix, its
-  // chunks' offsets and its status; misc[3] = its first word.
+  // chunks' offsets and its status; misc[3] = its first word.  The wait is
+  // bounded (spin_limit polls): past it the group is published with the
+  // prefix found so far and HQ_FLAG_STALL, so that every later group, and
+  // the kernel, still end.
   auto place = [&]() {
     uint32_t excl = 0;
+    bool stalled = false;
     if (pgrp > 0) {
       int64_t base = (int64_t)pgrp - 1;
+      uint32_t polls = 0;
       for (;;) {
         uint64_t v[kLookJ];
 #pragma unroll
@@ -327,8 +359,10 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
             }
           }
           if (__all(done)) break;
+          if (++polls > spin_limit) { stalled = true; break; }
           __builtin_amdgcn_s_sleep(1);
         }
+        if (stalled) break;
         uint32_t first = 0xFFFFFFFFu;                        // distance of the nearest inclusive prefix
 #pragma unroll
         for (int jj = kLookJ - 1; jj >= 0; jj--) {
@@ -357,6 +391,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
       for (uint32_t i = 0; i <= pgi; i++) chunk_off[c0 + i] = excl + goff[ph * kMaxGroupChunks + i];
       if (pchunk == C - 1) chunk_off[C] = excl + pgtotal;
       if (!pgfits || (uint64_t)excl + pgtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
+      if (stalled) atomicOr(status, HQ_FLAG_STALL);
     }
   };
   // all threads, after place() and a barrier: the placed group's words out,
@@ -381,6 +416,10 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     wave_priority(quarters >= 3u ? 0u : 3u - quarters);
     const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
     if (pend && last && tid < 64) place();
+    // before the first draw: wave 1 loads the started array now, to use it
+    // after this chunk's compute
+    if (last && !checked && tid >= 64 && tid < 128 && (uint32_t)(tid - 64) < kStartedWords)
+      started_word = __hip_atomic_load(&started[tid - 64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
@@ -689,7 +728,16 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     // after the group's last chunk: the next ticket now (its reply arrives
     // during the packing)
     uint32_t next_ticket = 0;
-    if (last && tid == 64) next_ticket = take_ticket(ws, last_draw, epoch);
+    if (last && tid >= 64 && tid < 128) {
+      // every workgroup of the grid has started (wave 1: lane i checks word i)
+      if (!checked) {
+        const uint32_t i = (uint32_t)(tid - 64), g = gridDim.x;
+        const uint32_t want = 32u * i >= g ? 0u : (32u * (i + 1u) <= g ? 0xFFFFFFFFu : (1u << (g & 31u)) - 1u);
+        all_started = __all((started_word & want) == want);
+        checked = true;
+      }
+      if (tid == 64) next_ticket = take_ticket(ws, CG, epoch, all_started);
+    }
 
     // the words about to be written would meet the finished group's: place it now
     if (pend && (h ? pgtotal + 2 > base1 : gw + W + 2 > base1)) {
@@ -1221,10 +1269,37 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   }
 }
 
+// --------------------------------------------------------------------------
+// The quantiser alone (Methodology 2): the nearest lattice point of each
+// d-block of t, with the encoder's own decision and tie rules, one block per
+// thread (grid-strided).
+// --------------------------------------------------------------------------
+template <int LAT>
+__global__ void __launch_bounds__(256) nearest_kernel(const float* __restrict__ t, uint64_t nblocks,
+                                                      float* __restrict__ pt, A2Consts a2) {
+  constexpr int D = LatticeTraits<LAT>::dim;
+  for (uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += (uint64_t)gridDim.x * blockDim.x) {
+    float v[D], p[D];
+#pragma unroll
+    for (int i = 0; i < D; i++) v[i] = t[b * D + i];
+    if constexpr (LAT == 8) {
+      nearest_e8_point(v, p);
+    } else {
+      int32_t d[D];
+      uint32_t c;
+      nearest<LAT>(v, d, c, a2);
+      code_point<LAT>(d, c, p, a2);
+    }
+#pragma unroll
+    for (int i = 0; i < D; i++) pt[b * D + i] = p[i];
+  }
+}
+using NearFn = void (*)(const float*, uint64_t, float*, A2Consts);
+
 // ---- per-lattice kernel tables (defined in hq_kern_<lattice>.hip) ----------
 using EncFn = void (*)(const void*, uint32_t, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t,
                        A2Consts, uint32_t*, uint64_t, uint16_t*, uint16_t*, uint32_t*, uint32_t*, uint32_t*,
-                       uint32_t, uint32_t, uint32_t);
+                       uint32_t, uint32_t, uint32_t, uint32_t);
 using DecFn = void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
                        uint64_t, float, uint32_t, uint32_t, A2Consts, void*, uint32_t, uint32_t*, uint32_t,
                        uint32_t, uint32_t);
@@ -1261,6 +1336,10 @@ DecFn dec_fn_z(uint32_t n, bool dither);
 DecFn dec_fn_a2(uint32_t n, bool dither);
 DecFn dec_fn_d4(uint32_t n, bool dither);
 DecFn dec_fn_e8(uint32_t n, bool dither);
+NearFn near_fn_z();
+NearFn near_fn_a2();
+NearFn near_fn_d4();
+NearFn near_fn_e8();
 DecFn dec_codes_fn_z(uint32_t n);
 DecFn dec_codes_fn_d4(uint32_t n);
 DecFn dec_codes_fn_e8(uint32_t n);

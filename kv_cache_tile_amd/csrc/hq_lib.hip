@@ -90,6 +90,9 @@ struct Plan {
   float c;
 };
 
+// the encode look-back's bound on polls of an unpublished predecessor
+constexpr uint32_t kSpinLimit = 1u << 20;
+
 // closed-loop rate: targets accepted, tolerance in bits per scalar, most encodes
 constexpr float kRateMin = 1.0f, kRateMax = 8.0f;
 constexpr double kRateTol = 0.01;
@@ -112,7 +115,7 @@ int plan_for_c(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint
   P->c = c;
   P->chunk_words = (uint32_t)(((uint64_t)kChunkTiles * bound + 31) / 32) + 1;   // one chunk, word-aligned
   P->cap_words = (P->T * bound + 31) / 32 + P->C;
-  P->ws_bytes = 8 + 8 * P->C;
+  P->ws_bytes = 4 * kLookBase + 8 * P->C;
   return HQ_OK;
 }
 
@@ -140,6 +143,13 @@ DecFn dec_fn(uint32_t lat, uint32_t n, bool dither) {
     default: return dec_fn_e8(n, dither);
   }
 }
+
+// LDS is granted to a workgroup in blocks of a few hundred bytes: on MI355X
+// five workgroups of exactly a fifth of a CU's 160 KB (32768 bytes) do not fit
+// together, although the occupancy query counts five; five of 32000 bytes do.
+// Per-workgroup LDS budgets derived from a CU share are rounded down to this
+// grain (a multiple of 320, 640 and 1280 bytes).
+constexpr size_t kLdsGrain = 1280;
 
 int grid_for(const void* fn, int block, size_t lds, uint64_t chunks, int* grid) {
   int dev = 0, cus = 0, per = 0;
@@ -173,6 +183,7 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
     return HQ_EHIP;
   size_t lds_cap = per_regs > 0 ? (size_t)lds_cu / (size_t)per_regs : (size_t)max_lds;
   if (lds_cap > (size_t)max_lds) lds_cap = (size_t)max_lds;
+  lds_cap = lds_cap / kLdsGrain * kLdsGrain;
   const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks;
   const size_t avail = lds_cap / 4 > fixed_words ? lds_cap / 4 - fixed_words : 0;
   uint32_t group = kMaxGroupChunks, grp_words = 0;
@@ -211,13 +222,29 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   }
   grp_words = group * P.chunk_words + 4;
   const uint64_t groups = (P.C + group - 1) / group;
-  const int grid = groups < (uint64_t)grid_full ? (int)groups : grid_full;
+  if (grid_full > (int)(32 * kStartedWords)) grid_full = (int)(32 * kStartedWords);   // the started array's size
+  int grid = groups < (uint64_t)grid_full ? (int)groups : grid_full;
+  // a grid of a given size, up to the group count, on request (tests use
+  // one several times larger than can be resident at once)
+  if (const char* e = getenv("HQ_ENCODE_GRID")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) grid = (uint64_t)v < groups ? (int)v : (int)groups;
+    if (grid > (int)(32 * kStartedWords)) grid = (int)(32 * kStartedWords);
+  }
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   const float inv_n = 1.0f / (float)tile;   // exact: tile is a power of two
+  // polls of a look-back before it gives up (HQ_FLAG_STALL): each poll waits
+  // on a device-scope load, so the default is about a second, far beyond any
+  // wait for a running predecessor; tests lower it to reach the flag
+  uint32_t spin_limit = kSpinLimit;
+  if (const char* e = getenv("HQ_ENCODE_SPIN_LIMIT")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 0 && v < (long)kSpinLimit) spin_limit = (uint32_t)v;
+  }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, x, (uint32_t)(dtype == HQ_BF16), P.T, P.C, P.c, inv_sqrtn, inv_n,
                      derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, payload, cap, step, meta,
-                     chunk_off, status, (uint32_t*)ws, stage_words, grp_words, group);
+                     chunk_off, status, (uint32_t*)ws, stage_words, grp_words, group, spin_limit);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
@@ -473,6 +500,20 @@ int hq_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, ui
   if ((rows + 127) / 128 > 0x7FFFFFFFull || tr > 65535 || (batch + 31) / 32 > 65535) return HQ_EINVAL;
   return launch_codes_matmul(codes, step, rows, cols, tile, q, scale, batch, y, work, (hipStream_t)stream) ? HQ_OK
                                                                                                            : HQ_EHIP;
+}
+
+int hq_nearest(uint32_t lattice, const float* t, uint64_t nblocks, float* points, void* stream) {
+  NearFn fn = lattice == HQ_Z ? near_fn_z() : lattice == HQ_A2 ? near_fn_a2() : lattice == HQ_D4 ? near_fn_d4()
+            : lattice == HQ_E8 ? near_fn_e8() : nullptr;
+  if (!fn || !t || !points || ((uintptr_t)t & 3) || ((uintptr_t)points & 3) || nblocks >= (1ull << 40))
+    return HQ_EINVAL;
+  if (nblocks == 0) return HQ_OK;
+  int grid;
+  int rc = grid_for((const void*)fn, 256, 0, (nblocks + 255) / 256, &grid);
+  if (rc) return rc;
+  A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, t, nblocks, points, a2);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
 const char* hq_strerror(int code) {

@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(HERE, "libhq.so")
 
 LATTICES = {"Z": 1, "A2": 2, "D4": 4, "E8": 8}
 F32, BF16 = 0, 1
-FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE, FLAG_RANGE = 1, 2, 4, 8
+FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE, FLAG_RANGE, FLAG_STALL = 1, 2, 4, 8, 16
 CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
            "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
-           "hq_codes_matmul")
+           "hq_codes_matmul", "hq_nearest")
 
 
 class HQError(RuntimeError):
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.hq_act_quant.restype = ctypes.c_int
         L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp, u64, vp]
         L.hq_codes_matmul.restype = ctypes.c_int
+        L.hq_nearest.argtypes = [u32, vp, u64, vp, vp]
+        L.hq_nearest.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
         L.hq_strerror.restype = ctypes.c_char_p
         L.hq_version.argtypes = []
@@ -121,10 +123,11 @@ _workspaces: dict = {}
 
 
 def workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised encode workspace, reused across calls on a device
-    (calls that overlap in time on different streams must not share one)."""
+    """A zero-initialised encode workspace, reused across the calls made on
+    one stream of a device (calls on different streams may overlap in time,
+    so each stream has its own)."""
     device = torch.device(device)
-    key = (device.index if device.index is not None else torch.cuda.current_device())
+    key = (device.index if device.index is not None else torch.cuda.current_device(), _stream(device))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
@@ -394,3 +397,17 @@ def matmul_compressed(h: HQTensor, x: torch.Tensor) -> torch.Tensor:
     codes = decode_codes(h)
     q, sc = act_quant(x, h.tile, h.seed)
     return codes_matmul(codes, h.step, h.tile, q, sc)
+
+
+# ---------------------------------------------------------------- the quantiser alone
+def nearest(lattice: str, t: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Nearest lattice points of the d-blocks of t (fp32 [..., d] on a GPU), with
+    the encoder's decision and tie rules; returns fp32 points of t's shape."""
+    if not t.is_cuda or t.dtype != torch.float32:
+        raise HQError("nearest needs an fp32 GPU tensor")
+    d = LATTICES[lattice]
+    t2 = t.reshape(-1, d).contiguous()
+    if out is None:
+        out = torch.empty(t.shape, dtype=torch.float32, device=t.device)
+    _check(lib().hq_nearest(LATTICES[lattice], t2.data_ptr(), t2.shape[0], out.data_ptr(), _stream(t.device)))
+    return out

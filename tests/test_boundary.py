@@ -68,7 +68,7 @@ def test_plan_sizes(lib):
     rc, T, C, cap, ws, bound, c = plan(lib)
     assert rc == OK
     assert T == 4096 * 16384 // 256 and C == (T + 63) // 64
-    assert ws == 8 + 8 * C                      # ticket, epoch, one look-back word per group (<= C)
+    assert ws == 768 + 8 * C                    # event word, epoch, started bits, a look-back word per group (<= C)
     assert cap >= (T * bound + 31) // 32        # every tile at its worst case fits
     assert 256 * 4 < bound < 256 * 8            # a tile's worst case lies above the 4 bps target
     assert 0.1 < c < 1.0
