@@ -280,16 +280,27 @@ def _rows_cols(x: torch.Tensor, tile: int, kv: bool):
     return x2, x2.shape[0], x2.shape[1]
 
 
-def encode_c(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int = 0, kv: bool = False) -> HQTensor:
-    """Encode with an explicit rate constant c (step = bf16(rms * c)); KV: tile = head_dim."""
+def encode_c(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int = 0, kv: bool = False,
+             out: HQTensor | None = None, zero_status: bool = True) -> HQTensor:
+    """Encode with an explicit rate constant c (step = bf16(rms * c)); KV: tile = head_dim.
+    With `out` (for instance the result of encode_rate on this tensor), its
+    buffers are reused and it is returned with its constant set to c."""
     x2, rows, cols = _rows_cols(x, tile, kv)
     dt = _dtype_code(x2.dtype)
     p = plan_c(dt, rows, cols, tile, lattice, c, kv)
-    payload, step, meta, off, status = _alloc(p, x.device)
+    if out is not None:
+        payload, step, meta, off, status = out.payload, out.step, out.meta, out.chunk_off, out.status
+        if zero_status:
+            status.zero_()
+    else:
+        payload, step, meta, off, status = _alloc(p, x.device)
     ws = workspace(x.device, p.workspace_bytes)
     _check(lib().hq_encode_c(x2.data_ptr(), dt, rows, cols, tile, LATTICES[lattice], float(c), seed, int(kv),
                              payload.data_ptr(), payload.numel(), step.data_ptr(), meta.data_ptr(), off.data_ptr(),
                              status.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x.device)))
+    if out is not None:
+        out.c = float(c)
+        return out
     return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float("nan"), seed,
                     kv, c=float(c))
 

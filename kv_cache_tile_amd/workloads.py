@@ -56,19 +56,22 @@ def gaussian_outlier_channels(rows: int, cols: int, key: int, std: float = 0.02,
     return w.astype(np.float32)
 
 
+def kv_cache_entry(b: int, heads: int, seq: int, head_dim: int, key: int, which: str) -> np.ndarray:
+    """Batch entry b [H, S, D] of kv_cache (each entry has a key of its own, so
+    one can be drawn alone).  fp32."""
+    sub = 0 if which == "K" else 1
+    v = _rng(key, sub, b).standard_normal((heads, seq, head_dim))
+    if which == "K":
+        v *= _rng(key, 0, 99).lognormal(0.0, 1.0, size=(heads, head_dim))[:, None, :]
+    return v.astype(np.float32)
+
+
 def kv_cache(batch: int, heads: int, seq: int, head_dim: int, key: int, which: str) -> np.ndarray:
     """KV cache [B, H, S, D]: V ~ N(0,1); K ~ N(0,1) * scale[h, d] with a
     per-channel outlier scale ~ LogNormal(0, 1).  Drawn per batch entry.  fp32."""
-    sub = 0 if which == "K" else 1
     out = np.empty((batch, heads, seq, head_dim), np.float32)
-    scale = None
-    if which == "K":
-        scale = _rng(key, 0, 99).lognormal(0.0, 1.0, size=(heads, head_dim))
     for b in range(batch):
-        v = _rng(key, sub, b).standard_normal((heads, seq, head_dim))
-        if scale is not None:
-            v *= scale[:, None, :]
-        out[b] = v
+        out[b] = kv_cache_entry(b, heads, seq, head_dim, key, which)
     return out
 
 

@@ -438,6 +438,7 @@ static int check_params(const hqo_params *p)
     if (p->dither > 1) return HQO_EINVAL;
     if (p->rows == 0 || p->cols == 0 || p->cols % p->tile) return HQO_EINVAL;
     if (p->rows * p->cols >= (1ull << 32)) return HQO_EINVAL;
+    if (p->tile_base > (1ull << 32) || p->tile_base * p->tile + p->rows * p->cols > (1ull << 32)) return HQO_EINVAL;
     if (!hqo_tile_bound_bits(p)) return HQO_EINVAL;
     return HQO_OK;
 }
@@ -486,7 +487,7 @@ static void encode_tile(const void *x, const hqo_params *p, uint64_t t, tile_cod
     if (p->dither) {                                          /* [M4] t + U */
         for (uint32_t b = 0; b < n; b += d) {
             float u[8];
-            hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + b), u);
+            hqo_dither_block(p->lattice, p->seed, (uint32_t)((p->tile_base + t) * n + b), u);
             for (uint32_t i = 0; i < d; i++) tt[b + i] = tt[b + i] + u[i];
         }
     }
@@ -634,7 +635,7 @@ static void rebuild_tile(const hqo_params *p, uint64_t t, int bad, uint16_t step
         block_point(p->lattice, pc, bad ? zero : sym + blk * d, pt);
         if (p->dither && !bad) {
             float u[8];
-            hqo_dither_block(p->lattice, p->seed, (uint32_t)(t * n + blk * d), u);
+            hqo_dither_block(p->lattice, p->seed, (uint32_t)((p->tile_base + t) * n + blk * d), u);
             for (uint32_t i = 0; i < d; i++) pt[i] = pt[i] - u[i];
         }
         for (uint32_t i = 0; i < d; i++) v[blk * d + i] = pt[i] * s;

@@ -40,6 +40,11 @@ typedef struct {
     float    c;        /* rate constant: step = bf16(rms * c) */
     uint32_t pad_;
     uint64_t seed;
+    uint64_t tile_base; /* global index of the first tile: the dither of a KV
+                           coordinate is indexed by its place in the whole
+                           tensor, so a slice of tiles [b, b + T) of a larger
+                           tensor is encoded (or decoded) as a tensor of its
+                           own with tile_base = b; 0 for a whole tensor */
 } hqo_params;
 
 /* ---- generator ---------------------------------------------------------- */

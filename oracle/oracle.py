@@ -44,7 +44,7 @@ class _Params(ctypes.Structure):
                 ("rows", ctypes.c_uint64), ("cols", ctypes.c_uint64),
                 ("lattice", ctypes.c_uint32), ("dither", ctypes.c_uint32),
                 ("c", ctypes.c_float), ("pad_", ctypes.c_uint32),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("tile_base", ctypes.c_uint64)]
 
 
 _lib = None
@@ -105,10 +105,10 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def params(rows, cols, tile, lattice, c, seed, dtype=BF16, dither=0) -> _Params:
+def params(rows, cols, tile, lattice, c, seed, dtype=BF16, dither=0, tile_base=0) -> _Params:
     lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
     return _Params(dtype=dtype, tile=tile, rows=rows, cols=cols, lattice=lat,
-                   dither=int(dither), c=float(np.float32(c)), pad_=0, seed=seed)
+                   dither=int(dither), c=float(np.float32(c)), pad_=0, seed=seed, tile_base=tile_base)
 
 
 @dataclass
@@ -215,12 +215,14 @@ def _as_input(x: np.ndarray, dtype: int) -> np.ndarray:
     return np.ascontiguousarray(x)
 
 
-def encode(x: np.ndarray, tile: int, lattice, c: float, seed: int, dither: int = 0) -> Encoded:
-    """x: 2-D float32 array, or uint16 array holding bf16 bit patterns."""
+def encode(x: np.ndarray, tile: int, lattice, c: float, seed: int, dither: int = 0, tile_base: int = 0) -> Encoded:
+    """x: 2-D float32 array, or uint16 array holding bf16 bit patterns.  With
+    tile_base, x is the slice of tiles [tile_base, ...) of a larger tensor
+    (the dither is indexed by the global coordinate)."""
     dtype = F32 if x.dtype == np.float32 else BF16
     x = _as_input(x, dtype)
     rows, cols = x.shape
-    p = params(rows, cols, tile, lattice, c, seed, dtype, dither)
+    p = params(rows, cols, tile, lattice, c, seed, dtype, dither, tile_base)
     cap = lib().hqo_payload_cap_words(ctypes.byref(p))
     if cap == 0:
         raise ValueError("configuration rejected by the oracle")
@@ -237,9 +239,9 @@ def encode(x: np.ndarray, tile: int, lattice, c: float, seed: int, dither: int =
 
 
 def decode(e: Encoded, rows: int, cols: int, tile: int, lattice, c: float, seed: int,
-           dtype: int = F32, dither: int = 0):
+           dtype: int = F32, dither: int = 0, tile_base: int = 0):
     """Returns (x_hat, status); x_hat float32, or uint16 bf16 bits if dtype == BF16."""
-    p = params(rows, cols, tile, lattice, c, seed, dtype, dither)
+    p = params(rows, cols, tile, lattice, c, seed, dtype, dither, tile_base)
     out = np.zeros((rows, cols), np.float32 if dtype == F32 else np.uint16)
     pay = np.ascontiguousarray(e.payload, dtype=np.uint32)
     if pay.size == 0:
