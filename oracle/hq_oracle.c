@@ -223,29 +223,40 @@ static void nearest_D8_coset(const float *t, int half, float *P, int32_t *d)
     }
 }
 
-/* squared distance |t - P|^2 in fp64 (each coordinate's error and square
- * computed in fp64 from the fp32 values; pairwise tree over the 8 squares) */
-static double dist8(const float *t, const float *P)
-{
-    double q[8];
-    for (int i = 0; i < 8; i++) { double e = (double)t[i] - (double)P[i]; q[i] = e * e; }
-    return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-}
-
 /* E8 = D8 u (D8 + 1/2) ([M2]: E8 has a closed-form decoder of fixed cost).
- * Conway & Sloane's E8 decoder: the nearest point of each of the two cosets
- * (nearest_D8_coset), then the nearer of the two by squared distance
- * (dist8); a tie goes to D8.  Reading: the pages fix no arithmetic for the
- * comparison; fp64 keeps it exact up to a relative 2^-50 or so, far below
- * any difference fp32 inputs produce away from an exact tie.  Code: p = 1
- * for the half-integer coset, and the integer vector d (point d + p/2). */
+ * Conway & Sloane's E8 decoder: the nearest point A of D8 and B of D8 + 1/2
+ * (nearest_D8_coset), then the nearer of the two.  Reading: the pages fix no
+ * arithmetic for the comparison.  With delta = t - rint(t), exact in fp32,
+ * the difference of the squared distances is, in exact arithmetic,
+ *   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|)
+ *                                       - [B moved](2 min|delta|)
+ * (every coordinate is |delta| from rint(t) and 1/2 - |delta| from
+ * floor(t) + 1/2; a moved coordinate is 1 - |delta| or 1/2 + |delta| away).
+ * B is taken iff this, evaluated in fp32 in the order written, is > 0 (ties
+ * go to D8): a fixed cost, and within 10 * 2^-23 of the exact difference,
+ * which the tests check against both candidates' fp64 distances. */
 static void nearest_E8(const float *t, int32_t *code, float *pt)
 {
     float A[8], B[8];
-    int32_t dA[8], dB[8];
+    int32_t dA[8], dB[8], sf = 0, sg = 0;
     nearest_D8_coset(t, 0, A, dA);
     nearest_D8_coset(t, 1, B, dB);
-    int useB = dist8(t, B) < dist8(t, A);
+    float ad[8];
+    for (int i = 0; i < 8; i++) {
+        ad[i] = fabsf(t[i] - rintf(t[i]));
+        sf += (int32_t)rintf(t[i]);
+        sg += (int32_t)floorf(t[i]);
+    }
+    float mx = ad[0], mn = ad[0];
+    for (int i = 1; i < 8; i++) {
+        if (ad[i] > mx) mx = ad[i];
+        if (ad[i] < mn) mn = ad[i];
+    }
+    float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
+    float diff = sabs - 2.0f;
+    if (sf & 1) diff = diff + (1.0f - 2.0f * mx);
+    if (sg & 1) diff = diff - 2.0f * mn;
+    int useB = diff > 0.0f;
     code[0] = useB;
     for (int i = 0; i < 8; i++) {
         code[1 + i] = useB ? dB[i] : dA[i];
