@@ -27,6 +27,10 @@ METRIC = "encode/decode GB/s of bf16 input (E8, 4 bps) at 1 GPU; % of HBM peak"
 KERNEL_SOURCES = ("kv_cache_tile_amd/csrc/hq_lib.hip", "kv_cache_tile_amd/csrc/hq_kernels.h",
                   "kv_cache_tile_amd/csrc/hq_device.h", "kv_cache_tile_amd/csrc/hq_kern_e8.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_hbm_traffic.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_counters.json")
+# vector instruction issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64
+# instruction takes a SIMD 4 cycles; no packed forms)
+VALU_PEAK = 256 * 4 * 16 * 2.4e9
 
 
 def kernel_source_digest() -> str:
@@ -54,6 +58,45 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def measured_valu(kernel: str):
+    """SQ_INSTS_VALU (wave instructions) per launch of `kernel` from the
+    committed counter summary, or None if absent or stale."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("valu_insts_per_launch")
+
+
+def roofline(kernel: str, us: float, alg: float, numel: int) -> dict:
+    """The kernel against its binding roof.  HBM: algorithmic bytes per launch
+    over its duration against 8 TB/s.  Vector issue: the counted VALU
+    instructions (64 lanes each) over the same duration against VALU_PEAK.
+    The bound is the roof the kernel is nearer; without current counters it
+    is HBM's."""
+    gbps = alg / (us * 1e-6) / 1e9
+    hbm = {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "traffic": measured_traffic(kernel), "algorithmic_bytes_per_launch": alg}
+    rec = {"kernel": kernel, "avg_launch_us": round(us, 2)}
+    insts = measured_valu(kernel)
+    if insts is None:
+        rec.update(bound="hbm", bound_source="no current VALU counters", **hbm)
+        return rec
+    rate = 64.0 * insts / (us * 1e-6)
+    valu = {"achieved": round(rate / 1e12, 2), "peak": round(VALU_PEAK / 1e12, 2), "unit": "T VALU lane-instr/s",
+            "frac": round(rate / VALU_PEAK, 4), "valu_per_scalar": round(64.0 * insts / numel, 2)}
+    if valu["frac"] > hbm["frac"]:
+        rec.update(bound="alu", bound_source="counters: VALU issue nearer its roof than HBM", **valu,
+                   traffic=hbm.pop("traffic"), hbm=hbm)
+    else:
+        rec.update(bound="hbm", bound_source="counters: HBM nearer its roof than VALU issue", **hbm, valu=valu)
+    return rec
+
+
 def algorithmic_bytes(numel: int, tiles: int, chunks: int, bps: float) -> float:
     """Bytes one encode (or decode) launch must move: the bf16 tensor (2 B per
     scalar), the payload at the target rate (bps/8 B per scalar), step + meta
@@ -61,27 +104,45 @@ def algorithmic_bytes(numel: int, tiles: int, chunks: int, bps: float) -> float:
     return numel * (2.0 + bps / 8.0) + 4.0 * tiles + 4.0 * (chunks + 1)
 
 
-def cpu_baseline(layers_host, rows, cols, tile, bps, seed_of, c):
-    """The oracle as it stands, single-threaded on this host, on a bounded
-    sample: encode + decode of the given layers."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layers_host, rows, cols, tile, seed_of, c_of):
+    """The oracle as it stands, single-threaded and pinned to one host core,
+    on a bounded sample: encode + decode of the given layers, each at its
+    closed-loop rate constant."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     oracle.build(force=False)
-    t_enc = t_dec = 0.0
-    n = 0
-    for li, xb in layers_host:
-        t0 = time.perf_counter()
-        e = oracle.encode(xb, tile, "E8", c, seed_of(li))
-        t1 = time.perf_counter()
-        oracle.decode(e, rows, cols, tile, "E8", c, seed_of(li), oracle.BF16)
-        t2 = time.perf_counter()
-        t_enc += t1 - t0
-        t_dec += t2 - t1
-        n += xb.size
+    allowed = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {allowed[0]})                  # this thread, one core
+    try:
+        t_enc = t_dec = 0.0
+        n = 0
+        for li, xb in layers_host:
+            t0 = time.perf_counter()
+            e = oracle.encode(xb, tile, "E8", c_of(li), seed_of(li))
+            t1 = time.perf_counter()
+            oracle.decode(e, rows, cols, tile, "E8", c_of(li), seed_of(li), oracle.BF16)
+            t2 = time.perf_counter()
+            t_enc += t1 - t0
+            t_dec += t2 - t1
+            n += xb.size
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     gb = 2.0 * n / 1e9
     return {"value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "pinned_core": allowed[0], "cores_available": len(allowed), "nproc": os.cpu_count(),
+            "cpu_model": cpu_model(),
             "sample": f"{len(layers_host)} of 48 layers ({n} scalars), encode {gb / t_enc:.4f} GB/s, "
-                      f"decode {gb / t_dec:.4f} GB/s, {t_enc + t_dec:.1f} s"}
+                      f"decode {gb / t_dec:.4f} GB/s, {t_enc + t_dec:.1f} s on one pinned core"}
 
 
 def config_runs():
@@ -309,7 +370,13 @@ def main():
     seed_of = lambda l: (4 << 32) | l  # noqa: E731
     p = hq.plan(hq.BF16, rows, cols, tile, lat, bps)
     xs = [workloads.dit_layer_device(rows, cols, l, dev) for l in range(L)]
-    hs = [hq.encode(xs[l], tile, lat, bps, seed_of(l)) for l in range(L)]
+    # closed-loop rate (the realized-rate claim of the explainer's Methodology
+    # section 3): each layer's rate constant is searched before the timed
+    # region, and the timed steps encode with it
+    t_rate = time.perf_counter()
+    hs = [hq.encode_rate(xs[l], tile, lat, bps, seed_of(l)) for l in range(L)]
+    t_rate = time.perf_counter() - t_rate
+    cs = [h.c for h in hs]
     outs = [torch.empty_like(xs[0]) for _ in range(L)]
     torch.cuda.synchronize()
 
@@ -320,7 +387,7 @@ def main():
         for l in range(L):
             if record:
                 ev[l][0].record(stream)
-            hq.encode(xs[l], tile, lat, bps, seed_of(l), out=hs[l], zero_status=False)
+            hq.encode_c(xs[l], tile, lat, cs[l], seed_of(l), out=hs[l], zero_status=False)
             if record:
                 ev[l][1].record(stream)
         for l in range(L):
@@ -366,12 +433,12 @@ def main():
     enc_avg_us = 1000.0 * sum(enc_ms) / len(enc_ms)
     dec_avg_us = 1000.0 * sum(dec_ms) / len(dec_ms)
     dom_name, dom_us = ("encode_kernel", enc_avg_us) if enc_avg_us >= dec_avg_us else ("decode_kernel", dec_avg_us)
-    achieved = alg / (dom_us * 1e-6) / 1e9
+    words = sum(h.payload_words() for h in hs)
 
     cpu = None
     if args.cpu_layers > 0:
         host = [(l, workloads.bf16_bits(xs[l])) for l in range(min(args.cpu_layers, L))]
-        cpu = cpu_baseline(host, rows, cols, tile, bps, seed_of, p.rate_constant)
+        cpu = cpu_baseline(host, rows, cols, tile, seed_of, lambda l: cs[l])
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -383,16 +450,15 @@ def main():
         "encode_hbm_frac_input": round(enc_gbps / HBM_PEAK_GBPS, 4),
         "decode_hbm_frac_input": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "encode_us_per_layer": round(enc_avg_us, 2), "decode_us_per_layer": round(dec_avg_us, 2),
-        "bps_payload": round(bits_payload / (numel * L), 4), "bps_total": round(bits_total / (numel * L), 4),
+        "bps_payload": round(bits_payload / (numel * L), 4), "bps_stream": round(32.0 * words / (numel * L), 4),
+        "bps_total": round(bits_total / (numel * L), 4),
+        "rate_control": {"kind": "closed loop per layer (bisection on the rate constant, before the timed region)",
+                         "c_min": min(cs), "c_max": max(cs), "c_table": p.rate_constant,
+                         "encodes": sum(h.extra["encodes"] for h in hs), "search_s": round(t_rate, 3)},
         "compression_vs_bf16": round(16.0 * numel * L / bits_total, 3), "nmse": err / ref, "status_flags": flags,
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dom_name), "algorithmic_bytes_per_launch": alg,
-                     "avg_launch_us": round(dom_us, 2)},
-        "roofline_per_kernel": {
-            nm: {"achieved": round(alg / (us * 1e-6) / 1e9, 1), "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                 "avg_launch_us": round(us, 2), "traffic": measured_traffic(nm)}
-            for nm, us in (("encode_kernel", enc_avg_us), ("decode_kernel", dec_avg_us))},
+        "roofline": roofline(dom_name, dom_us, alg, numel),
+        "roofline_per_kernel": {nm: roofline(nm, us, alg, numel)
+                                for nm, us in (("encode_kernel", enc_avg_us), ("decode_kernel", dec_avg_us))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -99,52 +99,11 @@ __device__ __forceinline__ void nearest_d4(const float* t, int32_t* d, uint32_t&
   p = 0;
 }
 
-// Squared distance from t to the nearest point of the coset D8 + h (h = 0,
-// or 1/2 in every coordinate: Conway & Sloane's decoder on the shifted
-// coset), in fp64 with the pairwise tree over the 8 squares.  Start from
-// rint(t) (h = 0) or floor(t) + 1/2; if the integer parts sum to an odd
-// number, move the first coordinate farthest from that start one step
-// towards t: the first of largest |t - rint t| for h = 0, of smallest for
-// h = 1/2 (|t - rint t| is exact in fp32, and the distance to floor(t) + 1/2
-// is 1/2 minus it).
-__device__ __forceinline__ double e8_coset_dist(const float* t, bool half) {
-  float P[8], ad[8], tgt = half ? 1.0f : 0.0f;
-  int32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const float f = __builtin_rintf(t[i]);
-    ad[i] = __builtin_fabsf(t[i] - f);
-    const float base = half ? __builtin_floorf(t[i]) : f;
-    sum += (int32_t)base;
-    P[i] = half ? base + 0.5f : base;
-    tgt = half ? __builtin_fminf(tgt, ad[i]) : __builtin_fmaxf(tgt, ad[i]);
-  }
-  bool seen = false;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const bool first = (sum & 1) && !seen && ad[i] == tgt;
-    seen = seen || first;
-    if (first) P[i] = P[i] + (t[i] >= P[i] ? 1.0f : -1.0f);
-  }
-  double q[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const double e = (double)t[i] - (double)P[i];
-    q[i] = e * e;
-  }
-  return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-}
-
-// E8 = D8 u (D8 + 1/2) (Methodology 2): the nearer of the two cosets' nearest
-// points by squared distance in fp64 (e8_coset_dist), a tie going to D8.
-// The fast path decides through an identity instead: with delta = t - rint(t),
+// E8 = D8 u (D8 + 1/2) (Methodology 2): the nearer of the two cosets'
+// nearest points A (D8) and B (D8 + 1/2).  With delta = t - rint(t) (exact),
 //   |t-A|^2 - |t-B|^2 = sum|delta| - 2 + [A moved](1 - 2 max|delta|) - [B moved] 2 min|delta|
-// (exact in the reals; B's moved coordinate is the one of smallest |delta|),
-// evaluated in fp32 as diff.  Every delta is exact in fp32, so diff is within
-// 10 * 2^-23 of the exact difference, and the fp64 distances are within a
-// relative 2^-50 or so of theirs: wherever |diff| > 2^-16 the two distances
-// compare as diff says.  A lane with |diff| <= 2^-16 (a near tie; rare)
-// computes the two distances themselves.
+// in exact arithmetic (B's moved coordinate is the one of smallest |delta|),
+// evaluated in fp32 in this order; B iff it is > 0.
 //
 // The encoder goes straight to Rice symbols (nearest_e8_symbols), arranged
 // for fewer operations.  With f = rint(t) and delta = t - f:
@@ -199,11 +158,6 @@ __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
   if (oddA) diff = diff + (1.0f - 2.0f * mx);
   if (oddB) diff = diff - 2.0f * mn;
   c.useB = diff > 0.0f;
-  const bool near_tie = __builtin_fabsf(diff) <= 0x1p-16f;
-  if (__any(near_tie)) {
-    asm volatile("");                                       // (rare: stays a branch)
-    if (near_tie) c.useB = e8_coset_dist(t, true) < e8_coset_dist(t, false);
-  }
   const float target = c.useB ? mn : mx;
   // (bitwise operators on the conditions: they stay lane masks)
   bool seen = false, negj = false;
@@ -522,6 +476,15 @@ __device__ __forceinline__ void lds_load16(const uint32_t* base, uint32_t voff, 
 __device__ __forceinline__ void lds_load_u16(const uint16_t* base, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// The same for one 32-bit word a lane (lane i's at lds + 4 i), read coherently
+// at device scope (sc1: not from a stale line of this XCD's L2), for words
+// that workgroups on other XCDs update with atomics.
+__device__ __forceinline__ void lds_load_u32_coherent(const uint32_t* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3 sc1\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 

@@ -253,6 +253,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   uint32_t* misc = tile_off + kChunkTiles;                  // [4]
   uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
   uint32_t* goff = smask + 8;                               // [2][kMaxGroupChunks] chunk word offsets per half
+  uint32_t* started_copy = goff + 2 * kMaxGroupChunks;      // [kStartedWords] the started array, read ahead
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -277,7 +278,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   // with no group left to draw (a grid as large as the group count) every
   // draw fails: no started bits are set or read
   bool checked = CG == gridDim.x, all_started = false;      // wave 1: the started array was read, and its verdict
-  uint32_t started_word = 0;                                // (lane i: word i, loaded ahead)
+  const uint32_t started_copy_lds = __builtin_amdgcn_readfirstlane(lds_addr(started_copy));
   for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
   uint64_t grp = blockIdx.x;
@@ -416,10 +417,11 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     wave_priority(quarters >= 3u ? 0u : 3u - quarters);
     const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
     if (pend && last && tid < 64) place();
-    // before the first draw: wave 1 loads the started array now, to use it
-    // after this chunk's compute
-    if (last && !checked && tid >= 64 && tid < 128 && (uint32_t)(tid - 64) < kStartedWords)
-      started_word = __hip_atomic_load(&started[tid - 64], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // before the first draw: wave 1 loads the started array into LDS now
+    // (no register held through the compute), to read it after this chunk's
+    // compute
+    if (last && !checked && tid >= 64 && tid < 128)
+      lds_load_u32_coherent(started, 4u * (uint32_t)(tid - 64), started_copy_lds);
 
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
@@ -731,9 +733,10 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     if (last && tid >= 64 && tid < 128) {
       // every workgroup of the grid has started (wave 1: lane i checks word i)
       if (!checked) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // (this wave's load of the started array)
         const uint32_t i = (uint32_t)(tid - 64), g = gridDim.x;
         const uint32_t want = 32u * i >= g ? 0u : (32u * (i + 1u) <= g ? 0xFFFFFFFFu : (1u << (g & 31u)) - 1u);
-        all_started = __all((started_word & want) == want);
+        all_started = __all((started_copy[i] & want) == want);
         checked = true;
       }
       if (tid == 64) next_ticket = take_ticket(ws, CG, epoch, all_started);

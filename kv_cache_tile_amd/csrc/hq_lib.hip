@@ -184,7 +184,7 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   size_t lds_cap = per_regs > 0 ? (size_t)lds_cu / (size_t)per_regs : (size_t)max_lds;
   if (lds_cap > (size_t)max_lds) lds_cap = (size_t)max_lds;
   lds_cap = lds_cap / kLdsGrain * kLdsGrain;
-  const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks;
+  const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks + kStartedWords;
   const size_t avail = lds_cap / 4 > fixed_words ? lds_cap / 4 - fixed_words : 0;
   uint32_t group = kMaxGroupChunks, grp_words = 0;
   for (;; group--) {
