@@ -202,6 +202,27 @@ int hq_decode_c(const uint32_t *payload, uint64_t payload_words, const uint16_t 
                 uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
                 float c, uint64_t seed, uint32_t kv, void *x_out, uint32_t *status, void *stream);
 int hq_rate_bracket(uint32_t lattice, float target_bps, float *c_lo, float *c_hi);
+
+/*
+ * hq_encode_c_noalloc — hq_encode_c without the workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The workspace is a
+ * static 1 MiB device array in the library, one per GPU, held until the
+ * process ends; the first call on a GPU takes its address and clears it with
+ * a kernel on `stream`.  The call allocates nothing (no hipMalloc, no
+ * library allocation); the caller still passes every input and output.
+ * Limit: the workspace hq_plan_c reports (768 + 8 C bytes) must fit 1 MiB,
+ * i.e. at most 130976 chunks of 64 tiles; larger tensors get HQ_ENOSPC
+ * before any device work.  Every call on one GPU shares its array, and each
+ * call leaves it ready for the next: calls issued on one stream follow one
+ * another safely, but calls that overlap in time on one GPU (different
+ * streams, or threads) race and must not be made.  Other arguments, errors
+ * and the stream are hq_encode_c's.
+ */
+int hq_encode_c_noalloc(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                        uint32_t lattice, float c, uint64_t seed, uint32_t kv,
+                        uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,
+                        uint32_t *chunk_off, uint32_t *status, void *stream);
 int hq_encode_rate(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
                    uint32_t lattice, float target_bps, uint64_t seed, uint32_t kv,
                    uint32_t *payload, uint64_t payload_cap_words, uint16_t *step, uint16_t *meta,

@@ -13,6 +13,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hq.h"
 #include "hq_kernels.h"
 
@@ -277,6 +279,43 @@ int do_decode(const Plan& P, const uint32_t* payload, uint64_t payload_words, co
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
+// --------------------------------------------------------------------------
+// The encode workspace of hq_encode_c_noalloc: a file-scope device array, one
+// copy per GPU for the life of the process.  In host code its name stands for
+// a host-side symbol, not a device address: each device's address is taken
+// once with hipGetSymbolAddress (with that device current) and kept, and only
+// that address is passed to kernels.
+// --------------------------------------------------------------------------
+constexpr uint64_t kScratchBytes = 1ull << 20;             // 768 + 8 C bytes: up to 130976 chunks
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];                              // device address, set up once per device
+
+__global__ void clear_words(uint32_t* w, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) w[i] = 0u;
+}
+
+// the current device's scratch address; on its first use on a device the
+// array is cleared by a kernel on `stream` (zero is the workspace's initial
+// state), ahead of the encode on the same stream
+int scratch_for_current_device(void* stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HQ_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return HQ_EHIP;
+    hipLaunchKernelGGL(clear_words, dim3(256), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ptr,
+                       (uint32_t)(kScratchBytes / 4));
+    if (hipGetLastError() != hipSuccess) return HQ_EHIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return HQ_OK;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -365,6 +404,22 @@ int hq_encode_c(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uin
   if (kv && cols != tile) return HQ_EINVAL;
   return do_encode(P, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off,
                    status, workspace, workspace_bytes, stream);
+}
+
+int hq_encode_c_noalloc(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                        uint32_t lattice, float c, uint64_t seed, uint32_t kv, uint32_t* payload,
+                        uint64_t payload_cap_words, uint16_t* step, uint16_t* meta, uint32_t* chunk_off,
+                        uint32_t* status, void* stream) {
+  Plan P;
+  int rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &P);
+  if (rc) return rc;
+  if (kv && cols != tile) return HQ_EINVAL;
+  if (P.ws_bytes > kScratchBytes) return HQ_ENOSPC;
+  void* ws = nullptr;
+  rc = scratch_for_current_device(stream, &ws);
+  if (rc) return rc;
+  return do_encode(P, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off, status,
+                   ws, kScratchBytes, stream);
 }
 
 int hq_decode_c(const uint32_t* payload, uint64_t payload_words, const uint16_t* step, const uint16_t* meta,

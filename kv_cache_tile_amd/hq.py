@@ -24,7 +24,7 @@ CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
            "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
-           "hq_codes_matmul", "hq_nearest")
+           "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc")
 
 
 class HQError(RuntimeError):
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.hq_plan_c.restype = ctypes.c_int
         L.hq_encode_c.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64, vp]
         L.hq_encode_c.restype = ctypes.c_int
+        L.hq_encode_c_noalloc.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp]
+        L.hq_encode_c_noalloc.restype = ctypes.c_int
         L.hq_decode_c.argtypes = [vp, u64, vp, vp, vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, vp, vp]
         L.hq_decode_c.restype = ctypes.c_int
         L.hq_rate_bracket.argtypes = [u32, f32, P(f32), P(f32)]
@@ -303,6 +305,19 @@ def encode_c(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int = 0, 
         return out
     return HQTensor(payload, step, meta, off, status, tuple(x.shape), x.dtype, tile, lattice, float("nan"), seed,
                     kv, c=float(c))
+
+
+def encode_c_noalloc(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int, out: HQTensor,
+                     kv: bool = False) -> HQTensor:
+    """encode_c into the buffers of `out` (sized for this tensor and c), with
+    the library's static workspace: no device allocation anywhere in the call."""
+    x2, rows, cols = _rows_cols(x, tile, kv)
+    _check(lib().hq_encode_c_noalloc(x2.data_ptr(), _dtype_code(x2.dtype), rows, cols, tile, LATTICES[lattice],
+                                     float(c), seed, int(kv), out.payload.data_ptr(), out.payload.numel(),
+                                     out.step.data_ptr(), out.meta.data_ptr(), out.chunk_off.data_ptr(),
+                                     out.status.data_ptr(), _stream(x.device)))
+    out.c = float(c)
+    return out
 
 
 def encode_rate(x: torch.Tensor, tile: int, lattice: str, target_bps: float, seed: int = 0,
