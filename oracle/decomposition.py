@@ -25,6 +25,17 @@ bit, the high-rate slope):
   unbounded = gain - slack              (the rest: unbounded codebook,
                                            entropy-coded step choice, lattice)
 
+A second fixed-rate scheme is the codec itself, clamped (fixed_rate_codec):
+the same RHT, per-tile step and nearest lattice point, but the integer code
+clamped to a finite codebook and stored at a fixed length, R bits per scalar:
+  - Z: the code clipped to [-2^(R-1), 2^(R-1) - 1], R bits;
+  - E8 (a block's code is the coset bit p and d in D8, point d + p/2): p raw,
+    d0..d6 clipped to R-bit two's complement, and d7's half (d7 >> 1, its
+    parity being that of d0 + ... + d6) clipped to R - 1 bits:
+    1 + 7R + (R - 1) = 8R bits a block.
+Its rate constant is searched for the least NMSE; its slack and the rest of
+the gain are reported beside the uniform codebook's.
+
 Only ``oracle/`` is called.  Run:  python oracle/decomposition.py
 """
 from __future__ import annotations
@@ -57,6 +68,16 @@ def entropy_bits(codes: np.ndarray) -> float:
     return float(-(p * np.log2(p)).sum())
 
 
+def symbol_entropy(lat: str, sym: np.ndarray) -> float:
+    """Bits per scalar an ideal entropy coder of a lattice code's symbols
+    (one row a block) would spend: Z one source; E8 the first seven
+    coordinates as one source, the halved last one as another, plus the raw
+    coset bit of each block."""
+    if lat == "Z":
+        return entropy_bits(sym.ravel())
+    return (7 * entropy_bits(sym[:, :7].ravel()) + entropy_bits(sym[:, 7]) + 1.0) / 8.0
+
+
 def fixed_rate_uniform(x: np.ndarray, R: int, grid: int = 400):
     """The 2^R-level uniform quantizer with the least MSE on x (step searched
     on a fine grid, then refined): (step, MSE, index entropy)."""
@@ -82,8 +103,9 @@ def ours(x: np.ndarray, lat: str, tile: int, R: float, seed: int = 5):
     """The oracle codec on x [rows][tile]: (payload bps, symbol entropy per
     scalar, NMSE).  Symbol entropy: the Rice symbols of every tile (zigzag of
     the lattice's integer coordinates, E8's last one halved first, the
-    parity strip) as one i.i.d. source, plus E8's raw coset bit per 8
-    scalars: what an ideal entropy coder of the same symbols would spend."""
+    parity strip) as i.i.d. sources (symbol_entropy), plus E8's raw coset
+    bit per 8 scalars: what an ideal entropy coder of the same symbols would
+    spend."""
     c = table_c(lat, tile, R)
     e = oracle.encode(x, tile, lat, c, seed)
     bps = float((e.meta >> 3).astype(np.int64).sum()) / x.size
@@ -100,12 +122,60 @@ def ours(x: np.ndarray, lat: str, tile: int, R: float, seed: int = 5):
             d = d.copy()
             d[:, 7] >>= 1                      # the stripped parity bit
         sym = np.where(d >= 0, 2 * d, -2 * d - 1)   # zigzag
-        codes.append(sym.ravel())
+        codes.append(sym.reshape(-1, 8 if lat == "E8" else 1))
         cos.append(p)
-    h = entropy_bits(np.concatenate(codes))
-    if lat == "E8":
-        h += 1.0 / 8.0                         # the raw coset bit of each block
+    h = symbol_entropy(lat, np.concatenate(codes))
     return bps, h, nmse
+
+
+def clamp_codes(lat: str, p: np.ndarray, d: np.ndarray, R: int):
+    """The fixed-rate codebook of the clamped codec: (points, symbols) of the
+    clamped codes (see the module text); symbols as coded, one row a block."""
+    lo, hi = -(1 << (R - 1)), (1 << (R - 1)) - 1
+    if lat == "Z":
+        dc = np.clip(d, lo, hi)
+        return dc.astype(np.float64), dc
+    dc = d.astype(np.int64).copy()
+    dc[:, :7] = np.clip(dc[:, :7], lo, hi)
+    h7 = np.clip(d[:, 7].astype(np.int64) >> 1, -(1 << (R - 2)), (1 << (R - 2)) - 1)
+    dc[:, 7] = 2 * h7 + (dc[:, :7].sum(axis=1) & 1)
+    sym = np.concatenate([dc[:, :7], h7[:, None]], axis=1)
+    return dc + p[:, None] / 2.0, sym
+
+
+def fixed_rate_codec(x: np.ndarray, lat: str, tile: int, R: int, seed: int = 5, grid: int = 24):
+    """The codec clamped to a fixed-rate codebook (module text) on x
+    [rows][tile], at the rate constant of least NMSE: (c, NMSE, entropy of
+    its symbols per scalar, bits per scalar).  The error is measured in the
+    rotated domain (the RHT is orthogonal)."""
+    ys = np.stack([oracle.rht_forward(r, seed) for r in x]).astype(np.float32)
+    d_ = 8 if lat == "E8" else 1
+    energy = float((ys.astype(np.float64) ** 2).sum())
+
+    def run(c):
+        pts, syms = [], []
+        for y in ys:
+            s, _ = oracle.tile_step(y, c)
+            inv = np.float32(0.0) if s == 0 else np.float32(1.0) / s
+            p, d, _ = oracle.nearest_batch(lat, (y * inv).astype(np.float32))
+            P, sym = clamp_codes(lat, p, d.reshape(-1, d_), R)
+            pts.append(P.reshape(-1) * float(s))
+            syms.append(sym.reshape(-1))
+        err = float(((np.stack(pts) - ys.astype(np.float64)) ** 2).sum())
+        return err / energy, np.concatenate(syms)
+
+    c_hr = float(np.array([oracle.RATE_K_BITS[lat]], np.uint32).view(np.float32)[0]) * 2.0 ** -R
+    lo, hi = 0.5 * c_hr, 3.0 * c_hr
+    for _ in range(3):
+        cs = np.geomspace(lo, hi, grid)
+        errs = [run(float(np.float32(c)))[0] for c in cs]
+        i = int(np.argmin(errs))
+        lo, hi = cs[max(i - 1, 0)], cs[min(i + 1, grid - 1)]
+    c = float(np.float32(np.sqrt(lo * hi)))
+    nmse, syms = run(c)
+    h = symbol_entropy(lat, syms.reshape(-1, d_))
+    bits = float(R) if lat == "Z" else (1 + 7 * R + (R - 1)) / 8.0
+    return c, nmse, h, bits
 
 
 def decomposition(R: int, n_rows: int = 512, tile: int = 256, key: int = 11):
@@ -121,7 +191,24 @@ def decomposition(R: int, n_rows: int = 512, tile: int = 256, key: int = 11):
     out["slack_bits"] = R - h_fixed
     for lat in ("Z", "E8"):
         out[lat]["unbounded_bits"] = out[lat]["gain_bits"] - out["slack_bits"]
+        # the codec clamped to a fixed-rate codebook of the same lattice
+        c, nmse_f, h_f, bits = fixed_rate_codec(x, lat, tile, R)
+        gain = 0.5 * math.log2(nmse_f / out[lat]["nmse"])
+        out[lat]["clamped"] = {"c": c, "bits": bits, "nmse": nmse_f, "entropy": h_f, "slack_bits": bits - h_f,
+                               "gain_bits": gain, "unbounded_bits": gain - (bits - h_f)}
     return out
+
+
+def main_clamped():
+    print("| R | lattice | clamped codec: NMSE, index entropy | slack | ours: Rice bps, NMSE | gain = slack + rest |")
+    print("|---|---|---|---|---|---|")
+    for R in (2, 3, 4, 5, 6):
+        o = decomposition(R)
+        for lat in ("Z", "E8"):
+            f, u = o[lat]["clamped"], o[lat]
+            print(f"| {R} | {lat} | {f['nmse']:.4e}, {f['entropy']:.3f} | {f['slack_bits']:.3f} | "
+                  f"{u['bps']:.3f}, {u['nmse']:.4e} | {f['gain_bits']:.3f} = {f['slack_bits']:.3f} + "
+                  f"{f['unbounded_bits']:.3f} |", flush=True)
 
 
 def main():
@@ -137,4 +224,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    main_clamped() if "--clamped" in sys.argv else main()
