@@ -102,7 +102,7 @@ int hq_plan(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_
  *   step, meta device, T uint16 each
  *   chunk_off  device, C+1 uint32
  *   status     device, one uint32 (flags OR-ed in)
- *   workspace  device, 8-byte aligned, workspace_bytes (>= hq_plan's: 16 + 8 C)
+ *   workspace  device, 8-byte aligned, workspace_bytes (>= hq_plan's: 768 + 8 C)
  *              zero-filled ONCE before its first use; the kernels leave it
  *              ready for the next call.  Calls that overlap in time must not
  *              share a workspace.
@@ -265,6 +265,9 @@ int hq_rotate(const float *Q, uint32_t d, uint32_t transpose, const void *x, uin
  *   per tile of n (the weights' tile size and seed), y = the codec's RHT of
  *   the tile, a = fl(max |y| / 127), q = rint(fl(y / a)) (0 where a = 0),
  *   clamped to [-127, 127]; q int8 [batch][cols], a fp32 [batch][cols / n].
+ *   A tile with a NaN gets a = NaN and one with an infinity a = inf (max |y|
+ *   lets a NaN through); a code whose quotient y / a is NaN is 0.  Such a
+ *   tile's products are then NaN, so the non-finite input shows in y.
  * hq_codes_matmul — y[b][r] = 0.5 * (fma chain over the row's tiles t in
  *   ascending order, from +0, of (float) I * fl(s_t * a_bt)), I the exact
  *   int32 <codes tile, q tile> (matrix cores, all tiles in parallel; the
@@ -283,6 +286,32 @@ int hq_act_quant(const void *x, uint32_t x_dtype, uint64_t batch, uint64_t cols,
 int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, uint64_t cols,
                     uint32_t tile, const int8_t *q, const float *scale, uint64_t batch, float *y,
                     int32_t *work, uint64_t work_bytes, void *stream);
+
+/*
+ * hq_codes_matmul_fused — hq_decode_codes followed by hq_codes_matmul in one
+ * launch, straight from the compressed stream (gist.science explainer of
+ * HyperQuant, "Significance and Claims": decoding fused with the matrix
+ * product): the same y, bit for bit, with no code tensor and no scratch in
+ * device memory.  Each tile's bits are parsed into its codes 2P in on-chip
+ * memory and multiplied there on the matrix cores; the fp32 chain over a
+ * row's tiles runs in ascending order.
+ *   payload .. chunk_off, rows, cols, tile, lattice, c: a weight stream as
+ *              for hq_decode_codes (Z, D4 or E8 without dither); every row
+ *              must be a whole number of 64-tile chunks: cols % (64 tile) == 0;
+ *              payload 16-byte aligned (it is read in 16-byte vectors)
+ *   q, scale   hq_act_quant's output for [batch][cols] activations (q 16-byte
+ *              aligned)
+ *   y          fp32 [batch][rows]
+ *   status     device word: HQ_FLAG_CORRUPT (a tile's codes taken as 0) and
+ *              HQ_FLAG_RANGE (a code saturated) are OR-ed in, as by
+ *              hq_decode_codes
+ * Asynchronous on `stream`; HQ_EINVAL for another lattice or shape, or a NULL
+ * or misaligned pointer, before any device work.
+ */
+int hq_codes_matmul_fused(const uint32_t *payload, uint64_t payload_words, const uint16_t *step,
+                          const uint16_t *meta, const uint32_t *chunk_off, uint64_t rows, uint64_t cols,
+                          uint32_t tile, uint32_t lattice, float c, const int8_t *q, const float *scale,
+                          uint64_t batch, float *y, uint32_t *status, void *stream);
 
 /*
  * hq_nearest — the lattice quantiser alone (gist.science explainer of

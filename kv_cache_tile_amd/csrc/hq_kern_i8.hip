@@ -49,16 +49,21 @@ act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_
     __syncthreads();
   }
   const float v0 = y[k] * inv_sqrtn, v1 = y[k + N / 2] * inv_sqrtn;
-  red[k] = fmaxf(fabsf(v0), fabsf(v1));
+  // max |y| with a NaN kept (a NaN or an infinity in the tile makes its scale
+  // non-finite; a code whose quotient is NaN is 0, so the tile's products are
+  // NaN downstream)
+  auto nan_max = [](float u, float v) { return (u != u || v != v) ? u + v : fmaxf(u, v); };
+  red[k] = nan_max(fabsf(v0), fabsf(v1));
   __syncthreads();
   for (int m = N / 4; m > 0; m >>= 1) {
-    if (k < m) red[k] = fmaxf(red[k], red[k + m]);
+    if (k < m) red[k] = nan_max(red[k], red[k + m]);
     __syncthreads();
   }
   const float a = red[0] / 127.0f;
   auto code = [&](float v) -> int8_t {
     if (a == 0.0f) return 0;
     float r = rintf(v / a);
+    if (r != r) return 0;
     r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
     return (int8_t)(int)r;
   };

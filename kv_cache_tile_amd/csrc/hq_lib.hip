@@ -28,6 +28,10 @@ const void* act_quant_fn(uint32_t n);
 bool launch_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t n,
                          const int8_t* q, const float* scale, uint64_t batch, float* y, int32_t* work,
                          hipStream_t stream);
+// hq_kern_fused.hip: the product read from the stream, for (lattice, n); its
+// threads and LDS bytes for segments of seg_words (null if unsupported)
+const void* fused_fn(uint32_t lattice, uint32_t n, uint32_t seg_words, uint32_t* threads, size_t* lds);
+constexpr int kFusedRowsHost = 8, kFusedColsHost = 8, kFusedBatchHost = 32;   // as in hq_kern_fused.hip
 }  // namespace hq
 
 using namespace hq;
@@ -568,6 +572,36 @@ int hq_nearest(uint32_t lattice, const float* t, uint64_t nblocks, float* points
   if (rc) return rc;
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, (hipStream_t)stream, t, nblocks, points, a2);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+int hq_codes_matmul_fused(const uint32_t* payload, uint64_t payload_words, const uint16_t* step,
+                          const uint16_t* meta, const uint32_t* chunk_off, uint64_t rows, uint64_t cols,
+                          uint32_t tile, uint32_t lattice, float c, const int8_t* q, const float* scale,
+                          uint64_t batch, float* y, uint32_t* status, void* stream) {
+  Plan P;
+  int rc = plan_for_c(HQ_BF16, rows, cols, tile, lattice, c, 0, &P);
+  if (rc) return rc;
+  if (lattice == HQ_A2 || cols % ((uint64_t)kChunkTiles * tile) != 0) return HQ_EINVAL;
+  if (!payload || !step || !meta || !chunk_off || !q || !scale || !y || !status) return HQ_EINVAL;
+  if (((uintptr_t)payload & 15) || ((uintptr_t)q & 15) || batch * cols >= (1ull << 32)) return HQ_EINVAL;
+  if (batch == 0) return HQ_OK;
+  // a row's run of a unit: its words, 3 before and 3 after for the 16-byte
+  // vectors it is streamed in, and 8 zero guard words
+  const uint32_t seg_words = ((kFusedColsHost * P.bound + 31) / 32 + 1 + 3 + 3 + 8 + 3) & ~3u;
+  const uint32_t chunk_cap = (uint32_t)(((uint64_t)kChunkTiles * P.bound + 31) / 32);
+  uint32_t threads = 0;
+  size_t lds = 0;
+  const void* fn = fused_fn(lattice, tile, seg_words, &threads, &lds);
+  if (!fn) return HQ_EINVAL;
+  const uint64_t gx = (rows + kFusedRowsHost - 1) / kFusedRowsHost, gy = (batch + kFusedBatchHost - 1) / kFusedBatchHost;
+  if (gx > 0x7FFFFFFFull || gy > 65535) return HQ_EINVAL;
+  hipLaunchKernelGGL((void (*)(const uint32_t*, uint64_t, const uint16_t*, const uint16_t*, const uint32_t*, uint64_t,
+                               uint32_t, const int8_t*, const float*, uint64_t, float*, uint32_t*, uint32_t, uint32_t,
+                               uint32_t))fn,
+                     dim3((uint32_t)gx, (uint32_t)gy), dim3(threads), lds, (hipStream_t)stream, payload, payload_words,
+                     step, meta, chunk_off, rows, (uint32_t)(cols / tile), q, scale, batch, y, status, seg_words,
+                     chunk_cap, P.bound);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 

@@ -24,7 +24,7 @@ CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
            "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
-           "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc")
+           "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc", "hq_codes_matmul_fused")
 
 
 class HQError(RuntimeError):
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.hq_act_quant.restype = ctypes.c_int
         L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp, u64, vp]
         L.hq_codes_matmul.restype = ctypes.c_int
+        L.hq_codes_matmul_fused.argtypes = [vp, u64, vp, vp, vp, u64, u64, u32, u32, f32, vp, vp, u64, vp, vp, vp]
+        L.hq_codes_matmul_fused.restype = ctypes.c_int
         L.hq_nearest.argtypes = [u32, vp, u64, vp, vp]
         L.hq_nearest.restype = ctypes.c_int
         L.hq_strerror.argtypes = [ctypes.c_int]
@@ -375,8 +377,7 @@ def kv_decode_haar(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor
 
 
 # ---------------------------------------------------------------- int8 product path
-def decode_codes(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """The weights' integer codes 2P (int8 [rows][cols]) for hq_codes_matmul."""
+def _rows_cols_c(h: HQTensor) -> tuple:
     if h.kv:
         raise HQError("integer codes: weights only (the KV path is dithered)")
     rows = 1
@@ -384,11 +385,40 @@ def decode_codes(h: HQTensor, out: torch.Tensor | None = None) -> torch.Tensor:
         rows *= s_
     cols = h.shape[-1]
     c = h.c if h.c is not None else plan(_dtype_code(h.dtype), rows, cols, h.tile, h.lattice, h.bps).rate_constant
+    return rows, cols, c
+
+
+def decode_codes(h: HQTensor, out: torch.Tensor | None = None, status: torch.Tensor | None = None) -> torch.Tensor:
+    """The weights' integer codes 2P (int8 [rows][cols]) for hq_codes_matmul;
+    flags go to `status` (default: the stream's own status word)."""
+    rows, cols, c = _rows_cols_c(h)
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.int8, device=h.payload.device)
+    st = h.status if status is None else status
     _check(lib().hq_decode_codes(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(), h.meta.data_ptr(),
                                  h.chunk_off.data_ptr(), rows, cols, h.tile, LATTICES[h.lattice], c, h.seed,
-                                 out.data_ptr(), h.status.data_ptr(), _stream(out.device)))
+                                 out.data_ptr(), st.data_ptr(), _stream(out.device)))
+    return out
+
+
+def fused_supported(h: HQTensor) -> bool:
+    """Whether codes_matmul_fused takes this stream: Z, D4 or E8 weights whose
+    rows are whole 64-tile chunks."""
+    return not h.kv and h.lattice != "A2" and h.shape[-1] % (CHUNK_TILES * h.tile) == 0
+
+
+def codes_matmul_fused(h: HQTensor, q: torch.Tensor, scale: torch.Tensor, status: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [batch][rows] = the int8 product straight from the stream (one launch);
+    CORRUPT / RANGE flags go to `status`."""
+    rows, cols, c = _rows_cols_c(h)
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, rows), dtype=torch.float32, device=q.device)
+    _check(lib().hq_codes_matmul_fused(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(),
+                                       h.meta.data_ptr(), h.chunk_off.data_ptr(), rows, cols, h.tile,
+                                       LATTICES[h.lattice], c, q.data_ptr(), scale.data_ptr(), B, out.data_ptr(),
+                                       status.data_ptr(), _stream(q.device)))
     return out
 
 
@@ -419,10 +449,22 @@ def codes_matmul(codes: torch.Tensor, step: torch.Tensor, tile: int, q: torch.Te
 
 
 def matmul_compressed(h: HQTensor, x: torch.Tensor) -> torch.Tensor:
-    """x @ W_hat^T for compressed weights h, through the int8 product path."""
-    codes = decode_codes(h)
+    """x @ W_hat^T for compressed weights h, through the int8 product path
+    (fused with the decode where the shape allows).  Synchronises to read its
+    own status word, and raises if a tile's codes were saturated (the result
+    would not be x W_hat^T) or the stream is corrupt."""
     q, sc = act_quant(x, h.tile, h.seed)
-    return codes_matmul(codes, h.step, h.tile, q, sc)
+    status = torch.zeros(1, dtype=torch.int32, device=q.device)
+    if fused_supported(h):
+        y = codes_matmul_fused(h, q, sc, status)
+    else:
+        y = codes_matmul(decode_codes(h, status=status), h.step, h.tile, q, sc)
+    flags = int(status.item())
+    if flags & FLAG_RANGE:
+        raise HQError("integer codes beyond [-127, 127] were saturated: the product is not x W_hat^T")
+    if flags & FLAG_CORRUPT:
+        raise HQError("corrupt compressed stream")
+    return y
 
 
 # ---------------------------------------------------------------- the quantiser alone

@@ -819,12 +819,23 @@ void hqo_act_quant(const float *x, uint64_t batch, uint64_t cols, uint32_t n, ui
     for (uint64_t b = 0; b < batch; b++)
         for (uint64_t t = 0; t < cols / n; t++) {
             hqo_rht_forward(x + b * cols + t * n, n, seed, y);
+            /* max |y|, a NaN kept (reading: the pages are silent on
+             * non-finite activations; a NaN or an infinity makes the tile's
+             * scale non-finite, every code whose quotient is NaN is 0, and the
+             * product over the tile is then NaN) */
             float m = 0.0f;
-            for (uint32_t i = 0; i < n; i++) m = fabsf(y[i]) > m ? fabsf(y[i]) : m;
+            for (uint32_t i = 0; i < n; i++) {
+                float v = fabsf(y[i]);
+                if (isnan(v) || v > m) m = v;
+            }
             float a = m / 127.0f;
             scale[b * (cols / n) + t] = a;
             for (uint32_t i = 0; i < n; i++) {
-                long v = a == 0.0f ? 0 : lrintf(y[i] / a);
+                long v = 0;
+                if (a != 0.0f) {
+                    float r = y[i] / a;
+                    v = isnan(r) ? 0 : lrintf(r);
+                }
                 q[b * cols + t * n + i] = (int8_t)(v > 127 ? 127 : (v < -127 ? -127 : v));
             }
         }

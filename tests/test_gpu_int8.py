@@ -1,7 +1,9 @@
 """GPU parity of the int8 product path (gist.science explainer of HyperQuant,
 Key Contributions, "Hardware Integration"; Methodology section 2): codes 2P
 from the decoder, the activations' int8 RHT, and the matrix-core product,
-each bit-exact against the oracle."""
+each bit-exact against the oracle; and the product read straight from the
+stream in one launch (hq_codes_matmul_fused; "Significance and Claims":
+decoding fused with the product), bit-exact against the same oracle chain."""
 import numpy as np
 import pytest
 import torch
@@ -91,7 +93,10 @@ def test_dit_layer_product_full():
     print("[case] int8 product DiT layer x 32", flush=True)
     h = hq.encode(wt.to(dev), 256, "E8", 4.0, seed)
     x = workloads.gaussian(32, 16384, key=77)
-    y = hq.matmul_compressed(h, torch.from_numpy(x).to(dev))
+    xd = torch.from_numpy(x).to(dev)
+    y = hq.matmul_compressed(h, xd)                           # (the fused product: rows are whole chunks)
+    qd, scd = hq.act_quant(xd, 256, seed)
+    y2 = hq.codes_matmul(hq.decode_codes(h), h.step, 256, qd, scd)   # the two-pass path
     torch.cuda.synchronize()
     c = rate_c("E8", 256, 4.0)
     e = oracle.encode(wo, 256, "E8", c, seed)
@@ -99,4 +104,88 @@ def test_dit_layer_product_full():
     q, sc = oracle.act_quant(x, 256, seed)
     ref = oracle.codes_matmul(codes, e.step, 256, q, sc)
     np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
-    assert h.flags() == (hq.FLAG_RANGE if flag else 0)
+    np.testing.assert_array_equal(y2.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert flag == 0 and h.flags() == 0
+
+
+def _nan_equal(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    both_nan = np.isnan(a) & np.isnan(b)
+    np.testing.assert_array_equal(np.where(both_nan, 0, a).view(np.uint32), np.where(both_nan, 0, b).view(np.uint32))
+
+
+def test_act_quant_non_finite():
+    dev = _dev()
+    x = workloads.gaussian(3, 512, key=6)
+    x[0, 5] = np.nan
+    x[1, 300] = np.inf
+    x[2, 0] = -np.inf
+    q, sc = hq.act_quant(torch.from_numpy(x).to(dev), 128, 4)
+    rq, rsc = oracle.act_quant(x, 128, 4)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    _nan_equal(sc.cpu().numpy(), rsc)
+
+
+@pytest.mark.parametrize("lat,tile,bps", [("E8", 256, 4.0), ("E8", 128, 3.0), ("D4", 128, 4.0), ("Z", 64, 5.0),
+                                          ("E8", 64, 8.0)])
+def test_fused_product(lat, tile, bps):
+    # rows not a multiple of 8, two chunks a row, activations in two blocks of 32
+    rows, batch = 43, 37
+    cols = 2 * 64 * tile
+    print(f"[case] fused product {lat} n={tile} bps={bps} rows={rows} batch={batch}", flush=True)
+    h, e = _weights(lat, tile, rows, cols, bps, key=tile)
+    x = workloads.gaussian(batch, cols, key=rows + tile)
+    q, sc = hq.act_quant(torch.from_numpy(x).to(_dev()), tile, 7)
+    status = torch.zeros(1, dtype=torch.int32, device=_dev())
+    y = hq.codes_matmul_fused(h, q, sc, status)
+    torch.cuda.synchronize()
+    c = rate_c(lat, tile, bps)
+    codes, st, flag = oracle.decode_codes(e, rows, cols, tile, lat, c, 7)
+    ref = oracle.codes_matmul(codes, e.step, tile, q.cpu().numpy(), sc.cpu().numpy())
+    np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert int(status.item()) == (hq.FLAG_RANGE if flag else 0)
+
+
+def test_fused_product_corrupt_streams():
+    # corrupt tiles and chunks give zero codes (and the flag) on both sides;
+    # a non-finite step makes that tile's products NaN on both sides
+    dev = _dev()
+    lat, tile, rows, cols, batch = "E8", 128, 16, 2 * 64 * 128, 8
+    h, e = _weights(lat, tile, rows, cols, 4.0, key=11)
+    x = workloads.gaussian(batch, cols, key=12)
+    q, sc = hq.act_quant(torch.from_numpy(x).to(dev), tile, 7)
+    c = rate_c(lat, tile, 4.0)
+    rng = np.random.default_rng(3)
+    for trial in range(6):
+        pay, meta, off, step = e.payload.copy(), e.meta.copy(), e.chunk_off.copy(), e.step.copy()
+        if trial % 3 == 0:
+            for _ in range(2):
+                w_ = rng.integers(0, pay.size)
+                pay[w_] ^= np.uint32(1) << np.uint32(rng.integers(0, 32))
+        elif trial % 3 == 1:
+            meta[rng.integers(0, meta.size)] += np.uint16(8)
+        else:
+            step[rng.integers(0, step.size)] = 0x7F80
+        hh = hq.HQTensor(torch.from_numpy(pay.view(np.int32)).to(dev), torch.from_numpy(step.view(np.int16)).to(dev),
+                         torch.from_numpy(meta.view(np.int16)).to(dev), torch.from_numpy(off.view(np.int32)).to(dev),
+                         torch.zeros(1, dtype=torch.int32, device=dev), (rows, cols), torch.bfloat16, tile, lat, 4.0, 7)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        y = hq.codes_matmul_fused(hh, q, sc, status)
+        torch.cuda.synchronize()
+        ee = oracle.Encoded(step, meta, off, pay, 0)
+        codes, st, flag = oracle.decode_codes(ee, rows, cols, tile, lat, c, 7)
+        ref = oracle.codes_matmul(codes, step, tile, q.cpu().numpy(), sc.cpu().numpy())
+        _nan_equal(y.cpu().numpy(), ref)
+        assert bool(int(status.item()) & hq.FLAG_CORRUPT) == (st == oracle.ECORRUPT)
+
+
+def test_matmul_compressed_raises_on_saturation():
+    # at 8 bps some codes pass 127: the product is not x W_hat^T and the
+    # binding says so, with a status word of its own
+    dev = _dev()
+    h, e = _weights("E8", 64, 16, 64 * 64, 8.0, key=13)
+    x = torch.from_numpy(workloads.gaussian(4, 64 * 64, key=14)).to(dev)
+    with pytest.raises(hq.HQError, match="saturated"):
+        hq.matmul_compressed(h, x)
+    assert h.flags() == 0

@@ -74,3 +74,24 @@ def test_product_integer_part_and_end_to_end_bound():
     ref = x.astype(np.float64) @ xh.astype(np.float64).T
     bound = 0.5 * (np.abs(codes.reshape(rows, -1, tile)).sum(-1)[None] * s[None] * sc.astype(np.float64)[:, None, :] / 2).sum(-1)
     assert np.all(np.abs(y - ref) <= bound * 1.01 + 1e-6)
+
+
+def test_act_quant_non_finite_tiles():
+    # a NaN or an infinity makes the tile's scale non-finite and its codes 0
+    # (the product over the tile is then NaN); the other tiles are untouched
+    x = workloads.gaussian(3, 512, key=5)
+    ref_q, ref_a = oracle.act_quant(x, 128, 4)
+    x[0, 5] = np.nan
+    x[1, 300] = np.inf
+    q, a = oracle.act_quant(x, 128, 4)
+    assert np.isnan(a[0, 0]) and np.isinf(a[1, 2])
+    assert not q[0, :128].any() and not q[1, 256:384].any()
+    keep = np.ones_like(a, bool)
+    keep[0, 0] = keep[1, 2] = False
+    np.testing.assert_array_equal(a[keep], ref_a[keep])
+    qm = np.ones_like(q, bool)
+    qm[0, :128] = qm[1, 256:384] = False
+    np.testing.assert_array_equal(q[qm], ref_q[qm])
+    codes = np.ones((2, 512), np.int8)
+    y = oracle.codes_matmul(codes, np.full(8, 0x3F80, np.uint16), 128, q, a)
+    assert np.all(np.isnan(y[:2]))
