@@ -13,7 +13,6 @@ with the fraction of the 8 TB/s HBM peak.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -22,25 +21,15 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# (the digest of the kernel sources gates the committed counter summaries;
+# VALU_PEAK: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, a wave64 instruction
+# takes a SIMD 4 cycles, no packed forms)
+from kv_cache_tile_amd.pmc_digest import VALU_PEAK, kernel_source_digest  # noqa: E402
+
 HBM_PEAK_GBPS = 8000.0
 METRIC = "encode/decode GB/s of bf16 input (E8, 4 bps) at 1 GPU; % of HBM peak"
-KERNEL_SOURCES = ("kv_cache_tile_amd/csrc/hq_lib.hip", "kv_cache_tile_amd/csrc/hq_kernels.h",
-                  "kv_cache_tile_amd/csrc/hq_device.h", "kv_cache_tile_amd/csrc/hq_kern_e8.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_hbm_traffic.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "dit_stack_e8_4bps_counters.json")
-# vector instruction issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64
-# instruction takes a SIMD 4 cycles; no packed forms)
-VALU_PEAK = 256 * 4 * 16 * 2.4e9
-
-
-def kernel_source_digest() -> str:
-    """sha256 over the kernel sources: HBM traffic measured with the counters
-    is only reported while the kernels are the ones it was measured on."""
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
 
 
 def measured_traffic(kernel: str):
@@ -199,7 +188,11 @@ def all_configs(args):
         ms = sorted(a.elapsed_time(b) for a, b in evs)
         return ms[len(ms) // 2], ms[0]
 
-    for cfg, which, lat, bps, tile, kv in config_runs():
+    runs = config_runs()
+    only = None if args.only is None else [int(i) for i in args.only.split(",")]
+    for ri, (cfg, which, lat, bps, tile, kv) in enumerate(runs):
+        if only is not None and ri not in only:
+            continue
         x = tensor(cfg, which)
         x2 = x.reshape(-1, tile) if kv else x
         seed = workloads.codec_seed(cfg, which=which)
@@ -213,7 +206,7 @@ def all_configs(args):
         p = hq.plan(hq.BF16 if esz == 2 else hq.F32, x2.shape[0], x2.shape[1], tile, lat, bps, kv)
         alg = numel * (esz + bps / 8.0) + 4.0 * p.tiles + 4.0 * (p.chunks + 1)
         fits = 2 * numel * esz < (256 << 20)
-        rec = {"config": cfg, "tensor": which, "shape": list(x.shape), "dtype": str(x2.dtype).split(".")[-1],
+        rec = {"run": ri, "config": cfg, "tensor": which, "shape": list(x.shape), "dtype": str(x2.dtype).split(".")[-1],
                "lattice": lat, "bps_target": bps, "tile": tile, "dither": kv}
         for flush in ((False, True) if fits else (False,)):
             e_med, e_min = timed(enc, flush)
@@ -237,6 +230,8 @@ def all_configs(args):
         print(json.dumps(rec), flush=True)
         del xf, out, h
 
+    if only is not None:
+        return
     # closed-loop rate: bisection on the rate constant until the stored stream
     # is within 0.01 bps of the target, against the table's open-loop rate
     for cfg, which, lat, bps, tile, kv in closed_loop_runs():
@@ -363,6 +358,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the DiT stack: one JSON line per run of the other configurations "
                          "(weights 1024x1024 fp32, 4096x4096, 11008x4096 over all lattices, the KV cache)")
+    ap.add_argument("--only", default=None,
+                    help="with --configs: only these runs (comma-separated indices of the per-configuration "
+                         "runs, in the order the lines print), e.g. for one counter collection per run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the codec "

@@ -292,6 +292,11 @@ __device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, f
   for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
 }
 
+// Wave votes over the active lanes, straight from the comparison's lane mask
+// (a ballot of the condition, then a scalar test).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0ull; }
+__device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0ull; }
+
 // Index of the lowest set bit of w, all ones when w is 0 (v_ffbl_b32).  Written
 // as the instruction itself: the C builtin leaves w == 0 undefined, and the
 // compiler then folds the range checks that the fast unary path relies on.
@@ -331,29 +336,25 @@ struct UnaryWindow {
       nb += 32u;
     }
   }
-  // next code on the fast path; valid only while the running max of z stays < 31
-  __device__ __forceinline__ uint32_t take(uint32_t& zmax) {
-    const uint32_t z = ffbl(lo);
-    zmax = zmax > z ? zmax : z;
-    const uint32_t c = z + 1u;
-    lo = __builtin_amdgcn_alignbit(hi, lo, c);
-    hi = hi >> c;
-    nb -= c;
-    return z;
-  }
   // the next 8 codes on the fast path, read at increasing offsets into the
   // unchanged window (each from the 32 bits at its offset), then the window
-  // advances once.  Valid only while the running max of the codes and of the
-  // offsets stays below 31 (an offset past 30 would wrap the funnel shift).
+  // advances once.  The read is exact while every offset and every code stays
+  // below 31 (an offset past 30 would wrap the funnel shift).  Offsets grow
+  // by code + 1, so that is the last offset and the last code below 31: a
+  // slice with no one gives the code 0xFFFFFFFF, which leaves the offset
+  // where it was, so every later code reads the same slice and the last code
+  // is 0xFFFFFFFF too.  zmax = max(last offset, last code): >= 31 means the
+  // fast read is not exact.
   __device__ __forceinline__ void take8(uint32_t (&z)[8], uint32_t& zmax) {
     uint32_t off = 0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < 7; i++) {
       z[i] = ffbl(__builtin_amdgcn_alignbit(hi, lo, off));
-      const uint32_t m = z[i] > off ? z[i] : off;
-      zmax = zmax > m ? zmax : m;
       off = off + z[i] + 1u;
     }
+    z[7] = ffbl(__builtin_amdgcn_alignbit(hi, lo, off));
+    zmax = off > z[7] ? off : z[7];
+    off = off + z[7] + 1u;
     const uint64_t W = (((uint64_t)hi << 32) | lo) >> (off & 63u);
     lo = (uint32_t)W;
     hi = (uint32_t)(W >> 32);

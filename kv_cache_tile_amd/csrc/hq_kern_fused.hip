@@ -141,7 +141,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
         const uint32_t total = __builtin_amdgcn_readlane(inc, kChunkTiles - 1);
         const uint64_t pw0 = exists ? chunk_off[c] : 0, pw1 = exists ? chunk_off[c + 1] : 0;
         const bool range_ok = pw1 >= pw0 && pw1 <= payload_words && (pw1 - pw0) <= chunk_cap_words;
-        const bool too_long = __any(len > tile_bound);
+        const bool too_long = wave_any(len > tile_bound);
         const bool chunk_ok = exists && range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == pw1 - pw0;
         tok[wr * kChunkTiles + lane] =
             (chunk_ok && len >= B + (uint32_t)N * (kk + 1u) && (st == 0u || st - 0x180u < 0x7E00u)) ? 1u : 0u;
@@ -186,7 +186,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     uint32_t carry = 0;
     for (uint32_t r = 0;; r++) {
       const bool more = r * kUW * (uint32_t)LPT < nwu;
-      if (!__any(more)) break;
+      if (!wave_any(more)) break;
       const uint32_t j0 = (r * (uint32_t)LPT + (uint32_t)p_lane) * kUW;
       uint32_t c[kUW], cs = 0;
 #pragma unroll

@@ -254,6 +254,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   uint32_t* smask = misc + 4;                               // [N / 32] sign diagonal bits
   uint32_t* goff = smask + 8;                               // [2][kMaxGroupChunks] chunk word offsets per half
   uint32_t* started_copy = goff + 2 * kMaxGroupChunks;      // [kStartedWords] the started array, read ahead
+  uint32_t* emask = started_copy + kStartedWords;           // [LPT][16] per-pair sign masks of each lane
 
   const int tid = threadIdx.x;
   const int tau = tid / LPT;
@@ -270,8 +271,14 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   // the butterfly's lane sign folded in (inputs presigned per lane); the
   // barrier inside also publishes the epoch
   const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q) ^ (lane_sign_odd(q) ? 0xFFFFFFFFu : 0u);
-  uint32_t sgnw[2];
-  pair_sign_words(sgn, sgnw);
+  // the packed-pair form of every logical lane's mask, read back from LDS
+  // where the pairs are loaded (one xor a pair)
+  if (tid < 16 * LPT) {
+    const int qq = tid >> 4;
+    uint32_t W[2];
+    pair_sign_words(smask[qq] ^ (lane_sign_odd(qq) ? 0xFFFFFFFFu : 0u), W);
+    emask[tid] = pair_sign_mask(W, tid & 15);
+  }
   uint32_t k_prev = 0xFFu;                                  // Rice parameter of this lane's previous tile
   const uint32_t epoch = misc[2];
   uint32_t* started = ws + kStartedBase + (epoch & 1u) * kStartedWords;
@@ -359,7 +366,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
               done = done & ((h2 >> 2) == epoch) & ((h2 & 3u) != 0);
             }
           }
-          if (__all(done)) break;
+          if (wave_all(done)) break;
           if (++polls > spin_limit) { stalled = true; break; }
           __builtin_amdgcn_s_sleep(1);
         }
@@ -395,17 +402,33 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
       if (stalled) atomicOr(status, HQ_FLAG_STALL);
     }
   };
-  // all threads, after place() and a barrier: the placed group's words out,
-  // clearing its area behind them
+  // all threads, after place() and a barrier: the placed group's words out
+  // (16-byte stores at 16-byte payload offsets; the up to 3 words before the
+  // first and after the last one by one), then its area cleared (the group
+  // areas are 16-byte aligned, whole vectors)
   auto copy_out = [&]() {
     const uint32_t excl = misc[3];
     const bool store = pgfits && (uint64_t)excl + pgtotal <= cap_words;
     const uint32_t zw = pgtotal + 2 < grp_words ? pgtotal + 2 : grp_words;
     uint32_t* src = stage + (ph ? base1 : 0u);
-    for (uint32_t i = tid; i < zw; i += blockDim.x) {
-      if (store && i < pgtotal) payload[excl + i] = src[i];
-      src[i] = 0u;
+    if (store) {
+      const uint32_t e = excl + pgtotal;
+      const uint32_t a0 = (excl + 3u) & ~3u, a1 = e & ~3u;
+      const uint32_t nv = a1 > a0 ? (a1 - a0) >> 2 : 0u;
+      for (uint32_t v = tid; v < nv; v += blockDim.x) {
+        const uint32_t s0 = a0 - excl + 4u * v;
+        *reinterpret_cast<uint4*>(payload + a0 + 4u * v) = make_uint4(src[s0], src[s0 + 1], src[s0 + 2], src[s0 + 3]);
+      }
+      if (tid < 8) {
+        const uint32_t lo = tid < 4 ? excl : (a1 > a0 ? a1 : a0);
+        const uint32_t hi = tid < 4 ? (a0 < e ? a0 : e) : e;
+        const uint32_t i = lo + (uint32_t)(tid & 3);
+        if (i < hi) payload[i] = src[i - excl];
+      }
     }
+    __syncthreads();                                        // (every read of the area is done)
+    uint4* src4 = reinterpret_cast<uint4*>(src);
+    for (uint32_t v = tid; v < (zw + 3u) >> 2; v += blockDim.x) src4[v] = make_uint4(0u, 0u, 0u, 0u);
   };
 
   // this workgroup's expected share of chunks; priority falls by quarters of it
@@ -429,19 +452,18 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     // ---- load + sign diagonal (bf16 -> fp32 is exact; the sign bits are
     // flipped on the packed pairs) ----
     float a[kLaneElems];
-    uint32_t sw[2] = {sgnw[0], sgnw[1]}, sg = sgn;
-    opaque(sw[0]);
-    opaque(sw[1]);
+    uint32_t sg = sgn;
     opaque(sg);
     // (an inactive tile works on the last tile's data and stores nothing)
     if (bf16) {
+      const uint4* em = reinterpret_cast<const uint4*>(emask + 16 * q);
 #pragma unroll
       for (int v = 0; v < 4; v++) {
-        const uint4 w = pre[v];
-        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        const uint4 w = pre[v], m = em[v];
+        uint32_t ww[4] = {w.x, w.y, w.z, w.w}, mm[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
         for (int h = 0; h < 4; h++) {
-          uint32_t pw = ww[h] ^ pair_sign_mask(sw, 4 * v + h);
+          uint32_t pw = ww[h] ^ mm[h];
           opaque(pw);                                       // one xor per pair, then the two halves
           a[v * 8 + 2 * h] = as_f(pw << 16);
           a[v * 8 + 2 * h + 1] = as_f(pw & 0xFFFF0000u);
@@ -495,7 +517,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     const bool in_range = est >= 0x1p-90f && est <= 0x1p100f && r_est >= 0x1p-100f && r_est <= 0x1p100f;
     bool nonfinite = false;
     uint32_t sbits;
-    if (__any(near_tie || !in_range)) {
+    if (wave_any(near_tie || !in_range)) {
       asm volatile("");                                     // (rare: stays a branch)
       // the pinned tree as a running stack of partial sums: part[l] holds
       // the sum of the last complete block of 2^l squares
@@ -541,7 +563,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     const float qf = ydom ? inv : inv * inv_sqrtn;
 #pragma unroll
     for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * qf;
-    if (__any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
+    if (wave_any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
       asm volatile("");                                     // (stays a branch, not 32 selects)
       if (nonfinite) {
 #pragma unroll
@@ -601,7 +623,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < kLaneElems / 2; i++) mx |= S2[i];
-    const bool bytes = __all((mx & 0xFF00FF00u) == 0u);
+    const bool bytes = wave_all((mx & 0xFF00FF00u) == 0u);
     // R: the byte-packed symbols (R[j], byte m = symbol 4j + m) when every
     // symbol of the wave fits a byte, else the 16-bit pairs
     uint32_t R[kLaneElems / 2];
@@ -647,7 +669,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
         best_c = tot + (uint32_t)N * (1u + k);
       }
     }
-    if (__any(!settled)) {
+    if (wave_any(!settled)) {
       // rare: all eight sums, one k per (rolled) iteration, running minimum
       uint32_t bk = 0, bc = 0xFFFFFFFFu, bsum = 0;
 #pragma unroll 1
@@ -736,7 +758,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // (this wave's load of the started array)
         const uint32_t i = (uint32_t)(tid - 64), g = gridDim.x;
         const uint32_t want = 32u * i >= g ? 0u : (32u * (i + 1u) <= g ? 0xFFFFFFFFu : (1u << (g & 31u)) - 1u);
-        all_started = __all((started_copy[i] & want) == want);
+        all_started = wave_all((started_copy[i] & want) == want);
         checked = true;
       }
       if (tid == 64) next_ticket = take_ticket(ws, CG, epoch, all_started);
@@ -850,7 +872,7 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
     const uint32_t saved = uw.pos();                        // the group's first bit, for a re-read
     uint32_t z[8], zmax = 0;
     uw.take8(z, zmax);
-    if (__any(zmax >= 31u)) {
+    if (wave_any(zmax >= 31u)) {
       if (zmax >= 31u) {
         // rare: read the group again exactly (a rolled loop; codes shift in from the top)
         uw.init(stage, saved);
@@ -984,7 +1006,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     const uint32_t inc = wave_incl_scan(len);
     tile_off0[set * kChunkTiles + tid] = inc - len;
     const uint32_t total = __builtin_amdgcn_readlane(inc, kChunkTiles - 1);
-    const bool too_long = __any(len > tile_bound);          // longer than any valid tile can be
+    const bool too_long = wave_any(len > tile_bound);          // longer than any valid tile can be
     const bool chunk_ok = range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == pw1 - pw0;
     tile_ok0[set * kChunkTiles + tid] = (chunk_ok && len >= B + (uint32_t)N * (kk + 1u)) ? 1u : 0u;
     tile_ms0[set * kChunkTiles + tid] = mt | (st_ << 16);
@@ -1094,7 +1116,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     uint32_t carry = 0;
     for (uint32_t r = 0;; r++) {
       const bool more = r * kUW * (uint32_t)LPT < nw;
-      if (!__any(more)) break;
+      if (!wave_any(more)) break;
       const uint32_t j0 = (r * (uint32_t)LPT + (uint32_t)p_lane) * kUW;
       uint32_t c[kUW], cs = 0;
 #pragma unroll
@@ -1228,7 +1250,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       // a +0 step: the outputs' signs (bit i for element i) from the rebuilt
       // values' signs; the values themselves become +0
       uint32_t zsign = 0;
-      if (__any(zero_step && lane_ok)) {
+      if (wave_any(zero_step && lane_ok)) {
         asm volatile("");                                   // (rare: kept out of line)
         uint32_t m = 0;
 #pragma unroll
@@ -1248,11 +1270,11 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
         for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
       }
       const uint32_t sg = smask[q] ^ zsign;
-      uint32_t sw[2];
-      pair_sign_words(sg, sw);
       const uint64_t base = t * N + (uint64_t)q * kLaneElems;
       if (bf16) {
         uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + base);
+        uint32_t sw[2];
+        pair_sign_words(sg, sw);
 #pragma unroll
         for (int v = 0; v < 4; v++) {
           uint32_t w[4];

@@ -190,14 +190,15 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   size_t lds_cap = per_regs > 0 ? (size_t)lds_cu / (size_t)per_regs : (size_t)max_lds;
   if (lds_cap > (size_t)max_lds) lds_cap = (size_t)max_lds;
   lds_cap = lds_cap / kLdsGrain * kLdsGrain;
-  const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks + kStartedWords;
+  const size_t fixed_words = 2 * kChunkTiles + 4 + 8 + 2 * kMaxGroupChunks + kStartedWords + 16 * 8;
   const size_t avail = lds_cap / 4 > fixed_words ? lds_cap / 4 - fixed_words : 0;
   uint32_t group = kMaxGroupChunks, grp_words = 0;
+  // (group areas start on 16-byte boundaries: both sizes multiples of 4 words)
   for (;; group--) {
-    grp_words = group * P.chunk_words + 4;
-    if (grp_words <= avail || group == 1) break;
+    grp_words = (group * P.chunk_words + 4 + 3) & ~3u;
+    if (grp_words <= (avail & ~(size_t)3) || group == 1) break;
   }
-  const uint32_t stage_words = avail > grp_words ? (uint32_t)avail : grp_words;
+  const uint32_t stage_words = (avail & ~(size_t)3) > grp_words ? (uint32_t)(avail & ~(size_t)3) : grp_words;
   const size_t lds = (stage_words + fixed_words) * 4;
   if (lds > (size_t)max_lds) return HQ_EINVAL;
   int grid_full;
