@@ -292,6 +292,17 @@ __device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, f
   for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
 }
 
+// This wave's LDS writes made visible to its own later LDS reads (for data
+// exchanged among lanes of one wave, such as a tile's lanes): the writes are
+// waited for, and neither the compiler nor the scheduler moves accesses
+// across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Wave votes over the active lanes, straight from the comparison's lane mask
 // (a ballot of the condition, then a scalar test).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0ull; }

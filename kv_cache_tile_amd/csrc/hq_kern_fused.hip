@@ -57,18 +57,23 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
   constexpr uint32_t B = CB_LANE * LPT;
   static_assert(LAT != 2, "integer codes: Z, D4 or E8");
   static_assert(WAVES >= 2, "at least two waves");
+  static_assert(ROWS == 8, "the products buffer holds rows in two 16-byte halves");
 
+  // LDS; row strides padded against bank conflicts (MS: one word; CRS: two
+  // 16-byte vectors) and each tile's 32-byte code chunks rotated by its column
+  constexpr int MS = kChunkTiles + 1;                       // words per row of the tile tables
+  constexpr int CRS = TC * N / 4 + 8;                       // words per row of codes
   extern __shared__ uint32_t smem[];
   uint32_t* stage0 = smem;                                  // [2][ROWS][seg_words] units' bits + guard
-  uint32_t* toff = stage0 + 2 * ROWS * seg_words;           // [ROWS][64] tile bit offsets in the chunk
-  uint32_t* tms = toff + ROWS * kChunkTiles;                // [ROWS][64] meta | step << 16
-  uint32_t* tok = tms + ROWS * kChunkTiles;                 // [ROWS][64] tile valid
-  uint32_t* cinfo = tok + ROWS * kChunkTiles;               // [ROWS][4] chunk's first word (lo, hi), valid
+  uint32_t* toff = stage0 + 2 * ROWS * seg_words;           // [ROWS][MS] tile bit offsets in the chunk
+  uint32_t* tms = toff + ROWS * MS;                         // [ROWS][MS] meta | step << 16
+  uint32_t* tok = tms + ROWS * MS;                          // [ROWS][MS] tile valid
+  uint32_t* cinfo = tok + ROWS * MS;                        // [ROWS][4] chunk's first word (lo, hi), valid
   uint32_t* adj = cinfo + 4 * ROWS;                         // [2][ROWS] stage bit of a chunk's bit 0
-  float* sscale = reinterpret_cast<float*>(adj + 2 * ROWS);  // [32][64] activation scales of the column
+  float* sscale = reinterpret_cast<float*>(adj + 2 * ROWS);  // [64][32] activation scales of the column
   uint32_t* ustart = reinterpret_cast<uint32_t*>(sscale + kFusedBatch * kChunkTiles);   // [THREADS]
-  uint32_t* codes = ustart + THREADS;                       // [ROWS][TC][N / 4] int8 codes 2P
-  int32_t* ibuf = reinterpret_cast<int32_t*>(codes + ROWS * TC * N / 4);   // [TC][32][ROWS] tile products
+  uint32_t* codes = ustart + THREADS;                       // [ROWS][CRS] int8 codes 2P
+  int32_t* ibuf = reinterpret_cast<int32_t*>(codes + ROWS * CRS);   // [TC][32][ROWS] tile products
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -95,9 +100,9 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     const uint32_t pn = tn % kChunkTiles;
     for (int j = wave; j < ROWS; j += WAVES) {
       const bool cok = __builtin_amdgcn_readfirstlane(cinfo[4 * j + 2]) != 0u;
-      const uint32_t first = __builtin_amdgcn_readfirstlane(toff[j * kChunkTiles + pn]);
-      const uint32_t lastm = __builtin_amdgcn_readfirstlane(tms[j * kChunkTiles + pn + TC - 1]) & 0xFFFFu;
-      const uint32_t endb = __builtin_amdgcn_readfirstlane(toff[j * kChunkTiles + pn + TC - 1]) + (lastm >> 3);
+      const uint32_t first = __builtin_amdgcn_readfirstlane(toff[j * MS + pn]);
+      const uint32_t lastm = __builtin_amdgcn_readfirstlane(tms[j * MS + pn + TC - 1]) & 0xFFFFu;
+      const uint32_t endb = __builtin_amdgcn_readfirstlane(toff[j * MS + pn + TC - 1]) + (lastm >> 3);
       const uint64_t cw0 = ((uint64_t)__builtin_amdgcn_readfirstlane(cinfo[4 * j + 1]) << 32) |
                            __builtin_amdgcn_readfirstlane(cinfo[4 * j]);
       const uint64_t L = (cw0 + (first >> 5)) & ~3ull;
@@ -137,15 +142,15 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
         const uint32_t st = exists ? step[c * kChunkTiles + lane] : 0u;
         const uint32_t len = mt >> 3, kk = mt & 7u;
         const uint32_t inc = wave_incl_scan(len);
-        toff[wr * kChunkTiles + lane] = inc - len;
+        toff[wr * MS + lane] = inc - len;
         const uint32_t total = __builtin_amdgcn_readlane(inc, kChunkTiles - 1);
         const uint64_t pw0 = exists ? chunk_off[c] : 0, pw1 = exists ? chunk_off[c + 1] : 0;
         const bool range_ok = pw1 >= pw0 && pw1 <= payload_words && (pw1 - pw0) <= chunk_cap_words;
         const bool too_long = wave_any(len > tile_bound);
         const bool chunk_ok = exists && range_ok && !too_long && (uint64_t)((total + 31u) >> 5) == pw1 - pw0;
-        tok[wr * kChunkTiles + lane] =
+        tok[wr * MS + lane] =
             (chunk_ok && len >= B + (uint32_t)N * (kk + 1u) && (st == 0u || st - 0x180u < 0x7E00u)) ? 1u : 0u;
-        tms[wr * kChunkTiles + lane] = mt | (st << 16);
+        tms[wr * MS + lane] = mt | (st << 16);
         if (lane == 0) {
           cinfo[4 * wr] = (uint32_t)pw0;
           cinfo[4 * wr + 1] = (uint32_t)(pw0 >> 32);
@@ -153,8 +158,8 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
         }
       }
       for (int i = tid; i < kFusedBatch * kChunkTiles; i += THREADS) {
-        const uint64_t bb = b0 + (uint64_t)(i / kChunkTiles);
-        sscale[i] = bb < batch ? scale[bb * tpr + t0 + (uint32_t)(i % kChunkTiles)] : 0.0f;
+        const uint64_t bb = b0 + (uint64_t)(i % kFusedBatch);
+        sscale[i] = bb < batch ? scale[bb * tpr + t0 + (uint32_t)(i / kFusedBatch)] : 0.0f;
       }
       __syncthreads();
       stage_in(t0, cur);                                    // (the first unit of the column: not ahead)
@@ -164,15 +169,28 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     // streaming into the other buffer during this unit's parse
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // the first half of this wave's first column's activation operands, in
+    // flight during the parse (the rest is loaded after it)
+    constexpr int KS = N / 32, KE = KS / 2;
+    const fz_i32x4 zero4 = {0, 0, 0, 0};
+    const int half = (lane >> 5) * 16;
+    const uint64_t bbl = b0 + (uint64_t)(lane & 31);
+    fz_i32x4 bv0[KE];
+    {
+      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)(t0 + (uint32_t)wave) * N;
+#pragma unroll
+      for (int ks = 0; ks < KE; ks++)
+        bv0[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
+    }
     if (t0 + TC < tpr && (t0 + TC) % kChunkTiles != 0) stage_in(t0 + TC, cur ^ 1);
     const uint32_t* stage = stage0;
 
     // ---- parse: the tile of (row jrow, column tcol) ----
     const uint32_t pos = p0 + (uint32_t)tcol;
-    const uint32_t ms = tms[jrow * kChunkTiles + pos];
+    const uint32_t ms = tms[jrow * MS + pos];
     const uint32_t len = (ms & 0xFFFFu) >> 3, k = ms & 7u;
-    bool ok = tok[jrow * kChunkTiles + pos] != 0u && r0 + (uint64_t)jrow < rows;
-    const uint32_t start = adj[cur * ROWS + jrow] + toff[jrow * kChunkTiles + pos];
+    bool ok = tok[jrow * MS + pos] != 0u && r0 + (uint64_t)jrow < rows;
+    const uint32_t start = adj[cur * ROWS + jrow] + toff[jrow * MS + pos];
     const uint32_t end = start + len;
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
     // where each lane's first unary code starts (the decoder's search: ones
@@ -212,7 +230,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
       carry += tot;
     }
     ok = ok && carry == (uint32_t)N;
-    __syncthreads();
+    wave_lds_sync();                                        // (a tile's lanes are in one wave)
 
     float a[kLaneElems];
     bool lane_ok;
@@ -269,7 +287,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
         w[v] = pk;
       }
       if (real && over) atomicOr(status, HQ_FLAG_RANGE);
-      uint4* dst = reinterpret_cast<uint4*>(codes + ((jrow * TC + tcol) * N + q * kLaneElems) / 4);
+      uint4* dst = reinterpret_cast<uint4*>(codes + jrow * CRS + tcol * (N / 4) + ((q + tcol) % LPT) * 8);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
@@ -283,25 +301,27 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     // column's activation operands are loaded before the codes are read. ----
     for (int c = wave; c < TC; c += WAVES) {
       const uint32_t t = t0 + (uint32_t)c;
-      const int arow = lane & 31, half = (lane >> 5) * 16;
-      const uint64_t bb = b0 + (uint64_t)(lane & 31);
-      const int8_t* brow = qa + bb * (uint64_t)tpr * N + (uint64_t)t * N;
-      const fz_i32x4 zero4 = {0, 0, 0, 0};
-      fz_i32x4 bv[N / 32];
+      const int arow = lane & 31;
+      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)t * N;
+      fz_i32x4 bv[KS];
 #pragma unroll
-      for (int ks = 0; ks < N / 32; ks++)
-        bv[ks] = bb < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
+      for (int ks = 0; ks < KS; ks++) {
+        if (ks < KE && c == wave) bv[ks] = bv0[ks];
+        else bv[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
+      }
       if (c == wave) __syncthreads();                       // (every wave: the codes are in LDS)
       fz_i32x16 I = {};
 #pragma unroll
       for (int ks = 0; ks < N / 32; ks++) {
         const fz_i32x4 av = arow < ROWS
-            ? *reinterpret_cast<const fz_i32x4*>(codes + ((arow * TC + c) * N + 32 * ks + half) / 4) : zero4;
+            ? *reinterpret_cast<const fz_i32x4*>(codes + arow * CRS + c * (N / 4) + ((ks + c) % LPT) * 8 + half / 4)
+            : zero4;
         I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv[ks], I, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        ibuf[(c * kFusedBatch + (lane & 31)) * ROWS + (lane >> 5) * 4 + i] = I[i];
+      // rows 4h .. 4h + 3 of activation b as one 16-byte store, the halves
+      // swapped for b = 8..15 and 24..31 (16 lanes, 16 distinct bank groups)
+      const int b = lane & 31, hs = (lane >> 5) ^ ((b >> 3) & 1);
+      *reinterpret_cast<fz_i32x4*>(ibuf + (c * kFusedBatch + b) * ROWS + hs * 4) = fz_i32x4{I[0], I[1], I[2], I[3]};
     }
     __syncthreads();
 
@@ -313,9 +333,10 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
         const int cb = e / ROWS, cj = e % ROWS;
 #pragma unroll
         for (int c = 0; c < TC; c++) {
-          const float s = as_f((tms[cj * kChunkTiles + p0 + c] >> 16) << 16);
-          const float av = sscale[cb * kChunkTiles + p0 + c];
-          acc[i] = __builtin_fmaf((float)ibuf[(c * kFusedBatch + cb) * ROWS + cj], s * av, acc[i]);
+          const float s = as_f((tms[cj * MS + p0 + c] >> 16) << 16);
+          const float av = sscale[(p0 + c) * kFusedBatch + cb];
+          const int js = (((cj >> 2) ^ ((cb >> 3) & 1)) << 2) | (cj & 3);   // (the halves' swap)
+          acc[i] = __builtin_fmaf((float)ibuf[(c * kFusedBatch + cb) * ROWS + js], s * av, acc[i]);
         }
       }
     }
@@ -347,8 +368,8 @@ const void* fused_fn(uint32_t lattice, uint32_t n, uint32_t seg_words, uint32_t*
   if (!f) return nullptr;
   const uint32_t th = (uint32_t)(kFusedRows * kFusedCols) * (n / kLaneElems);
   *threads = th;
-  *lds = 4 * (2 * (size_t)kFusedRows * seg_words + 3 * kFusedRows * kChunkTiles + 4 * kFusedRows +
-              2 * kFusedRows + kFusedBatch * kChunkTiles + th + (size_t)kFusedRows * kFusedCols * n / 4 +
+  *lds = 4 * (2 * (size_t)kFusedRows * seg_words + 3 * kFusedRows * (kChunkTiles + 1) + 4 * kFusedRows +
+              2 * kFusedRows + kFusedBatch * kChunkTiles + th + (size_t)kFusedRows * (kFusedCols * n / 4 + 8) +
               (size_t)kFusedCols * kFusedBatch * kFusedRows);
   return (const void*)f;
 }

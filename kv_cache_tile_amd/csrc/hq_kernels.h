@@ -951,18 +951,21 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   constexpr uint32_t CB_LANE = LatticeTraits<LAT>::coset * BPL;
   constexpr uint32_t B = CB_LANE * LPT;
 
-  // Two buffer sets, used by alternate units: while a unit is decoded from
+  // Two stage buffers, used by alternate units: while a unit is decoded from
   // one, the next unit's words stream into the other (global -> LDS loads in
   // flight during the decode), and wave 0 has scanned its chunk from tile
-  // metadata it loaded a unit earlier.  No global load is waited for on the
-  // critical path; two barriers per unit.
+  // metadata it loaded a unit earlier.  The scan's tables rotate over three
+  // sets: wave 0 writes the next unit's before the unit's barrier, while
+  // another wave may still be a unit behind it, reading its own unit's set
+  // (the barrier keeps every wave within one unit of the others).  No global
+  // load is waited for on the critical path; one barrier per unit.
   extern __shared__ uint32_t smem[];
   uint32_t* stage0 = smem;                                  // [2][stage_words] a unit's words + guard
-  uint32_t* tile_off0 = smem + 2 * stage_words;             // [2][64] bit offset of each tile in the chunk
-  uint32_t* tile_ok0 = tile_off0 + 2 * kChunkTiles;         // [2][64]
-  uint32_t* tile_ms0 = tile_ok0 + 2 * kChunkTiles;          // [2][64] meta | step << 16
-  uint32_t* misc0 = tile_ms0 + 2 * kChunkTiles;             // [2][4] see scan()
-  uint32_t* pmeta0 = misc0 + 8;                             // [2][64] a chunk's meta, loaded ahead
+  uint32_t* tile_off0 = smem + 2 * stage_words;             // [3][64] bit offset of each tile in the chunk
+  uint32_t* tile_ok0 = tile_off0 + 3 * kChunkTiles;         // [3][64]
+  uint32_t* tile_ms0 = tile_ok0 + 3 * kChunkTiles;          // [3][64] meta | step << 16
+  uint32_t* misc0 = tile_ms0 + 3 * kChunkTiles;             // [3][4] see scan()
+  uint32_t* pmeta0 = misc0 + 12;                            // [2][64] a chunk's meta, loaded ahead
   uint32_t* pstep0 = pmeta0 + 2 * kChunkTiles;              // [2][64] and its steps
   uint32_t* ustart = pstep0 + 2 * kChunkTiles;              // [TPW * LPT] first unary bit per lane
   uint32_t* smask = ustart + TPW * LPT;                     // [N / 32] sign diagonal bits
@@ -1027,13 +1030,14 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       misc0[set * 4 + 3] = (uint32_t)(L >> 32);
     }
   };
-  // all threads: start the unit's words streaming into its stage (16 bytes a
-  // lane, straight to LDS; the stream's last, partial vector by plain loads)
-  // and zero the guard words behind them
-  auto stage_in = [&](int set) {
-    const uint32_t nvec = __builtin_amdgcn_readfirstlane(misc0[set * 4 + 1]);
-    const uint64_t L = (uint64_t)__builtin_amdgcn_readfirstlane(misc0[set * 4 + 2]) |
-                       ((uint64_t)__builtin_amdgcn_readfirstlane(misc0[set * 4 + 3]) << 32);
+  // all threads: start the unit's words (its scan in table set ts) streaming
+  // into stage buffer buf (16 bytes a lane, straight to LDS; the stream's
+  // last, partial vector by plain loads) and zero the guard words behind them
+  auto stage_in = [&](int buf, int ts) {
+    const uint32_t nvec = __builtin_amdgcn_readfirstlane(misc0[ts * 4 + 1]);
+    const uint64_t L = (uint64_t)__builtin_amdgcn_readfirstlane(misc0[ts * 4 + 2]) |
+                       ((uint64_t)__builtin_amdgcn_readfirstlane(misc0[ts * 4 + 3]) << 32);
+    const int set = buf;
     uint32_t* st = stage0 + set * stage_words;
     uint32_t lt = (uint32_t)tid;
     opaque(lt);                                             // (recomputed here, not held across the unit)
@@ -1058,31 +1062,32 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
   const uint64_t units = C * SUB;
   // priority by the units this workgroup has left (the current one included)
   uint64_t left = blockIdx.x < units ? (units - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
-  // unit k (k-th of this workgroup) uses buffer set k & 1; its metadata
-  // slot is k & 1 as well
+  // unit k (k-th of this workgroup) uses stage buffer k & 1, metadata slot
+  // k & 1 and table set k mod 3
   if (blockIdx.x < units) {
     fetch(blockIdx.x, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (tid < 64) scan(blockIdx.x, 0, 0);
     if (blockIdx.x + gridDim.x < units) fetch(blockIdx.x + gridDim.x, 1);
     __syncthreads();
-    stage_in(0);
+    stage_in(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  int cur = 0;
-  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x, cur ^= 1) {
+  int cur = 0, ts = 0;
+  for (uint64_t unit = blockIdx.x; unit < units; unit += gridDim.x, cur ^= 1, ts = ts == 2 ? 0 : ts + 1) {
     wave_priority(left >= 4u ? 3u : (uint32_t)left - 1u);
     left--;
     const uint64_t un = unit + gridDim.x;
+    const int tn = ts == 2 ? 0 : ts + 1;                    // the next unit's table set
     // this unit's words have landed (each wave waited for its own loads
     // before its previous stores, the barrier waits for everyone's); wave 0
     // scans the next unit
     if (un < units) {
-      if (tid < 64) scan(un, cur ^ 1, cur ^ 1);
+      if (tid < 64) scan(un, tn, cur ^ 1);
       if (un + gridDim.x < units) fetch(un + gridDim.x, cur);   // (issued before the stage loads)
     }
     __syncthreads();
-    if (un < units) stage_in(cur ^ 1);
+    if (un < units) stage_in(cur ^ 1, tn);
 
     const uint32_t* stage = stage0 + cur * stage_words;
     const uint64_t chunk = unit / SUB;
@@ -1090,14 +1095,14 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     const int ct = first + tau;                             // tile index in the chunk
     const uint64_t t = chunk * kChunkTiles + (uint64_t)ct;
     const bool active = t < T;
-    const uint32_t ms = tile_ms0[cur * kChunkTiles + ct];
+    const uint32_t ms = tile_ms0[ts * kChunkTiles + ct];
     const uint32_t m = active ? (ms & 0xFFFFu) : 0u;
     const uint32_t len = m >> 3, k = m & 7u;
     const uint32_t sraw = active ? (ms >> 16) : 0u;
     // the encoder writes +0 or a finite step of at least 2^-124, nothing
     // else: any other step marks a corrupt tile
-    bool ok = active && tile_ok0[cur * kChunkTiles + ct] != 0u && (sraw == 0u || sraw - 0x180u < 0x7E00u);
-    const uint32_t start = tile_off0[cur * kChunkTiles + ct] - misc0[cur * 4 + 0], end = start + len;
+    bool ok = active && tile_ok0[ts * kChunkTiles + ct] != 0u && (sraw == 0u || sraw - 0x180u < 0x7E00u);
+    const uint32_t start = tile_off0[ts * kChunkTiles + ct] - misc0[ts * 4 + 0], end = start + len;
     const uint32_t ub = start + B + (uint32_t)N * k;        // unary plane
 
     // ---- where does each lane's first unary code start?  Every codeword has
@@ -1106,8 +1111,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     // end), kUW consecutive words per physical lane per round, so the usual
     // tile takes one round.  The lane whose word holds the (32 q)-th one
     // records that word's index and the one's rank in it for logical lane q
-    // (index < 2^27, rank < 32: one word), and after the barrier lane q finds
-    // the bit itself: one select per lane. ----
+    // (index < 2^27, rank < 32: one word), and after a wave-level sync (a
+    // tile's lanes share a wave) lane q finds the bit itself: one select per
+    // lane. ----
     constexpr uint32_t kUW = 3;
     const uint32_t a0 = ub >> 5;
     const uint32_t nw = ok ? ((end - 1u) >> 5) - a0 + 1u : 0u;   // ok: end - ub >= N
@@ -1142,7 +1148,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       carry += tot;
     }
     ok = ok && carry == (uint32_t)N;
-    __syncthreads();
+    wave_lds_sync();                                        // (a tile's lanes are in one wave)
 
     // ---- parse and rebuild, specialised on the tile's Rice parameter; a lane
     // of an invalid tile reads from bit 0 with no run limit (in bounds, result

@@ -271,7 +271,9 @@ int do_decode(const Plan& P, const uint32_t* payload, uint64_t payload_words, co
   // readers' guard (8); each of the two stages a multiple of 16 bytes
   const uint32_t stage_words =
       ((uint32_t)(((uint64_t)tpw * P.bound + 31) / 32) + 1 + 3 + 3 + 8 + 3) & ~3u;
-  const size_t lds = (size_t)(2 * stage_words + 5 * 2 * kChunkTiles + 8 + tpw * lpt + 8) * 4;
+  // stages, 3 table sets (offsets, flags, meta|step) + 3 x 4 words, 2
+  // metadata slots (meta, step), the lanes' unary starts, the sign words
+  const size_t lds = (size_t)(2 * stage_words + 3 * 3 * kChunkTiles + 12 + 2 * 2 * kChunkTiles + tpw * lpt + 8) * 4;
   int grid;
   rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
   if (rc) return rc;

@@ -18,6 +18,9 @@ kernel sources), plus a markdown table on stdout.
   python -m kv_cache_tile_amd.pmc_digest table --run LABEL=DIR ... --numel LABEL=N ...
       one markdown row per (label, kernel) from SQ runs, for per-configuration
       tables.
+  python -m kv_cache_tile_amd.pmc_digest trace --dir DIR
+      the kernel-trace statistics (rocprofv3 --kernel-trace --stats) as a
+      markdown table.
 """
 import argparse
 import csv
@@ -77,8 +80,17 @@ def per_dispatch(rows):
     return dict(sorted(out.items()))
 
 
-def averages(dispatches, pattern=None):
-    """{kernel key: {"dispatches": n, counter: mean per dispatch}}"""
+def averages(dispatches, pattern=None, last=0):
+    """{kernel key: {"dispatches": n, counter: mean per dispatch}}, over
+    each kernel's last `last` dispatches (0: all)"""
+    if last:
+        keep, seen = set(), {}
+        for did, (name, _) in reversed(list(dispatches.items())):
+            k = kernel_key(name)
+            if seen.get(k, 0) < last:
+                seen[k] = seen.get(k, 0) + 1
+                keep.add(did)
+        dispatches = {d: v for d, v in dispatches.items() if d in keep}
     acc = {}
     for _, (name, cs) in dispatches.items():
         if pattern and not re.search(pattern, name):
@@ -92,11 +104,11 @@ def averages(dispatches, pattern=None):
                 **{c: v / a["dispatches"] for c, v in a["sums"].items()}} for k, a in acc.items()}
 
 
-def sq_summary(dirs, numel):
+def sq_summary(dirs, numel, last=0):
     d = {}
     for dd in dirs:
         d.update({(dd, k): v for k, v in per_dispatch(read_rows(dd)).items()})
-    avg = averages({i: v for i, v in enumerate(d.values())}, r"hq::")
+    avg = averages({i: v for i, v in enumerate(d.values())}, r"hq::", last)
     out = {}
     for k, a in avg.items():
         rec = {"dispatches": a["dispatches"], "kernel_name": a["name"]}
@@ -120,8 +132,8 @@ def sq_summary(dirs, numel):
 
 
 def cmd_sq(args):
-    ks = sq_summary(args.run, args.numel)
-    rec = {"workload": args.workload, "command": args.command, "numel": args.numel,
+    ks = sq_summary(args.run, args.numel, args.last)
+    rec = {"workload": args.workload, "command": args.command, "numel": args.numel, "last_dispatches": args.last,
            "kernel_source_sha256": kernel_source_digest(), "kernels": ks}
     with open(args.out, "w") as f:
         json.dump(rec, f, indent=1)
@@ -146,7 +158,7 @@ def cmd_traffic(args):
     mib_kib = args.copy_mib * 1024.0
     fk, wk = copy_reading(fd, "FETCH_SIZE"), copy_reading(wd, "WRITE_SIZE")
     fs, ws = mib_kib / fk, mib_kib / wk
-    fa, wa = averages(fd, r"hq::"), averages(wd, r"hq::")
+    fa, wa = averages(fd, r"hq::", args.last), averages(wd, r"hq::", args.last)
     ks = {}
     for k in sorted(set(fa) & set(wa)):
         rb = fa[k]["FETCH_SIZE"] * 1024.0 * fs
@@ -155,7 +167,8 @@ def cmd_traffic(args):
                  "fetch_kib": round(fa[k]["FETCH_SIZE"], 1), "write_kib": round(wa[k]["WRITE_SIZE"], 1),
                  "hbm_read_bytes": int(rb), "hbm_write_bytes": int(wb), "hbm_bytes_per_launch": int(rb + wb),
                  "algorithmic_bytes_per_launch": args.alg, "ratio_to_algorithmic": round((rb + wb) / args.alg, 4)}
-    rec = {"workload": args.workload, "command": args.command, "kernel_source_sha256": kernel_source_digest(),
+    rec = {"workload": args.workload, "command": args.command, "last_dispatches": args.last,
+           "kernel_source_sha256": kernel_source_digest(),
            "copy_reference": {"kernel": f"dispatch matching {args.copy_pattern!r}, {args.copy_mib} MiB read + "
                                         f"{args.copy_mib} MiB written",
                               "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
@@ -187,6 +200,44 @@ def cmd_table(args):
                   f"{r.get('lds_bank_conflict_cycles_per_launch', '')} | {r.get('valu_roof_us', '')} |")
 
 
+def short_name(name: str) -> str:
+    """hq::encode_kernel<8, 256, false, true>(...) -> encode_kernel<E8, 256, no dither, bf16 input>;
+    other kernels: the demangled name up to its argument list, cut to 70 characters."""
+    lat = {"1": "Z", "2": "A2", "4": "D4", "8": "E8"}
+    m = re.search(r"hq::(encode_kernel|decode_kernel|fused_product_kernel|nearest_kernel)<([^>]*)>", name)
+    if m:
+        a = [x.strip() for x in m.group(2).split(",")]
+        parts = [lat.get(a[0], a[0])] + a[1:2]
+        if m.group(1) == "encode_kernel" and len(a) >= 4:
+            parts += ["dither" if a[2] == "true" else "no dither", "bf16 input" if a[3] == "true" else "fp32 input"]
+        elif m.group(1) == "decode_kernel" and len(a) >= 3:
+            parts += ["dither" if a[2] == "true" else "no dither"] + (["int8 codes"] if len(a) > 3 and a[3] == "true" else [])
+        return f"{m.group(1)}<{', '.join(parts)}>"
+    m = re.search(r"hq::(\w+)", name)
+    if m:
+        return m.group(1) + (re.search(r"<[^>]*>", name[m.end():]) or [""])[0] if "<" in name[m.end():m.end() + 1] else m.group(1)
+    base = name.replace("(anonymous namespace)::", "").split("(")[0]
+    base = re.sub(r"^void\s+", "", base)
+    base = re.sub(r"^(at::native::|\(anonymous namespace\)::)+", "", base)
+    return base[:70]
+
+
+def cmd_trace(args):
+    files = sorted(glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {args.dir}")
+    rows = []
+    with open(files[0], newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append({k.strip().lower(): v for k, v in r.items() if k is not None})
+    rows.sort(key=lambda r: -float(r.get("totaldurationns", 0)))
+    print("| kernel | calls | average us | min us | max us | % of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows[:args.top]:
+        print(f"| `{short_name(r['name'])}` | {r['calls']} | {float(r['averagens']) / 1000:.1f} | "
+              f"{float(r['minns']) / 1000:.1f} | {float(r['maxns']) / 1000:.1f} | {float(r['percentage']):.1f} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -196,6 +247,7 @@ def main(argv=None):
     a.add_argument("--workload", required=True)
     a.add_argument("--command", required=True)
     a.add_argument("--out", required=True)
+    a.add_argument("--last", type=int, default=0, help="each kernel's last N dispatches only (0: all)")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -205,11 +257,15 @@ def main(argv=None):
     b.add_argument("--workload", required=True)
     b.add_argument("--command", required=True)
     b.add_argument("--out", required=True)
+    b.add_argument("--last", type=int, default=0, help="each kernel's last N dispatches only (0: all)")
     c = sub.add_parser("table")
     c.add_argument("--run", action="append", required=True)
     c.add_argument("--numel", action="append", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--dir", required=True)
+    t.add_argument("--top", type=int, default=12)
     args = ap.parse_args(argv)
-    {"sq": cmd_sq, "traffic": cmd_traffic, "table": cmd_table}[args.cmd](args)
+    {"sq": cmd_sq, "traffic": cmd_traffic, "table": cmd_table, "trace": cmd_trace}[args.cmd](args)
 
 
 if __name__ == "__main__":
