@@ -80,7 +80,11 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
   const int tau = tid / LPT;                                // tile of the unit
   const int p_lane = tid % LPT;
   const int q = tile_lane<LPT>(p_lane);                     // logical lane
-  const int jrow = tau / TC, tcol = tau % TC;               // its row and column in the unit
+  // tiles column-major in the unit: wave w holds the CPW whole columns
+  // w CPW .. w CPW + CPW - 1 (all ROWS rows), which it also multiplies
+  constexpr int CPW = TC / WAVES;
+  static_assert(CPW * WAVES == TC && ROWS * LPT * CPW == 64, "a wave holds whole columns");
+  const int jrow = tau % ROWS, tcol = tau / ROWS;           // its row and column in the unit
   const uint64_t r0 = (uint64_t)blockIdx.x * ROWS;
   const uint64_t b0 = (uint64_t)blockIdx.y * kFusedBatch;
   const uint32_t cpr = tpr / kChunkTiles;                   // chunks per row
@@ -177,7 +181,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     const uint64_t bbl = b0 + (uint64_t)(lane & 31);
     fz_i32x4 bv0[KE];
     {
-      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)(t0 + (uint32_t)wave) * N;
+      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)(t0 + (uint32_t)(wave * CPW)) * N;
 #pragma unroll
       for (int ks = 0; ks < KE; ks++)
         bv0[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
@@ -291,25 +295,24 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
-    static_assert(WAVES <= TC, "every wave reaches the codes barrier once");
 
-    // ---- the tile products on the matrix cores: wave w takes columns w,
-    // w + waves, ...; operand A = codes (lane l: row l % 32, zero past ROWS),
+    // ---- the tile products on the matrix cores: each wave takes the columns
+    // it parsed (no block barrier); operand A = codes (lane l: row l % 32, zero past ROWS),
     // B = activations (lane l: activation l % 32), 16 bytes each at the
     // 16-byte half l / 32 of every 32-code step; output register i of lane l
-    // holds row (i / 4) 8 + (l / 32) 4 + i % 4, activation l % 32.  A
-    // column's activation operands are loaded before the codes are read. ----
-    for (int c = wave; c < TC; c += WAVES) {
+    // holds row (i / 4) 8 + (l / 32) 4 + i % 4, activation l % 32. ----
+    wave_lds_sync();                                        // (this wave's columns' codes are in LDS)
+    for (int cc = 0; cc < CPW; cc++) {
+      const int c = wave * CPW + cc;
       const uint32_t t = t0 + (uint32_t)c;
       const int arow = lane & 31;
       const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)t * N;
       fz_i32x4 bv[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
-        if (ks < KE && c == wave) bv[ks] = bv0[ks];
+        if (ks < KE && cc == 0) bv[ks] = bv0[ks];
         else bv[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
       }
-      if (c == wave) __syncthreads();                       // (every wave: the codes are in LDS)
       fz_i32x16 I = {};
 #pragma unroll
       for (int ks = 0; ks < N / 32; ks++) {
