@@ -313,7 +313,7 @@ def all_configs(args):
     fst = torch.zeros(1, dtype=torch.int32, device=dev)
     yf = hq.codes_matmul_fused(h, q, sc, fst)
     d_med, _ = timed(lambda: hq.decode_codes(h, out=codes), False)
-    a_med, _ = timed(lambda: hq.act_quant(xa, 256, seed), False)
+    a_med, _ = timed(lambda: hq.act_quant(xa, 256, seed, out=(q, sc)), False)
     wk = torch.empty(32 * 4096 * 64, dtype=torch.int32, device=dev)
     m_med, _ = timed(lambda: hq.codes_matmul(codes, h.step, 256, q, sc, out=yv, work=wk), False)
     f_med, _ = timed(lambda: hq.codes_matmul_fused(h, q, sc, fst, out=yf), False)

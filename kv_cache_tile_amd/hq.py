@@ -422,12 +422,19 @@ def codes_matmul_fused(h: HQTensor, q: torch.Tensor, scale: torch.Tensor, status
     return out
 
 
-def act_quant(x: torch.Tensor, tile: int, seed: int) -> tuple:
-    """Per-tile RHT of activations x [batch][cols] in int8, with fp32 scales."""
+def act_quant(x: torch.Tensor, tile: int, seed: int, out: tuple | None = None) -> tuple:
+    """Per-tile RHT of activations x [batch][cols] in int8, with fp32 scales
+    (into out = (q, scale) when given)."""
     x2 = x.reshape(-1, x.shape[-1]).contiguous()
     B, cols = x2.shape
-    q = torch.empty((B, cols), dtype=torch.int8, device=x.device)
-    sc = torch.empty((B, cols // tile), dtype=torch.float32, device=x.device)
+    if out is not None:
+        q, sc = out
+        if q.shape != (B, cols) or q.dtype != torch.int8 or sc.shape != (B, cols // tile) or \
+                sc.dtype != torch.float32 or not (q.is_contiguous() and sc.is_contiguous()):
+            raise ValueError("act_quant: out must be int8 [batch][cols] and fp32 [batch][cols / tile], contiguous")
+    else:
+        q = torch.empty((B, cols), dtype=torch.int8, device=x.device)
+        sc = torch.empty((B, cols // tile), dtype=torch.float32, device=x.device)
     _check(lib().hq_act_quant(x2.data_ptr(), _dtype_code(x2.dtype), B, cols, tile, seed, q.data_ptr(),
                               sc.data_ptr(), _stream(x.device)))
     return q, sc
