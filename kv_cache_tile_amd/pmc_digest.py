@@ -18,9 +18,10 @@ kernel sources), plus a markdown table on stdout.
   python -m kv_cache_tile_amd.pmc_digest table --run LABEL=DIR ... --numel LABEL=N ...
       one markdown row per (label, kernel) from SQ runs, for per-configuration
       tables.
-  python -m kv_cache_tile_amd.pmc_digest trace --dir DIR
+  python -m kv_cache_tile_amd.pmc_digest trace --dir DIR [--last N]
       the kernel-trace statistics (rocprofv3 --kernel-trace --stats) as a
-      markdown table.
+      markdown table; with --last, each library kernel's last N dispatches
+      from the per-dispatch trace.
 """
 import argparse
 import csv
@@ -222,7 +223,30 @@ def short_name(name: str) -> str:
     return base[:70]
 
 
+def cmd_trace_last(args):
+    """per kernel (short name), over its last `last` dispatches in the kernel
+    trace: calls, average, min and max duration"""
+    files = sorted(glob.glob(os.path.join(args.dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {args.dir}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                per.setdefault(short_name(r["Kernel_Name"]), []).append((int(r["Dispatch_Id"]), d))
+    print(f"| kernel | calls (last) | average us | min us | max us |")
+    print("|---|---|---|---|---|")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1][-args.last:])):
+        if not re.search(args.pattern, k):
+            continue
+        v = [d for _, d in sorted(v)][-args.last:]
+        print(f"| `{k}` | {len(v)} | {sum(v) / len(v) / 1000:.1f} | {min(v) / 1000:.1f} | {max(v) / 1000:.1f} |")
+
+
 def cmd_trace(args):
+    if args.last:
+        return cmd_trace_last(args)
     files = sorted(glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no *kernel_stats.csv under {args.dir}")
@@ -264,6 +288,9 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("--dir", required=True)
     t.add_argument("--top", type=int, default=12)
+    t.add_argument("--last", type=int, default=0, help="each kernel's last N dispatches, from the per-dispatch trace")
+    t.add_argument("--pattern", default=r"hq|encode|decode|fused|act_quant|codes_|rotate|nearest",
+                   help="with --last: kernels whose short name matches")
     args = ap.parse_args(argv)
     {"sq": cmd_sq, "traffic": cmd_traffic, "table": cmd_table, "trace": cmd_trace}[args.cmd](args)
 
