@@ -123,6 +123,7 @@ __device__ __forceinline__ void nearest_d4(const float* t, int32_t* d, uint32_t&
 // selects, an fma and a conversion.
 struct E8Choice {
   float f[8];        // rint(t)
+  float dl[8];       // t - rint(t) (exact)
   bool neg[8];       // t - rint(t) < 0
   bool first[8];     // the moved coordinate, if any moves (at most one)
   bool useB;         // half-integer coset
@@ -131,13 +132,13 @@ struct E8Choice {
 };
 
 __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
-  float dl[8], ad[8];
+  float ad[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     c.f[i] = __builtin_rintf(t[i]);
-    dl[i] = t[i] - c.f[i];
-    ad[i] = __builtin_fabsf(dl[i]);
-    c.neg[i] = dl[i] < 0.0f;
+    c.dl[i] = t[i] - c.f[i];
+    ad[i] = __builtin_fabsf(c.dl[i]);
+    c.neg[i] = c.dl[i] < 0.0f;
   }
   const float sf = ((c.f[0] + c.f[1]) + (c.f[2] + c.f[3])) + ((c.f[4] + c.f[5]) + (c.f[6] + c.f[7]));   // exact
   const bool oddA = ((int32_t)sf & 1) != 0;
@@ -209,6 +210,22 @@ __device__ __forceinline__ void nearest_e8_point(const float* t, float* pt) {
   }
 }
 
+// t - (its nearest E8 point), for t a multiple of 2^-23 in [-1, 1) (the
+// dither's box sample): (t - f) - (adj + p/2) with the point never formed.
+// Both ways are exact for such t (every value is a multiple of 2^-23 below 2
+// in magnitude), so this equals t - nearest_e8_point(t).
+__device__ __forceinline__ void e8_box_residual(const float* t, float* u) {
+  E8Choice c;
+  e8_choose(t, c);
+  const float base = c.useB ? 0.5f : 0.0f;
+  const float Kp = ((c.useB & c.negj) ? -0.5f : base) + c.mvh;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float x = (c.useB & c.neg[i]) ? -0.5f : base;
+    u[i] = c.dl[i] - (c.first[i] ? Kp : x);
+  }
+}
+
 // A2 = R u (R + (1/2, sqrt3/2)), R = Z x sqrt3 Z; code (p, m, n') with point
 // (m + p/2, sqrt3 (n' + p/2)).
 __device__ __forceinline__ void nearest_a2(const float* t, int32_t* d, uint32_t& p, A2Consts k) {
@@ -274,22 +291,24 @@ __device__ __forceinline__ void dither_block(uint32_t key_dither, uint32_t g0, f
   float v[D];
 #pragma unroll
   for (int i = 0; i < D; i++) {
+    // (a < 2^24: the product and the difference are exact, so one fused
+    // multiply-add gives the same value as the two operations)
     float a = (float)(pcg_hash(key_dither + g0 + (uint32_t)i) >> 8);
-    if constexpr (LAT == 8 || LAT == 4) v[i] = a * 0x1p-23f - 1.0f;
-    else v[i] = a * 0x1p-24f - 0.5f;
+    if constexpr (LAT == 8 || LAT == 4) v[i] = __builtin_fmaf(a, 0x1p-23f, -1.0f);
+    else v[i] = __builtin_fmaf(a, 0x1p-24f, -0.5f);
   }
   if constexpr (LAT == 2) v[1] = k.sqrt3 * v[1];
-  float pt[D];
   if constexpr (LAT == 8) {
-    nearest_e8_point(v, pt);
+    e8_box_residual(v, u);
   } else {
+    float pt[D];
     int32_t d[D];
     uint32_t p;
     nearest<LAT>(v, d, p, k);
     code_point<LAT>(d, p, pt, k);
-  }
 #pragma unroll
-  for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
+    for (int i = 0; i < D; i++) u[i] = v[i] - pt[i];
+  }
 }
 
 // This wave's LDS writes made visible to its own later LDS reads (for data
