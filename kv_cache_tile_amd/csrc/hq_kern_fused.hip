@@ -22,8 +22,8 @@
 //   1. the unit's bits (8 contiguous runs, one per row) stream into one of
 //      two LDS buffers, the next unit's during this unit's work;
 //   2. each tile's lanes find their first unary code and parse their 32
-//      codes (the decoder's parse_lane, rebuilding 2P), saturated to int8 in
-//      LDS;
+//      codes (the decoder's reader, parse_codes) straight to the integers
+//      2P, saturated to int8 in LDS;
 //   3. one wave per tile column forms the 8 rows x 32 activations of int32
 //      products with v_mfma_i32_32x32x32_i8 (rows 8..31 of the operand are
 //      zero), written to LDS;
@@ -236,7 +236,7 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     ok = ok && carry == (uint32_t)N;
     wave_lds_sync();                                        // (a tile's lanes are in one wave)
 
-    float a[kLaneElems];
+    CodesSink<LAT> csink;
     bool lane_ok;
     {
       uint32_t cbits = 0;
@@ -254,13 +254,12 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
       const uint32_t lim = ok ? end : 0u;
       uint32_t upos = 0;
       bool pok;
-      const A2Consts a2{0.0f, 0.0f};
       switch (k) {
 #define HQ_FPARSE_CASE(KK) \
-        case KK: pok = parse_lane<LAT, false, KK>(stage, rb, u0, lim, cbits, 2.0f, 0u, 0u, a2, a, upos); break;
+        case KK: pok = parse_codes<LAT, KK>(stage, rb, u0, lim, cbits, csink, upos); break;
         HQ_FPARSE_CASE(0) HQ_FPARSE_CASE(1) HQ_FPARSE_CASE(2) HQ_FPARSE_CASE(3)
         HQ_FPARSE_CASE(4) HQ_FPARSE_CASE(5) HQ_FPARSE_CASE(6)
-        default: pok = parse_lane<LAT, false, 7>(stage, rb, u0, lim, cbits, 2.0f, 0u, 0u, a2, a, upos); break;
+        default: pok = parse_codes<LAT, 7>(stage, rb, u0, lim, cbits, csink, upos); break;
 #undef HQ_FPARSE_CASE
       }
       lane_ok = ok && pok;
@@ -277,20 +276,9 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
       const bool real = r0 + (uint64_t)jrow < rows;
       if (real && !lane_ok && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
       uint32_t w[8];
-      bool over = false;
 #pragma unroll
-      for (int v = 0; v < 8; v++) {
-        uint32_t pk = 0;
-#pragma unroll
-        for (int h = 0; h < 4; h++) {
-          int cv = lane_ok ? (int)a[4 * v + h] : 0;
-          over = over | (cv > 127) | (cv < -127);
-          cv = cv > 127 ? 127 : (cv < -127 ? -127 : cv);
-          pk |= ((uint32_t)cv & 0xFFu) << (8 * h);
-        }
-        w[v] = pk;
-      }
-      if (real && over) atomicOr(status, HQ_FLAG_RANGE);
+      for (int v = 0; v < 8; v++) w[v] = lane_ok ? csink.w[v] : 0u;
+      if (real && lane_ok && csink.over()) atomicOr(status, HQ_FLAG_RANGE);
       uint4* dst = reinterpret_cast<uint4*>(codes + jrow * CRS + tcol * (N / 4) + ((q + tcol) % LPT) * 8);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -836,19 +836,17 @@ struct DecodeGeom {
   static constexpr int THREADS = TPW * LPT;
 };
 
-// Rice parse and lattice rebuild of one lane's 32 codes for Rice parameter
-// K: a[e] = (lattice point - dither) * s, every zero +0 (a product with +0
-// added, one fused multiply-add; no nonzero product rounds to zero for the
-// steps the caller passes).  Remainders come from the lane's
-// K-bit fields (static offsets), quotients from the unary window, 8 codes per
-// group; a group whose fast read saw a run of 31+ zeros (or ran out of window)
-// is read again exactly.  Returns false if the codes are not a valid stream
-// (a symbol above 16 bits, or a run past `end`); `upos` is left at the bit
-// after the lane's last code.
-template <int LAT, bool DITHER, int K>
-__device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, uint32_t u0, uint32_t end,
-                                           uint32_t cbits, float s, uint32_t key_dither, uint32_t g_lane,
-                                           A2Consts a2, float (&a)[kLaneElems], uint32_t& upos) {
+// Rice parse of one lane's 32 codes for Rice parameter K, each block's
+// integer code (d, p) handed to sink.block(b, d, p) as it is read, and
+// sink.group_done(g) after the 8 codes of group g.  Remainders come from the
+// lane's K-bit fields (static offsets), quotients from the unary window, 8
+// codes per group; a group whose fast read saw a run of 31+ zeros (or ran out
+// of window) is read again exactly.  Returns false if the codes are not a
+// valid stream (a symbol above 16 bits, or a run past `end`); `upos` is left
+// at the bit after the lane's last code.
+template <int LAT, int K, class Sink>
+__device__ __forceinline__ bool parse_codes(const uint32_t* stage, uint32_t rb, uint32_t u0, uint32_t end,
+                                            uint32_t cbits, Sink& sink, uint32_t& upos) {
   constexpr int D = LatticeTraits<LAT>::dim;
   uint32_t seg[K + 1];
   seg[K] = 0u;
@@ -863,9 +861,6 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
   UnaryWindow uw;
   uw.init(stage, u0);
   bool ok = true;
-  // E8 without dither: (d + p/2) * s as one fma, exact (13 and 8 significant
-  // bits) for normal products
-  const float half_s = 0.5f * s;
 #pragma unroll
   for (int g = 0; g < kLaneElems / 8; g++) {
     uw.refill();
@@ -902,32 +897,93 @@ __device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, u
         }
         d[D - 1] = (int32_t)(((uint32_t)d[D - 1] << 1) | (par & 1u));
       }
-      const uint32_t p = (cbits >> b) & 1u;
-      if constexpr (LAT == 8 && !DITHER) {
-        const float add = p ? half_s : 0.0f;
-#pragma unroll
-        for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf((float)d[i], s, add);
-      } else {
-        float pt[D];
-        code_point<LAT>(d, p, pt, a2);
-        if constexpr (DITHER) {
-          float du[D];
-          dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), du, a2);
-#pragma unroll
-          for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
-        }
-#pragma unroll
-        for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf(pt[i], s, 0.0f);
-      }
+      sink.block(b, d, (cbits >> b) & 1u);
     }
-    // the group's values are final here: keeps the compiler from holding all
-    // 32 quotients and rebuilding every block at the end (register pressure)
-    asm volatile("" : "+v"(a[8 * g + 0]), "+v"(a[8 * g + 1]), "+v"(a[8 * g + 2]), "+v"(a[8 * g + 3]),
-                      "+v"(a[8 * g + 4]), "+v"(a[8 * g + 5]), "+v"(a[8 * g + 6]), "+v"(a[8 * g + 7]));
+    sink.group_done(g);
   }
   upos = uw.pos();
   return ok;
 }
+
+// The decoder's sink: a[e] = (lattice point - dither) * s, every zero +0 (a
+// product with +0 added, one fused multiply-add; no nonzero product rounds
+// to zero for the steps the caller passes).
+template <int LAT, bool DITHER>
+struct RebuildSink {
+  static constexpr int D = LatticeTraits<LAT>::dim;
+  float (&a)[kLaneElems];
+  float s;
+  uint32_t key_dither, g_lane;
+  A2Consts a2;
+  __device__ __forceinline__ void block(int b, const int32_t (&d)[D], uint32_t p) {
+    if constexpr (LAT == 8 && !DITHER) {
+      // E8 without dither: (d + p/2) * s as one fma, exact (13 and 8
+      // significant bits) for normal products
+      const float add = p ? 0.5f * s : 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf((float)d[i], s, add);
+    } else {
+      float pt[D];
+      code_point<LAT>(d, p, pt, a2);
+      if constexpr (DITHER) {
+        float du[D];
+        dither_block<LAT>(key_dither, g_lane + (uint32_t)(b * D), du, a2);
+#pragma unroll
+        for (int i = 0; i < D; i++) pt[i] = pt[i] - du[i];
+      }
+#pragma unroll
+      for (int i = 0; i < D; i++) a[b * D + i] = __builtin_fmaf(pt[i], s, 0.0f);
+    }
+  }
+  // the group's values are final here: keeps the compiler from holding all
+  // 32 quotients and rebuilding every block at the end (register pressure)
+  __device__ __forceinline__ void group_done(int g) {
+    asm volatile("" : "+v"(a[8 * g + 0]), "+v"(a[8 * g + 1]), "+v"(a[8 * g + 2]), "+v"(a[8 * g + 3]),
+                      "+v"(a[8 * g + 4]), "+v"(a[8 * g + 5]), "+v"(a[8 * g + 6]), "+v"(a[8 * g + 7]));
+  }
+};
+
+template <int LAT, bool DITHER, int K>
+__device__ __forceinline__ bool parse_lane(const uint32_t* stage, uint32_t rb, uint32_t u0, uint32_t end,
+                                           uint32_t cbits, float s, uint32_t key_dither, uint32_t g_lane,
+                                           A2Consts a2, float (&a)[kLaneElems], uint32_t& upos) {
+  RebuildSink<LAT, DITHER> sink{a, s, key_dither, g_lane, a2};
+  return parse_codes<LAT, K>(stage, rb, u0, end, cbits, sink, upos);
+}
+
+// The int8 product's sink (Z, D4, E8 without dither): the integer codes 2P
+// = 2 d + p (p the E8 coset bit; 0 for Z and D4), saturated to [-127, 127]
+// and packed four to a word (w[j], byte m = code 4 j + m); lo and hi track
+// the least and greatest code before saturation.
+template <int LAT>
+struct CodesSink {
+  static constexpr int D = LatticeTraits<LAT>::dim;
+  uint32_t w[kLaneElems / 4];
+  int32_t c[8];
+  int32_t lo = 0, hi = 0;
+  __device__ __forceinline__ void block(int b, const int32_t (&d)[D], uint32_t p) {
+    static_assert(LAT != 2, "integer codes: Z, D4 or E8");
+    const int o = (b * D) & 7;
+#pragma unroll
+    for (int i = 0; i < D; i++) c[o + i] = LAT == 8 ? (int32_t)(((uint32_t)d[i] << 1) | p) : (int32_t)((uint32_t)d[i] << 1);
+  }
+  __device__ __forceinline__ void group_done(int g) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      lo = c[i] < lo ? c[i] : lo;
+      hi = c[i] > hi ? c[i] : hi;
+      c[i] = c[i] < -127 ? -127 : (c[i] > 127 ? 127 : c[i]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint32_t x = __builtin_amdgcn_perm((uint32_t)c[4 * h + 1], (uint32_t)c[4 * h], 0x0c0c0400u);
+      const uint32_t y = __builtin_amdgcn_perm((uint32_t)c[4 * h + 3], (uint32_t)c[4 * h + 2], 0x04000c0cu);
+      w[2 * g + h] = x | y;
+    }
+    asm volatile("" : "+v"(w[2 * g]), "+v"(w[2 * g + 1]));
+  }
+  __device__ __forceinline__ bool over() const { return lo < -127 || hi > 127; }
+};
 
 // Occupancy target: 7 waves per SIMD (72 VGPRs) without dither, 5 with it.
 // CODES: write each tile's integer codes 2P (int8, saturated to [-127, 127]
@@ -1171,6 +1227,7 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
     static_assert(!CODES || (!DITHER && LAT != 2), "integer codes: Z, D4 or E8 without dither");
     constexpr bool kFoldScale = kPow2Scale<N> && LAT != 2 && !DITHER && !CODES;
     float a[kLaneElems];
+    CodesSink<LAT == 2 ? 8 : LAT> codes;                    // (CODES only)
     bool lane_ok;
     const bool zero_step = sraw == 0u;
     {
@@ -1198,13 +1255,24 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       const uint32_t g_lane = (uint32_t)(t * N) + (uint32_t)(q * kLaneElems);
       uint32_t upos = 0;
       bool pok;
-      switch (k) {
+      if constexpr (CODES) {
+        switch (k) {
 #define HQ_PARSE_CASE(KK) \
-        case KK: pok = parse_lane<LAT, DITHER, KK>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
-        HQ_PARSE_CASE(0) HQ_PARSE_CASE(1) HQ_PARSE_CASE(2) HQ_PARSE_CASE(3)
-        HQ_PARSE_CASE(4) HQ_PARSE_CASE(5) HQ_PARSE_CASE(6)
-        default: pok = parse_lane<LAT, DITHER, 7>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
+          case KK: pok = parse_codes<LAT, KK>(stage, rb, u0, lim, cbits, codes, upos); break;
+          HQ_PARSE_CASE(0) HQ_PARSE_CASE(1) HQ_PARSE_CASE(2) HQ_PARSE_CASE(3)
+          HQ_PARSE_CASE(4) HQ_PARSE_CASE(5) HQ_PARSE_CASE(6)
+          default: pok = parse_codes<LAT, 7>(stage, rb, u0, lim, cbits, codes, upos); break;
 #undef HQ_PARSE_CASE
+        }
+      } else {
+        switch (k) {
+#define HQ_PARSE_CASE(KK) \
+          case KK: pok = parse_lane<LAT, DITHER, KK>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
+          HQ_PARSE_CASE(0) HQ_PARSE_CASE(1) HQ_PARSE_CASE(2) HQ_PARSE_CASE(3)
+          HQ_PARSE_CASE(4) HQ_PARSE_CASE(5) HQ_PARSE_CASE(6)
+          default: pok = parse_lane<LAT, DITHER, 7>(stage, rb, u0, lim, cbits, s_lane, key_dither, g_lane, a2, a, upos); break;
+#undef HQ_PARSE_CASE
+        }
       }
       lane_ok = ok && pok;
       if (q == LPT - 1 && upos != end) lane_ok = false;      // the last one ends the tile
@@ -1226,20 +1294,9 @@ decode_kernel(const uint32_t* __restrict__ payload, uint64_t payload_words,
       if (active) {
         if (!lane_ok && q == 0) atomicOr(status, HQ_FLAG_CORRUPT);
         uint32_t w[8];
-        bool over = false;
 #pragma unroll
-        for (int v = 0; v < 8; v++) {
-          uint32_t pk = 0;
-#pragma unroll
-          for (int h = 0; h < 4; h++) {
-            int c = lane_ok ? (int)a[4 * v + h] : 0;
-            over = over | (c > 127) | (c < -127);
-            c = c > 127 ? 127 : (c < -127 ? -127 : c);
-            pk |= ((uint32_t)c & 0xFFu) << (8 * h);
-          }
-          w[v] = pk;
-        }
-        if (over) atomicOr(status, HQ_FLAG_RANGE);
+        for (int v = 0; v < 8; v++) w[v] = lane_ok ? codes.w[v] : 0u;
+        if (lane_ok && codes.over()) atomicOr(status, HQ_FLAG_RANGE);
         uint4* p = reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(out) + t * N + (uint64_t)q * kLaneElems);
         p[0] = make_uint4(w[0], w[1], w[2], w[3]);
         p[1] = make_uint4(w[4], w[5], w[6], w[7]);
