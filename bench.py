@@ -309,14 +309,16 @@ def all_configs(args):
     xa = torch.from_numpy(workloads.gaussian(32, 16384, key=77)).to(dev)
     codes = hq.decode_codes(h)
     q, sc = hq.act_quant(xa, 256, seed)
+    qb, scb = hq.act_quant(xa, 256, seed, blocked=True)
     yv = hq.codes_matmul(codes, h.step, 256, q, sc)
     fst = torch.zeros(1, dtype=torch.int32, device=dev)
-    yf = hq.codes_matmul_fused(h, q, sc, fst)
+    yf = hq.codes_matmul_fused(h, qb, scb, fst)
     d_med, _ = timed(lambda: hq.decode_codes(h, out=codes), False)
     a_med, _ = timed(lambda: hq.act_quant(xa, 256, seed, out=(q, sc)), False)
     wk = torch.empty(32 * 4096 * 64, dtype=torch.int32, device=dev)
     m_med, _ = timed(lambda: hq.codes_matmul(codes, h.step, 256, q, sc, out=yv, work=wk), False)
-    f_med, _ = timed(lambda: hq.codes_matmul_fused(h, q, sc, fst, out=yf), False)
+    ab_med, _ = timed(lambda: hq.act_quant(xa, 256, seed, out=(qb, scb), blocked=True), False)
+    f_med, _ = timed(lambda: hq.codes_matmul_fused(h, qb, scb, fst, out=yf), False)
     # context: the uncompressed product, bf16 weights (right operand made
     # contiguous), the same shape
     wt = w.t().contiguous()
@@ -328,14 +330,15 @@ def all_configs(args):
            "bps_target": 4.0, "tile": 256, "decode_codes_us": round(1000 * d_med, 2),
            "act_quant_us": round(1000 * a_med, 2), "codes_matmul_us": round(1000 * m_med, 2),
            "two_pass_total_us": round(1000 * (d_med + a_med + m_med), 2),
-           "fused_product_us": round(1000 * f_med, 2), "fused_total_us": round(1000 * (a_med + f_med), 2),
+           "act_quant_blocked_us": round(1000 * ab_med, 2),
+           "fused_product_us": round(1000 * f_med, 2), "fused_total_us": round(1000 * (ab_med + f_med), 2),
            "bf16_torch_matmul_us": round(1000 * bf_med, 2),
            "matmul_TOPs": round(2.0 * 4096 * 16384 * 32 / (m_med / 1000) / 1e12, 2),
            "fused_equals_two_pass": bool(torch.equal(yf, yv)),
            "rel_err_vs_decoded_fp64": float(((yv.double() - ref).norm() / ref.norm()).item()),
            "status_flags": h.flags() | int(fst.item())}
     print(json.dumps(rec), flush=True)
-    del w, h, xa, codes, q, sc, yv, yf, ref, wk, wt, xb
+    del w, h, xa, codes, q, sc, qb, scb, yv, yf, ref, wk, wt, xb
 
     cache.clear()
     src = torch.ones(1 << 28, dtype=torch.int32, device=dev)             # 1 GiB

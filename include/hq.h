@@ -288,6 +288,19 @@ int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, ui
                     int32_t *work, uint64_t work_bytes, void *stream);
 
 /*
+ * hq_act_quant_blocked — hq_act_quant (the same codes and scales) with q in
+ * the matrix cores' operand order, for hq_codes_matmul_fused: with T = cols /
+ * n tiles a row, the code of activation b, column t n + 32 k + j (j < 32) is
+ * q[(((b / 32) T + t) (n / 32) + k) 1024 + (b % 32) 32 + j], so that q holds
+ * ceil(batch / 32) * 32 * cols bytes (the entries of activations at or past
+ * batch are neither written nor read).  scale fp32 [batch][cols / n] as for
+ * hq_act_quant.  Asynchronous on `stream`; HQ_EINVAL before any device work
+ * as for hq_act_quant.
+ */
+int hq_act_quant_blocked(const void *x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile,
+                         uint64_t seed, int8_t *q, float *scale, void *stream);
+
+/*
  * hq_codes_matmul_fused — hq_decode_codes followed by hq_codes_matmul in one
  * launch, straight from the compressed stream (gist.science explainer of
  * HyperQuant, "Significance and Claims": decoding fused with the matrix
@@ -299,8 +312,8 @@ int hq_codes_matmul(const int8_t *codes, const uint16_t *step, uint64_t rows, ui
  *              for hq_decode_codes (Z, D4 or E8 without dither); every row
  *              must be a whole number of 64-tile chunks: cols % (64 tile) == 0;
  *              payload 16-byte aligned (it is read in 16-byte vectors)
- *   q, scale   hq_act_quant's output for [batch][cols] activations (q 16-byte
- *              aligned)
+ *   q, scale   hq_act_quant_blocked's output for [batch][cols] activations
+ *              (q in its blocked order, 16-byte aligned)
  *   y          fp32 [batch][rows]
  *   status     device word: HQ_FLAG_CORRUPT (a tile's codes taken as 0) and
  *              HQ_FLAG_RANGE (a code saturated) are OR-ed in, as by

@@ -510,6 +510,13 @@ __device__ __forceinline__ void lds_load_u16(const uint16_t* base, uint32_t voff
                : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
+// The same for one 32-bit word a lane (lane i's at lds + 4 i).
+__device__ __forceinline__ void lds_load4(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
 // The same for one 32-bit word a lane (lane i's at lds + 4 i), read coherently
 // at device scope (sc1: not from a stale line of this XCD's L2), for words
 // that workgroups on other XCDs update with atomics.

@@ -26,7 +26,8 @@
 //      2P, saturated to int8 in LDS;
 //   3. one wave per tile column forms the 8 rows x 32 activations of int32
 //      products with v_mfma_i32_32x32x32_i8 (rows 8..31 of the operand are
-//      zero), written to LDS;
+//      zero; the activation operand read from hq_act_quant_blocked's layout,
+//      1 KB of contiguous memory a load), written to LDS;
 //   4. each (activation b, row j) takes the unit's chain steps in order, in
 //      registers of one thread.
 #include "hq_kernels.h"
@@ -39,6 +40,12 @@ typedef int fz_i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kFusedRows = 8;      // weight rows per workgroup
 constexpr int kFusedCols = 8;      // tile columns per unit
 constexpr int kFusedBatch = 32;    // activations per launch row of workgroups
+
+// Tile products live in the codes rows of their column once the column's
+// products are formed (n >= 128: a column's rows hold 2n >= 256 words);
+// at n = 64 they have a buffer of their own.
+template <int N>
+constexpr bool kProductsInCodes = N >= 128;
 
 template <int LAT, int N>
 __global__ void __launch_bounds__(kFusedRows * kFusedCols * (N / kLaneElems))
@@ -70,10 +77,22 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
   uint32_t* tok = tms + ROWS * MS;                          // [ROWS][MS] tile valid
   uint32_t* cinfo = tok + ROWS * MS;                        // [ROWS][4] chunk's first word (lo, hi), valid
   uint32_t* adj = cinfo + 4 * ROWS;                         // [2][ROWS] stage bit of a chunk's bit 0
-  float* sscale = reinterpret_cast<float*>(adj + 2 * ROWS);  // [64][32] activation scales of the column
-  uint32_t* ustart = reinterpret_cast<uint32_t*>(sscale + kFusedBatch * kChunkTiles);   // [THREADS]
+  float* sscale = reinterpret_cast<float*>(adj + 2 * ROWS);  // [TC][32] activation scales of the unit
+  uint32_t* ustart = reinterpret_cast<uint32_t*>(sscale + kFusedBatch * TC);   // [THREADS]
   uint32_t* codes = ustart + THREADS;                       // [ROWS][CRS] int8 codes 2P
-  int32_t* ibuf = reinterpret_cast<int32_t*>(codes + ROWS * CRS);   // [TC][32][ROWS] tile products
+  int32_t* ibuf = reinterpret_cast<int32_t*>(codes + ROWS * CRS);   // [TC][32][ROWS] tile products (n = 64)
+  // word of the product (activation b, row j) of column c: in the column's
+  // codes rows, row segment b % 8 at (b / 8) 8 + j, the row halves swapped
+  // for b / 8 odd (n >= 128); else in ibuf, (c 32 + b) 8 + j, halves swapped
+  // the same way.  Either way a 16-byte store of a row half by 16 lanes, and
+  // a word read by 64 lanes, find distinct banks.
+  auto prod_word = [&](int c, int b, int j) -> int32_t* {
+    const int js = (((j >> 2) ^ ((b >> 3) & 1)) << 2) | (j & 3);
+    if constexpr (kProductsInCodes<N>)
+      return reinterpret_cast<int32_t*>(codes) + (b & 7) * CRS + c * (N / 4) + (b >> 3) * 8 + js;
+    else
+      return ibuf + (c * kFusedBatch + b) * ROWS + js;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -161,10 +180,6 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
           cinfo[4 * wr + 2] = chunk_ok ? 1u : 0u;
         }
       }
-      for (int i = tid; i < kFusedBatch * kChunkTiles; i += THREADS) {
-        const uint64_t bb = b0 + (uint64_t)(i % kFusedBatch);
-        sscale[i] = bb < batch ? scale[bb * tpr + t0 + (uint32_t)(i / kFusedBatch)] : 0.0f;
-      }
       __syncthreads();
       stage_in(t0, cur);                                    // (the first unit of the column: not ahead)
     }
@@ -173,18 +188,14 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     // streaming into the other buffer during this unit's parse
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // the first half of this wave's first column's activation operands, in
-    // flight during the parse (the rest is loaded after it)
-    constexpr int KS = N / 32, KE = KS / 2;
-    const fz_i32x4 zero4 = {0, 0, 0, 0};
-    const int half = (lane >> 5) * 16;
-    const uint64_t bbl = b0 + (uint64_t)(lane & 31);
-    fz_i32x4 bv0[KE];
-    {
-      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)(t0 + (uint32_t)(wave * CPW)) * N;
-#pragma unroll
-      for (int ks = 0; ks < KE; ks++)
-        bv0[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
+    // the unit's activation scales stream into LDS (sscale[c 32 + b]; an
+    // activation past the batch reads activation 0's, and its chain is never
+    // stored), read by the chain after the unit's products
+    for (int i0 = wave * 64; i0 < TC * kFusedBatch; i0 += WAVES * 64) {
+      const uint32_t i = (uint32_t)(i0 + lane);
+      const uint64_t bb = b0 + (uint64_t)(i % kFusedBatch);
+      const uint64_t src = (bb < batch ? bb : 0) * tpr + t0 + i / kFusedBatch;
+      lds_load4(scale, (uint32_t)(4 * src), smem_lds + 4u * (uint32_t)((sscale - reinterpret_cast<float*>(smem)) + i0));
     }
     if (t0 + TC < tpr && (t0 + TC) % kChunkTiles != 0) stage_in(t0 + TC, cur ^ 1);
     const uint32_t* stage = stage0;
@@ -290,17 +301,20 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
     // 16-byte half l / 32 of every 32-code step; output register i of lane l
     // holds row (i / 4) 8 + (l / 32) 4 + i % 4, activation l % 32. ----
     wave_lds_sync();                                        // (this wave's columns' codes are in LDS)
+    constexpr int KS = N / 32;
+    const fz_i32x4 zero4 = {0, 0, 0, 0};
+    const int half = (lane >> 5) * 16;
+    const uint64_t bbl = b0 + (uint64_t)(lane & 31);
     for (int cc = 0; cc < CPW; cc++) {
       const int c = wave * CPW + cc;
       const uint32_t t = t0 + (uint32_t)c;
       const int arow = lane & 31;
-      const int8_t* brow = qa + bbl * (uint64_t)tpr * N + (uint64_t)t * N;
+      // the activations' 32-code steps of tile t, 1 KB each (the blocked layout)
+      const int8_t* bstep = qa + ((uint64_t)blockIdx.y * tpr + t) * (uint64_t)(KS * 1024) + (lane & 31) * 32 + half;
       fz_i32x4 bv[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        if (ks < KE && cc == 0) bv[ks] = bv0[ks];
-        else bv[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(brow + 32 * ks + half) : zero4;
-      }
+      for (int ks = 0; ks < KS; ks++)
+        bv[ks] = bbl < batch ? *reinterpret_cast<const fz_i32x4*>(bstep + 1024 * ks) : zero4;
       fz_i32x16 I = {};
 #pragma unroll
       for (int ks = 0; ks < N / 32; ks++) {
@@ -309,11 +323,11 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
             : zero4;
         I = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv[ks], I, 0, 0, 0);
       }
-      // rows 4h .. 4h + 3 of activation b as one 16-byte store, the halves
-      // swapped for b = 8..15 and 24..31 (16 lanes, 16 distinct bank groups)
-      const int b = lane & 31, hs = (lane >> 5) ^ ((b >> 3) & 1);
-      *reinterpret_cast<fz_i32x4*>(ibuf + (c * kFusedBatch + b) * ROWS + hs * 4) = fz_i32x4{I[0], I[1], I[2], I[3]};
+      // rows 4h .. 4h + 3 of activation b as one 16-byte store (the column's
+      // codes are read: each MFMA above waited for its operands)
+      *reinterpret_cast<fz_i32x4*>(prod_word(c, lane & 31, (lane >> 5) * 4)) = fz_i32x4{I[0], I[1], I[2], I[3]};
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");        // (this wave's scale loads)
     __syncthreads();
 
     // ---- 4. the chain steps of the unit, in column order ----
@@ -325,9 +339,8 @@ fused_product_kernel(const uint32_t* __restrict__ payload, uint64_t payload_word
 #pragma unroll
         for (int c = 0; c < TC; c++) {
           const float s = as_f((tms[cj * MS + p0 + c] >> 16) << 16);
-          const float av = sscale[(p0 + c) * kFusedBatch + cb];
-          const int js = (((cj >> 2) ^ ((cb >> 3) & 1)) << 2) | (cj & 3);   // (the halves' swap)
-          acc[i] = __builtin_fmaf((float)ibuf[(c * kFusedBatch + cb) * ROWS + js], s * av, acc[i]);
+          const float av = sscale[c * kFusedBatch + cb];
+          acc[i] = __builtin_fmaf((float)*prod_word(c, cb, cj), s * av, acc[i]);
         }
       }
     }
@@ -360,8 +373,8 @@ const void* fused_fn(uint32_t lattice, uint32_t n, uint32_t seg_words, uint32_t*
   const uint32_t th = (uint32_t)(kFusedRows * kFusedCols) * (n / kLaneElems);
   *threads = th;
   *lds = 4 * (2 * (size_t)kFusedRows * seg_words + 3 * kFusedRows * (kChunkTiles + 1) + 4 * kFusedRows +
-              2 * kFusedRows + kFusedBatch * kChunkTiles + th + (size_t)kFusedRows * (kFusedCols * n / 4 + 8) +
-              (size_t)kFusedCols * kFusedBatch * kFusedRows);
+              2 * kFusedRows + kFusedBatch * kFusedCols + th + (size_t)kFusedRows * (kFusedCols * n / 4 + 8) +
+              (n >= 128 ? 0 : (size_t)kFusedCols * kFusedBatch * kFusedRows));
   return (const void*)f;
 }
 

@@ -22,7 +22,11 @@ namespace hq {
 // One workgroup of N / 2 threads per activation tile: sign diagonal (the
 // codec's sign bits of positions 0 .. n-1), the butterfly with strides 1, 2,
 // ..., n/2 in LDS, the scale fl(1/sqrt(n)), then max |y| and the int8 codes.
-template <int N>
+// BLOCKED: the codes in the matrix cores' operand order, so that one 16-byte
+// load a lane brings a whole 32-code step of 32 activations from 1 KB of
+// contiguous memory: code (b, column t n + 32 k + j) at
+// (((b / 32) T + t) (n / 32) + k) 1024 + (b % 32) 32 + j, T = tiles a row.
+template <int N, bool BLOCKED>
 __global__ void __launch_bounds__(N / 2)
 act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_row, uint32_t key_sign,
                  float inv_sqrtn, int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -67,10 +71,16 @@ act_quant_kernel(const void* __restrict__ x, uint32_t xbf16, uint64_t tiles_per_
     r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
     return (int8_t)(int)r;
   };
-  q[base + k] = code(v0);
-  q[base + k + N / 2] = code(v1);
+  if constexpr (BLOCKED) {
+    const uint64_t b = tile / tiles_per_row, t = tile % tiles_per_row;
+    int8_t* qt = q + (((b >> 5) * tiles_per_row + t) * (N / 32)) * 1024 + (b & 31) * 32;
+    qt[(k >> 5) * 1024 + (k & 31)] = code(v0);
+    qt[((k + N / 2) >> 5) * 1024 + (k & 31)] = code(v1);
+  } else {
+    q[base + k] = code(v0);
+    q[base + k + N / 2] = code(v1);
+  }
   if (k == 0) scale[tile] = a;
-  (void)tiles_per_row;
 }
 
 // The product in two passes, so that the tiles' exact int32 products run in
@@ -152,10 +162,10 @@ codes_chain_kernel(const int32_t* __restrict__ work, const uint16_t* __restrict_
   y[b * rows + r] = 0.5f * acc;
 }
 
-const void* act_quant_fn(uint32_t n) {
-  if (n == 64) return (const void*)act_quant_kernel<64>;
-  if (n == 128) return (const void*)act_quant_kernel<128>;
-  if (n == 256) return (const void*)act_quant_kernel<256>;
+const void* act_quant_fn(uint32_t n, bool blocked) {
+  if (n == 64) return blocked ? (const void*)act_quant_kernel<64, true> : (const void*)act_quant_kernel<64, false>;
+  if (n == 128) return blocked ? (const void*)act_quant_kernel<128, true> : (const void*)act_quant_kernel<128, false>;
+  if (n == 256) return blocked ? (const void*)act_quant_kernel<256, true> : (const void*)act_quant_kernel<256, false>;
   return nullptr;
 }
 // both passes on `stream` (shapes checked by the caller); false on a launch error

@@ -24,7 +24,7 @@ namespace hq {
 const void* rot_mfma_fn(uint32_t d, bool xbf16, bool ybf16, size_t* lds, uint32_t* threads,
                         uint32_t* rows_per_block);
 // hq_kern_i8.hip: the int8 product path's kernels for tile size n (null otherwise)
-const void* act_quant_fn(uint32_t n);
+const void* act_quant_fn(uint32_t n, bool blocked);
 bool launch_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t n,
                          const int8_t* q, const float* scale, uint64_t batch, float* y, int32_t* work,
                          hipStream_t stream);
@@ -535,11 +535,11 @@ int hq_decode_codes(const uint32_t* payload, uint64_t payload_words, const uint1
                    stream, fn);
 }
 
-int hq_act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile, uint64_t seed,
-                 int8_t* q, float* scale, void* stream) {
-  const void* fn = act_quant_fn(tile);
+static int act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile,
+                     uint64_t seed, int8_t* q, float* scale, void* stream, bool blocked) {
+  const void* fn = act_quant_fn(tile, blocked);
   if (!fn || (x_dtype != HQ_F32 && x_dtype != HQ_BF16) || !x || !q || !scale || cols % tile ||
-      batch * cols >= (1ull << 32))
+      (blocked ? (batch + 31) & ~31ull : batch) * cols >= (1ull << 32))
     return HQ_EINVAL;
   const uint64_t tiles = batch * (cols / tile);
   if (tiles == 0) return HQ_OK;
@@ -547,6 +547,16 @@ int hq_act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols,
                      dim3((uint32_t)tiles), dim3(tile / 2), 0, (hipStream_t)stream, x, (uint32_t)(x_dtype == HQ_BF16),
                      cols / tile, derive_key(seed, 0x5349474Eu), (float)(1.0 / sqrt((double)tile)), q, scale);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+int hq_act_quant(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile, uint64_t seed,
+                 int8_t* q, float* scale, void* stream) {
+  return act_quant(x, x_dtype, batch, cols, tile, seed, q, scale, stream, false);
+}
+
+int hq_act_quant_blocked(const void* x, uint32_t x_dtype, uint64_t batch, uint64_t cols, uint32_t tile,
+                         uint64_t seed, int8_t* q, float* scale, void* stream) {
+  return act_quant(x, x_dtype, batch, cols, tile, seed, q, scale, stream, true);
 }
 
 int hq_codes_matmul(const int8_t* codes, const uint16_t* step, uint64_t rows, uint64_t cols, uint32_t tile,
@@ -587,7 +597,8 @@ int hq_codes_matmul_fused(const uint32_t* payload, uint64_t payload_words, const
   if (rc) return rc;
   if (lattice == HQ_A2 || cols % ((uint64_t)kChunkTiles * tile) != 0) return HQ_EINVAL;
   if (!payload || !step || !meta || !chunk_off || !q || !scale || !y || !status) return HQ_EINVAL;
-  if (((uintptr_t)payload & 15) || ((uintptr_t)q & 15) || batch * cols >= (1ull << 32)) return HQ_EINVAL;
+  if (((uintptr_t)payload & 15) || ((uintptr_t)q & 15) || ((batch + 31) & ~31ull) * cols >= (1ull << 32))
+    return HQ_EINVAL;
   if (batch == 0) return HQ_OK;
   // a row's run of a unit: its words, 3 before and 3 after for the 16-byte
   // vectors it is streamed in, and 8 zero guard words

@@ -24,7 +24,7 @@ CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
            "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
-           "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc", "hq_codes_matmul_fused")
+           "hq_act_quant_blocked", "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc", "hq_codes_matmul_fused")
 
 
 class HQError(RuntimeError):
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.hq_decode_codes.restype = ctypes.c_int
         L.hq_act_quant.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
         L.hq_act_quant.restype = ctypes.c_int
+        L.hq_act_quant_blocked.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
+        L.hq_act_quant_blocked.restype = ctypes.c_int
         L.hq_codes_matmul.argtypes = [vp, vp, u64, u64, u32, vp, vp, u64, vp, vp, u64, vp]
         L.hq_codes_matmul.restype = ctypes.c_int
         L.hq_codes_matmul_fused.argtypes = [vp, u64, vp, vp, vp, u64, u64, u32, u32, f32, vp, vp, u64, vp, vp, vp]
@@ -409,10 +411,13 @@ def fused_supported(h: HQTensor) -> bool:
 
 def codes_matmul_fused(h: HQTensor, q: torch.Tensor, scale: torch.Tensor, status: torch.Tensor,
                        out: torch.Tensor | None = None) -> torch.Tensor:
-    """y [batch][rows] = the int8 product straight from the stream (one launch);
-    CORRUPT / RANGE flags go to `status`."""
+    """y [batch][rows] = the int8 product straight from the stream (one launch),
+    with q, scale = act_quant(x, ..., blocked=True); CORRUPT / RANGE flags go
+    to `status`."""
     rows, cols, c = _rows_cols_c(h)
-    B = q.shape[0]
+    B = scale.shape[0]
+    if q.dim() != 1 or q.numel() != blocked_size(B, cols) or scale.shape != (B, cols // h.tile):
+        raise HQError("codes_matmul_fused takes act_quant(x, tile, seed, blocked=True)'s output")
     if out is None:
         out = torch.empty((B, rows), dtype=torch.float32, device=q.device)
     _check(lib().hq_codes_matmul_fused(h.payload.data_ptr(), h.payload.numel(), h.step.data_ptr(),
@@ -422,21 +427,30 @@ def codes_matmul_fused(h: HQTensor, q: torch.Tensor, scale: torch.Tensor, status
     return out
 
 
-def act_quant(x: torch.Tensor, tile: int, seed: int, out: tuple | None = None) -> tuple:
+def blocked_size(batch: int, cols: int) -> int:
+    """Bytes of act_quant(..., blocked=True)'s codes: batch rounded up to 32, times cols."""
+    return (batch + 31) // 32 * 32 * cols
+
+
+def act_quant(x: torch.Tensor, tile: int, seed: int, out: tuple | None = None, blocked: bool = False) -> tuple:
     """Per-tile RHT of activations x [batch][cols] in int8, with fp32 scales
-    (into out = (q, scale) when given)."""
+    (into out = (q, scale) when given).  q is int8 [batch][cols], or with
+    blocked=True the flat matrix-core order that codes_matmul_fused reads
+    (hq_act_quant_blocked)."""
     x2 = x.reshape(-1, x.shape[-1]).contiguous()
     B, cols = x2.shape
+    qshape = (blocked_size(B, cols),) if blocked else (B, cols)
     if out is not None:
         q, sc = out
-        if q.shape != (B, cols) or q.dtype != torch.int8 or sc.shape != (B, cols // tile) or \
+        if q.shape != qshape or q.dtype != torch.int8 or sc.shape != (B, cols // tile) or \
                 sc.dtype != torch.float32 or not (q.is_contiguous() and sc.is_contiguous()):
-            raise ValueError("act_quant: out must be int8 [batch][cols] and fp32 [batch][cols / tile], contiguous")
+            raise ValueError(f"act_quant: out must be int8 {list(qshape)} and fp32 [batch][cols / tile], contiguous")
     else:
-        q = torch.empty((B, cols), dtype=torch.int8, device=x.device)
+        q = torch.empty(qshape, dtype=torch.int8, device=x.device)
         sc = torch.empty((B, cols // tile), dtype=torch.float32, device=x.device)
-    _check(lib().hq_act_quant(x2.data_ptr(), _dtype_code(x2.dtype), B, cols, tile, seed, q.data_ptr(),
-                              sc.data_ptr(), _stream(x.device)))
+    fn = lib().hq_act_quant_blocked if blocked else lib().hq_act_quant
+    _check(fn(x2.data_ptr(), _dtype_code(x2.dtype), B, cols, tile, seed, q.data_ptr(), sc.data_ptr(),
+              _stream(x.device)))
     return q, sc
 
 
@@ -460,9 +474,10 @@ def matmul_compressed(h: HQTensor, x: torch.Tensor) -> torch.Tensor:
     (fused with the decode where the shape allows).  Synchronises to read its
     own status word, and raises if a tile's codes were saturated (the result
     would not be x W_hat^T) or the stream is corrupt."""
-    q, sc = act_quant(x, h.tile, h.seed)
+    fused = fused_supported(h)
+    q, sc = act_quant(x, h.tile, h.seed, blocked=fused)
     status = torch.zeros(1, dtype=torch.int32, device=q.device)
-    if fused_supported(h):
+    if fused:
         y = codes_matmul_fused(h, q, sc, status)
     else:
         y = codes_matmul(decode_codes(h, status=status), h.step, h.tile, q, sc)

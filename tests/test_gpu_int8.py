@@ -137,14 +137,39 @@ def test_fused_product(lat, tile, bps):
     h, e = _weights(lat, tile, rows, cols, bps, key=tile)
     x = workloads.gaussian(batch, cols, key=rows + tile)
     q, sc = hq.act_quant(torch.from_numpy(x).to(_dev()), tile, 7)
+    qb, scb = hq.act_quant(torch.from_numpy(x).to(_dev()), tile, 7, blocked=True)
     status = torch.zeros(1, dtype=torch.int32, device=_dev())
-    y = hq.codes_matmul_fused(h, q, sc, status)
+    y = hq.codes_matmul_fused(h, qb, scb, status)
     torch.cuda.synchronize()
     c = rate_c(lat, tile, bps)
     codes, st, flag = oracle.decode_codes(e, rows, cols, tile, lat, c, 7)
     ref = oracle.codes_matmul(codes, e.step, tile, q.cpu().numpy(), sc.cpu().numpy())
     np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     assert int(status.item()) == (hq.FLAG_RANGE if flag else 0)
+
+
+def _unblock(qb, batch, cols, tile):
+    # the blocked order [batch / 32][tile t][32-code step k][activation % 32][32]
+    # back to [batch][cols]
+    nb = (batch + 31) // 32
+    a = qb.reshape(nb, cols // tile, tile // 32, 32, 32).permute(0, 3, 1, 2, 4).reshape(nb * 32, cols)
+    return a[:batch]
+
+
+@pytest.mark.parametrize("tile,batch", [(64, 37), (128, 64), (256, 5), (256, 33)])
+def test_act_quant_blocked(tile, batch):
+    # the same codes and scales as hq_act_quant, in the matrix-core order
+    cols = 3 * tile
+    x = torch.from_numpy(workloads.gaussian(batch, cols, key=tile + batch)).to(_dev())
+    q, sc = hq.act_quant(x, tile, 5)
+    qb, scb = hq.act_quant(x, tile, 5, blocked=True)
+    torch.cuda.synchronize()
+    assert qb.numel() == (batch + 31) // 32 * 32 * cols
+    assert torch.equal(_unblock(qb.cpu(), batch, cols, tile), q.cpu())
+    assert torch.equal(scb.cpu(), sc.cpu())
+    with pytest.raises(hq.HQError, match="blocked=True"):
+        hq.codes_matmul_fused(hq.encode(torch.zeros(8, 64 * tile, device=_dev()), tile, "E8", 4.0, 1),
+                              q, sc, torch.zeros(1, dtype=torch.int32, device=_dev()))
 
 
 def test_fused_product_corrupt_streams():
@@ -155,6 +180,7 @@ def test_fused_product_corrupt_streams():
     h, e = _weights(lat, tile, rows, cols, 4.0, key=11)
     x = workloads.gaussian(batch, cols, key=12)
     q, sc = hq.act_quant(torch.from_numpy(x).to(dev), tile, 7)
+    qb, scb = hq.act_quant(torch.from_numpy(x).to(dev), tile, 7, blocked=True)
     c = rate_c(lat, tile, 4.0)
     rng = np.random.default_rng(3)
     for trial in range(6):
@@ -171,7 +197,7 @@ def test_fused_product_corrupt_streams():
                          torch.from_numpy(meta.view(np.int16)).to(dev), torch.from_numpy(off.view(np.int32)).to(dev),
                          torch.zeros(1, dtype=torch.int32, device=dev), (rows, cols), torch.bfloat16, tile, lat, 4.0, 7)
         status = torch.zeros(1, dtype=torch.int32, device=dev)
-        y = hq.codes_matmul_fused(hh, q, sc, status)
+        y = hq.codes_matmul_fused(hh, qb, scb, status)
         torch.cuda.synchronize()
         ee = oracle.Encoded(step, meta, off, pay, 0)
         codes, st, flag = oracle.decode_codes(ee, rows, cols, tile, lat, c, 7)
