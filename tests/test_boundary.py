@@ -37,6 +37,9 @@ def lib():
     L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
                                  P(f32), P(ctypes.c_double), P(u32), vp]
     L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
+    L.hq_act_quant.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
+    L.hq_act_quant_blocked.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
+    L.hq_codes_matmul_fused.argtypes = [vp, u64, vp, vp, vp, u64, u64, u32, u32, f32, vp, vp, u64, vp, vp, vp]
     L.hq_strerror.argtypes = [ctypes.c_int]
     L.hq_strerror.restype = ctypes.c_char_p
     L.hq_version.restype = u32
@@ -189,6 +192,33 @@ def test_rotate_rejects_before_device_work(lib):
     assert lib.hq_rotate(A, 128, 0, A, BF16, 10, A + 4, F32, None) == EINVAL
     assert lib.hq_rotate(A, 128, 0, A, BF16, 1 << 32, A, F32, None) == EINVAL
     assert lib.hq_rotate(A, 128, 0, A, BF16, 0, A, F32, None) == OK               # nothing to do
+
+
+def test_int8_calls_reject_before_device_work(lib):
+    A = 1 << 40
+    for fn in (lib.hq_act_quant, lib.hq_act_quant_blocked):
+        assert fn(None, BF16, 4, 1024, 256, 1, A, A, None) == EINVAL
+        assert fn(A, BF16, 4, 1000, 256, 1, A, A, None) == EINVAL             # cols not a multiple of n
+        assert fn(A, BF16, 4, 1024, 96, 1, A, A, None) == EINVAL              # n is 64, 128 or 256
+        assert fn(A, 7, 4, 1024, 256, 1, A, A, None) == EINVAL
+        assert fn(A, BF16, 0, 1024, 256, 1, A, A, None) == OK                 # nothing to do
+    # at most 2^32 - 1 codes: row-major, 33 activations of 2^27 columns pass
+    # it; blocked, 17 activations already do (rounded up to 32)
+    assert lib.hq_act_quant(A, BF16, 33, 1 << 27, 256, 1, A, A, None) == EINVAL
+    assert lib.hq_act_quant_blocked(A, BF16, 17, 1 << 27, 256, 1, A, A, None) == EINVAL
+    c = ctypes.c_float(0.3)
+
+    def fused(**kw):
+        a = dict(pay=A, rows=16, cols=64 * 256, tile=256, lat=E8, q=A, batch=8)
+        a.update(kw)
+        return lib.hq_codes_matmul_fused(a["pay"], 100, A, A, A, a["rows"], a["cols"], a["tile"], a["lat"], c,
+                                         a["q"], A, a["batch"], A, A, None)
+    assert fused(lat=A2) == EINVAL                                                # integer codes only
+    assert fused(cols=32 * 256) == EINVAL                                         # rows of whole chunks
+    assert fused(pay=A + 4) == EINVAL and fused(q=A + 8) == EINVAL               # 16-byte alignment
+    assert fused(pay=None) == EINVAL
+    assert fused(batch=(1 << 32) // (64 * 256)) == EINVAL                         # blocked codes past 2^32
+    assert fused(batch=0) == OK
 
 
 def test_library_has_no_undefined_internal_symbols():
