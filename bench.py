@@ -134,6 +134,63 @@ def cpu_baseline(layers_host, rows, cols, tile, seed_of, c_of):
                       f"decode {gb / t_dec:.4f} GB/s, {t_enc + t_dec:.1f} s on one pinned core"}
 
 
+# normalized second moments G (Conway & Sloane) and covolumes V, for the
+# high-rate distortion prediction 2 pi e G 2^-2R of an entropy-coded lattice
+# quantizer at R bits a scalar
+LATTICE_G = {"Z": 1.0 / 12.0, "A2": 5.0 / (36.0 * 3.0 ** 0.5), "D4": 0.0766032, "E8": 929.0 / 12960.0}
+
+
+def nmse_high_rate(lattice: str, bps: float) -> float:
+    return 2.0 * 3.141592653589793 * 2.718281828459045 * LATTICE_G[lattice] * 2.0 ** (-2.0 * bps)
+
+
+def cpu_baseline_config(x_host, rows, cols, tile, lat, c, seed, dither, h, out, max_scalars=1 << 22):
+    """The oracle on a bounded sample of one configuration's tensor, single-
+    threaded on one pinned host core: encode and decode of its first whole
+    chunks (at most max_scalars), timed, and compared with the GPU's stream
+    and reconstruction of the same tiles (step, meta, chunk offsets, payload
+    words, decoded values, bit for bit)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle
+    oracle.build(force=False)
+    tpr = cols // tile
+    unit = 64 // tpr if tpr < 64 else 1                     # rows per whole chunk (tiles a row divide 64)
+    rs = min(rows, max(unit, max_scalars // cols // unit * unit))
+    T = rs * tpr
+    C = (T + 63) // 64
+    xs = np.ascontiguousarray(x_host[:rs])
+    allowed = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {allowed[0]})
+    try:
+        t0 = time.perf_counter()
+        e = oracle.encode(xs, tile, lat, c, seed, dither=dither)
+        t1 = time.perf_counter()
+        xo, st = oracle.decode(e, rs, cols, tile, lat, c, seed, oracle.F32 if xs.dtype == np.float32 else oracle.BF16,
+                               dither=dither)
+        t2 = time.perf_counter()
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    off = h.chunk_off[: C + 1].cpu().numpy().view(np.uint32).astype(np.int64)
+    words = int(off[-1])
+    same = (np.array_equal(h.step[:T].cpu().numpy().view(np.uint16), e.step) and
+            np.array_equal(h.meta[:T].cpu().numpy().view(np.uint16), e.meta) and
+            np.array_equal(off, e.chunk_off.astype(np.int64)) and
+            np.array_equal(h.payload[:words].cpu().numpy().view(np.uint32), e.payload) and
+            np.array_equal(out[:rs].contiguous().cpu().view(torch_int_of(out)).numpy(),
+                           xo.view(np.int32 if xs.dtype == np.float32 else np.int16)))
+    mb = xs.nbytes / 1e6
+    return {"kind": "oracle", "sample": f"first {rs} of {rows} rows ({T} tiles, {C} chunks, {rs * cols} scalars)",
+            "encode_MBps": round(mb / (t1 - t0), 2), "decode_MBps": round(mb / (t2 - t1), 2),
+            "seconds": round(t2 - t0, 3), "cores": 1, "pinned_core": allowed[0], "cores_available": len(allowed),
+            "parity_sample": "bit-exact" if same and st == oracle.OK else f"MISMATCH (oracle status {st})"}
+
+
+def torch_int_of(t):
+    import torch
+    return torch.int32 if t.element_size() == 4 else torch.int16
+
+
 def config_runs():
     """The corroborating configurations (the DiT stack is the default bench):
     (config, tensor name, lattice, bps, tile, kv).  The MLP weight runs every
@@ -226,7 +283,14 @@ def all_configs(args):
         rec["bps_total"] = round(h.bits_total() / numel, 4)
         rec["compression_vs_input"] = round(8.0 * esz * numel / h.bits_total(), 3)
         rec["nmse"] = float(((out.double() - xf) ** 2).sum() / (xf ** 2).sum())
+        rec["nmse_high_rate"] = nmse_high_rate(lat, bps)
+        rec["nmse_vs_high_rate"] = round(rec["nmse"] / rec["nmse_high_rate"], 3)
         rec["status_flags"] = h.flags()
+        if only is None and not args.no_oracle:
+            xh = x2.cpu()
+            xh = xh.numpy() if xh.dtype == torch.float32 else xh.view(torch.int16).numpy().view("uint16")
+            rec["oracle"] = cpu_baseline_config(xh, x2.shape[0], x2.shape[1], tile, lat, p.rate_constant, seed,
+                                                int(kv), h, out)
         print(json.dumps(rec), flush=True)
         del xf, out, h
 
@@ -361,6 +425,8 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the DiT stack: one JSON line per run of the other configurations "
                          "(weights 1024x1024 fp32, 4096x4096, 11008x4096 over all lattices, the KV cache)")
+    ap.add_argument("--no-oracle", action="store_true",
+                    help="with --configs: skip the oracle leg (a timed, parity-checked sample of each run)")
     ap.add_argument("--only", default=None,
                     help="with --configs: only these runs (comma-separated indices of the per-configuration "
                          "runs, in the order the lines print), e.g. for one counter collection per run")

@@ -155,9 +155,11 @@ __device__ __forceinline__ void e8_choose(const float* t, E8Choice& c) {
       __builtin_fminf(__builtin_fminf(ad[0], __builtin_fminf(ad[1], ad[2])), __builtin_fminf(ad[3], __builtin_fminf(ad[4], ad[5]))),
       __builtin_fminf(ad[6], ad[7]));
   const float sabs = ((ad[0] + ad[1]) + (ad[2] + ad[3])) + ((ad[4] + ad[5]) + (ad[6] + ad[7]));
+  // (2 mx and 2 mn are exact, so each fused multiply-add below rounds once,
+  // as the two-operation forms 1 - 2 mx and diff - 2 mn do)
   float diff = sabs - 2.0f;
-  if (oddA) diff = diff + (1.0f - 2.0f * mx);
-  if (oddB) diff = diff - 2.0f * mn;
+  if (oddA) diff = diff + __builtin_fmaf(-2.0f, mx, 1.0f);
+  if (oddB) diff = __builtin_fmaf(-2.0f, mn, diff);
   c.useB = diff > 0.0f;
   const float target = c.useB ? mn : mx;
   // (bitwise operators on the conditions: they stay lane masks)
