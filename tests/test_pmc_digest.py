@@ -87,3 +87,4 @@ def test_bench_reads_counters_only_for_current_sources(tmp_path, monkeypatch):
     p.write_text(json.dumps(rec))
     assert bench.measured_valu("encode_kernel") is None
     assert bench.roofline("encode_kernel", 10.0, 1.0e6, 1 << 20)["bound_source"] == "no current VALU counters"
+
