@@ -172,6 +172,32 @@ def test_act_quant_blocked(tile, batch):
                               q, sc, torch.zeros(1, dtype=torch.int32, device=_dev()))
 
 
+def test_fused_product_non_finite_activations():
+    # a NaN or an infinity in an activation tile makes that tile's scale
+    # non-finite: its products are NaN in the fused chain as in the oracle's,
+    # and the other activations' outputs are untouched; 70 activations (three
+    # blocks of 32, the last partial)
+    dev = _dev()
+    lat, tile, rows, batch = "E8", 128, 24, 70
+    cols = 64 * tile
+    h, e = _weights(lat, tile, rows, cols, 4.0, key=21)
+    x = workloads.gaussian(batch, cols, key=22)
+    x[3, 17] = np.nan
+    x[40, 5000] = np.inf
+    x[69, 1] = -np.inf
+    xt = torch.from_numpy(x).to(dev)
+    q, sc = hq.act_quant(xt, tile, 7)
+    qb, scb = hq.act_quant(xt, tile, 7, blocked=True)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = hq.codes_matmul_fused(h, qb, scb, status)
+    torch.cuda.synchronize()
+    c = rate_c(lat, tile, 4.0)
+    codes, st, flag = oracle.decode_codes(e, rows, cols, tile, lat, c, 7)
+    ref = oracle.codes_matmul(codes, e.step, tile, q.cpu().numpy(), sc.cpu().numpy())
+    _nan_equal(y.cpu().numpy(), ref)
+    assert np.isnan(ref[3]).all() and np.isfinite(ref[4]).all()
+
+
 def test_fused_product_corrupt_streams():
     # corrupt tiles and chunks give zero codes (and the flag) on both sides;
     # a non-finite step makes that tile's products NaN on both sides
