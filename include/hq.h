@@ -175,18 +175,27 @@ int hq_kv_decode(const uint32_t *payload, uint64_t payload_words, const uint16_t
  *   K = fl32(sqrt(2 pi e) V^(-1/d)) is the high-rate step constant of an
  *   entropy-coded lattice quantiser (V the covolume: Z 1, A2 sqrt3/2, D4 2,
  *   E8 1).
+ * hq_encode_length_c — the length pass: adds to *words (a device uint64,
+ *   8-byte aligned; the caller zeroes it first) the payload size in words,
+ *   chunk_off[C], that hq_encode_c with the same arguments would produce,
+ *   without writing a stream: the same per-tile steps, lattice points,
+ *   symbols and Rice parameters, each chunk's tile lengths summed and
+ *   rounded up to a word.  Asynchronous on `stream`; needs no workspace;
+ *   sets no status flags (a non-finite tile counts as the zero tile the
+ *   encoder writes).  Arguments and errors as hq_encode_c.
  * hq_encode_rate — synchronous: bisection on c over that bracket, at the
- *   geometric midpoint fl32(sqrt(lo * hi)); each trial is one hq_encode_c
- *   on `stream` followed by a 4-byte read of chunk_off[C] and a stream
- *   synchronisation.  A trial with more bits than the target raises lo,
- *   one with fewer lowers hi.  It stops when the rate is within 0.01 of the
- *   target, when the midpoint equals an end of the interval (fp32
- *   resolution), or after 30 trials; the buffers then hold the last trial's
- *   stream, encoded with *c_out (pass it to hq_decode_c), at *bps_out bits
- *   per scalar after *encodes_out encodes (the outputs may be NULL).
- *   Buffers are sized by hq_plan_c at the bracket's low end (its tiles are
- *   the longest); smaller capacities give HQ_ENOSPC before any device work.
- *   Other arguments and errors as hq_encode_c.
+ *   geometric midpoint fl32(sqrt(lo * hi)); each trial is one length pass
+ *   on `stream`, counting into workspace bytes 16..23, followed by an
+ *   8-byte read and a stream synchronisation.  A trial with more bits than
+ *   the target raises lo, one with fewer lowers hi.  It stops when the rate
+ *   is within 0.01 of the target, when the midpoint equals an end of the
+ *   interval (fp32 resolution), or after 30 trials, and then encodes the
+ *   stream once, with hq_encode_c at *c_out (pass it to hq_decode_c): its
+ *   rate is *bps_out bits per scalar, found after *encodes_out trials (the
+ *   outputs may be NULL).  Buffers are sized by hq_plan_c at the bracket's
+ *   low end (its tiles are the longest); smaller capacities and null or
+ *   misaligned buffers give their errors before any device work.  Other
+ *   arguments and errors as hq_encode_c.
  */
 int hq_plan_c(uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
               float c, uint32_t kv,
@@ -202,6 +211,9 @@ int hq_decode_c(const uint32_t *payload, uint64_t payload_words, const uint16_t 
                 uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile, uint32_t lattice,
                 float c, uint64_t seed, uint32_t kv, void *x_out, uint32_t *status, void *stream);
 int hq_rate_bracket(uint32_t lattice, float target_bps, float *c_lo, float *c_hi);
+int hq_encode_length_c(const void *x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                       uint32_t lattice, float c, uint64_t seed, uint32_t kv, unsigned long long *words,
+                       void *stream);
 
 /*
  * hq_encode_c_noalloc — hq_encode_c without the workspace argument, for

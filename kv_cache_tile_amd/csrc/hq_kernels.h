@@ -196,6 +196,7 @@ __device__ __forceinline__ void pack_lane_pairs(uint32_t* stage, uint32_t t0, in
 // workgroup is done.
 constexpr uint32_t kStartedWords = 64;                      // bits for up to 2048 workgroups
 constexpr uint32_t kStartedBase = 64, kLookBase = 192;      // word offsets in the workspace
+constexpr uint32_t kLengthWord = 4;                          // (words 4, 5) the rate search's length count
 __device__ __forceinline__ uint32_t take_ticket(uint32_t* ws, uint64_t CG, uint32_t epoch, bool all_started) {
   const uint32_t grid = gridDim.x;
   const uint64_t dyn = CG - grid;                            // groups handed out by draws
@@ -225,6 +226,279 @@ __device__ __forceinline__ uint32_t sign_mask(uint32_t* smask, uint32_t key_sign
   }
   __syncthreads();
   return smask[q];
+}
+
+// The encoder's work on one tile up to its length, shared by the encoder and
+// the length pass: load and sign diagonal, butterfly, step, nearest lattice
+// points, symbols and the Rice parameter.  The lane's symbols come back in R
+// (bytes, four a register, when `bytes`; else 16-bit pairs), its blocks'
+// coset bits in cb, the tile's bf16 step bits in sbits (nonfinite: a
+// non-finite tile, coded as zero), the Rice parameter in k, the tile's
+// Rice-coded length without its coset bits in best_c, and this lane's sum of
+// quotients in lane_sum.  k_prev carries the lane's previous Rice parameter.
+template <int LAT, int N, bool DITHER, bool BF16>
+__device__ __forceinline__ void encode_tile(const void* __restrict__ x, const uint4 (&pre)[4], const uint32_t* emask,
+                                            uint32_t sgn, uint64_t T, uint64_t t, bool active, int q, float c,
+                                            float inv_sqrtn, float inv_n, uint32_t key_dither, A2Consts a2,
+                                            uint32_t& k_prev, uint32_t (&R)[kLaneElems / 2], uint32_t& cb,
+                                            uint32_t& sbits, bool& nonfinite, bool& bytes, uint32_t& k,
+                                            uint32_t& best_c, uint32_t& lane_sum) {
+  constexpr int LPT = N / kLaneElems;
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr int BPL = kLaneElems / D;
+  constexpr bool bf16 = BF16;
+  // ---- load + sign diagonal (bf16 -> fp32 is exact; the sign bits are
+  // flipped on the packed pairs) ----
+  float a[kLaneElems];
+  uint32_t sg = sgn;
+  opaque(sg);
+  // (an inactive tile works on the last tile's data and stores nothing)
+  if (bf16) {
+    const uint4* em = reinterpret_cast<const uint4*>(emask + 16 * q);
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const uint4 w = pre[v], m = em[v];
+      uint32_t ww[4] = {w.x, w.y, w.z, w.w}, mm[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        uint32_t pw = ww[h] ^ mm[h];
+        opaque(pw);                                       // one xor per pair, then the two halves
+        a[v * 8 + 2 * h] = as_f(pw << 16);
+        a[v * 8 + 2 * h + 1] = as_f(pw & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const uint64_t base = (active ? t : T - 1) * N + (uint64_t)q * kLaneElems;
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
+#pragma unroll
+    for (int v = 0; v < 8; v++) {
+      float4 w = p[v];
+      a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
+    }
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ ((sg << (31 - i)) & 0x80000000u));
+  }
+
+  // ---- RHT: the butterfly (exact values in every lane), then y = z fl(1/sqrt(n)).
+  // When 1/sqrt(n) is a power of two and the input is bf16 the scale is
+  // exact: every butterfly value z is a multiple of 2^-133 (the finest bf16
+  // unit; sums round to coarser multiples), so z / sqrt(n) is representable
+  // even below the normal range.  Then the lane keeps z and the scale is
+  // folded into the quantiser's factor (ydom false). ----
+  fwht_tile_signed<LPT>(a, q);
+  constexpr bool ydom = !kPow2Scale<N> || !bf16;
+  if (ydom) {
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
+  }
+
+  // ---- tile energy and step = bf16(sqrt(ss / n) * c), ss the pinned
+  // pairwise sum of y^2.  An estimate from fused multiply-add chains decides
+  // the step unless it lies within 64 units in the last place of a bf16
+  // rounding tie: the pinned sum and the estimate are each within 9 and 13
+  // roundings of the exact sum of squares, so their two values of
+  // sqrt(ss / n) * c (the estimate's square root by the hardware
+  // instruction, within 1 ulp) differ by less than 16 units in the last
+  // place.  A wave
+  // with such a tile, or with an estimate outside [2^-90, 2^100] (where
+  // subnormal terms, overflow, a flushed or an infinite step could enter),
+  // computes the pinned sum (steps below 2^-124 are stored as 0). ----
+  float e4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) e4[i & 3] = __builtin_fmaf(a[i], a[i], e4[i & 3]);
+  float est = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+#pragma unroll
+  for (int m = 1; m < LPT; m <<= 1) est = est + lane_xor(est, partner_xor<LPT>(m));
+  if (!ydom) est = est * inv_n;                            // sum of z^2 / n (exact power-of-two scale)
+  const float r_est = __builtin_amdgcn_sqrtf(est * inv_n) * c;   // v_sqrt_f32: within 1 ulp
+  const bool near_tie = ((as_u(r_est) & 0xFFFFu) - 0x7FC0u) <= 0x80u;
+  const bool in_range = est >= 0x1p-90f && est <= 0x1p100f && r_est >= 0x1p-100f && r_est <= 0x1p100f;
+  nonfinite = false;
+  if (wave_any(near_tie || !in_range)) {
+    asm volatile("");                                     // (rare: stays a branch)
+    // the pinned tree as a running stack of partial sums: part[l] holds
+    // the sum of the last complete block of 2^l squares
+    float part[6];
+#pragma unroll
+    for (int i = 0; i < kLaneElems; i++) {
+      const float y = ydom ? a[i] : a[i] * inv_sqrtn;
+      float v = y * y;
+      int l = 0;
+#pragma unroll
+      for (; (i >> l) & 1; l++) v = part[l] + v;
+      part[l] = v;
+    }
+    float ss = part[5];
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) ss = ss + lane_xor(ss, partner_xor<LPT>(m));
+    nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
+    sbits = 0;
+    if (!nonfinite) {
+      const float rms = sqrtf(ss * inv_n);
+      const float r = rms * c;
+      sbits = bf16_rne_bits(r);
+      if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
+      else if ((sbits & 0x7F80u) < 0x0180u) sbits = 0;    // below 2^-124: stored as 0
+    }
+  } else {
+    sbits = bf16_rne_bits(r_est);
+  }
+  // fl(1 / s) from the hardware reciprocal r0 (within 1 ulp) and one
+  // correction: e = 1 - s r0 is exact (s has 8 significant bits), r0 + r0 e
+  // differs from 1 / s by e^2 / s (below 2^-22 ulp), and 1 / s = 2^-j / M
+  // (s = M 2^j, M < 256 an integer) lies at least 2^-9 ulp from every
+  // rounding midpoint, so the fused multiply-add rounds to fl(1 / s).  s is
+  // in [2^-124, 2^61 c]: r0 and 1 / s are normal.
+  const float s = as_f(sbits << 16);
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  const float inv = sbits == 0u ? 0.0f : __builtin_fmaf(e, r0, r0);
+  // t = y / s; with z kept, z * (inv / sqrt(n)) is the same product: both
+  // scalings are exact (a finite tile energy bounds the step by
+  // sqrt(FLT_MAX / n) * c < 2^61 c, far below 2^122 for the table's rate
+  // constants, so inv / sqrt(n) is a normal number)
+  const float qf = ydom ? inv : inv * inv_sqrtn;
+#pragma unroll
+  for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * qf;
+  if (wave_any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
+    asm volatile("");                                     // (stays a branch, not 32 selects)
+    if (nonfinite) {
+#pragma unroll
+      for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
+    }
+  }
+
+
+  // ---- nearest lattice point, strip, zigzag: symbols as 16-bit pairs
+  // (every symbol is below 2^12: |t| <= sqrt(n) / c' for the table's c) ----
+  uint32_t S2[kLaneElems / 2];
+  cb = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems / 2; i++) S2[i] = 0u;
+#pragma unroll
+  for (int b = 0; b < BPL; b++) {
+    uint32_t p;
+    uint32_t u[D];
+    if constexpr (DITHER) {
+      // KV: add the dither (Methodology 4), block by block
+      float du[D];
+      dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
+#pragma unroll
+      for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + du[i];
+    }
+    if constexpr (LAT == 8) {
+      if (b > 0) {
+        // one 8-block at a time: its inputs are released together with the
+        // previous block's symbols (keeps four blocks' temporaries from
+        // being live at once)
+        asm volatile("" : "+v"(S2[4 * b - 4]), "+v"(S2[4 * b - 3]), "+v"(S2[4 * b - 2]), "+v"(S2[4 * b - 1]),
+                          "+v"(a[8 * b + 0]), "+v"(a[8 * b + 1]), "+v"(a[8 * b + 2]), "+v"(a[8 * b + 3]),
+                          "+v"(a[8 * b + 4]), "+v"(a[8 * b + 5]), "+v"(a[8 * b + 6]), "+v"(a[8 * b + 7]));
+      }
+      nearest_e8_symbols(&a[b * D], u, p);
+    } else {
+      int32_t d[D];
+      nearest<LAT>(&a[b * D], d, p, a2);
+      block_symbols<LAT>(d, u);
+    }
+#pragma unroll
+    for (int i = 0; i < D; i++) {
+      const int e = b * D + i;
+      S2[e >> 1] |= u[i] << (16 * (e & 1));
+    }
+    cb |= p << b;
+  }
+
+  // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
+  // cost(k) = S(k) + n (1 + k) with S(k) = sum of sym >> k is convex in k
+  // (S(k) - S(k+1) = sum ceil((sym >> k) / 2) does not grow with k), so the
+  // smallest minimiser is the first k with S(k) - S(k+1) <= n (7 if none).
+  // Three sums around the tile's previous k settle it when k has not moved;
+  // otherwise the wave computes all eight.  When every symbol of the wave
+  // fits a byte, four symbols share a register and one shift, one mask and
+  // one byte-sum (v_sad_u8) add four terms.
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < kLaneElems / 2; i++) mx |= S2[i];
+  bytes = wave_all((mx & 0xFF00FF00u) == 0u);
+  // R: the byte-packed symbols (R[j], byte m = symbol 4j + m) when every
+  // symbol of the wave fits a byte, else the 16-bit pairs
+  if (bytes) {
+#pragma unroll
+    for (int j = 0; j < kLaneElems / 4; j++) R[j] = __builtin_amdgcn_perm(S2[2 * j + 1], S2[2 * j], 0x06040200u);
+#pragma unroll
+    for (int j = kLaneElems / 4; j < kLaneElems / 2; j++) R[j] = S2[j];   // (unread: no copies)
+  } else {
+#pragma unroll
+    for (int j = 0; j < kLaneElems / 2; j++) R[j] = S2[j];
+  }
+  k = 0;
+  best_c = 0;
+  lane_sum = 0;
+  bool settled = false;
+  if (bytes && k_prev < 8u) {
+    const uint32_t kb = k_prev == 0u ? 0u : (k_prev >= 6u ? 5u : k_prev - 1u);
+    uint32_t L[3], Tt[3];
+#pragma unroll
+    for (int jj = 0; jj < 3; jj++) {
+      // sum of (sym >> k) = (sum of sym with its low k bits cleared) >> k
+      const uint32_t kk = kb + (uint32_t)jj;
+      const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
+      uint32_t acc = 0;
+#pragma unroll
+      for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
+      acc >>= kk;
+      L[jj] = acc;
+      uint32_t tot = acc;
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
+      Tt[jj] = tot;
+    }
+    const bool drop0 = Tt[0] - Tt[1] > (uint32_t)N, drop1 = Tt[1] - Tt[2] > (uint32_t)N;
+    int pick = -1;
+    if (kb == 0u && !drop0) pick = 0;
+    else if (drop0 && !drop1) pick = 1;
+    else if (kb == 5u && drop0 && drop1) pick = 2;
+    if (pick >= 0) {
+      settled = true;
+      k = kb + (uint32_t)pick;
+      const uint32_t tot = pick == 0 ? Tt[0] : (pick == 1 ? Tt[1] : Tt[2]);
+      lane_sum = pick == 0 ? L[0] : (pick == 1 ? L[1] : L[2]);
+      best_c = tot + (uint32_t)N * (1u + k);
+    }
+  }
+  if (wave_any(!settled)) {
+    // rare: all eight sums, one k per (rolled) iteration, running minimum
+    uint32_t bk = 0, bc = 0xFFFFFFFFu, bsum = 0;
+#pragma unroll 1
+    for (uint32_t kk = 0; kk < 8u; kk++) {
+      uint32_t acc = 0;
+      if (bytes) {
+        const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
+#pragma unroll
+        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
+        acc >>= kk;
+      } else {
+        // 16-bit halves: each half's sum stays below 2^16 (16 symbols < 2^12)
+        const uint32_t hmask = 0x00010001u * (0xFFFFu >> kk);
+        uint32_t a2acc = 0;
+#pragma unroll
+        for (int j = 0; j < kLaneElems / 2; j++) a2acc += (R[j] >> kk) & hmask;
+        acc = (a2acc & 0xFFFFu) + (a2acc >> 16);
+      }
+      uint32_t tot = acc;
+#pragma unroll
+      for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
+      const uint32_t cost = tot + (uint32_t)N * (1u + kk);
+      if (cost < bc) { bc = cost; bk = kk; bsum = acc; }
+    }
+    if (!settled) {
+      k = bk;
+      best_c = bc;
+      lane_sum = bsum;
+    }
+  }
+  k_prev = k;
 }
 
 // --------------------------------------------------------------------------
@@ -449,258 +723,11 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
 
-    // ---- load + sign diagonal (bf16 -> fp32 is exact; the sign bits are
-    // flipped on the packed pairs) ----
-    float a[kLaneElems];
-    uint32_t sg = sgn;
-    opaque(sg);
-    // (an inactive tile works on the last tile's data and stores nothing)
-    if (bf16) {
-      const uint4* em = reinterpret_cast<const uint4*>(emask + 16 * q);
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const uint4 w = pre[v], m = em[v];
-        uint32_t ww[4] = {w.x, w.y, w.z, w.w}, mm[4] = {m.x, m.y, m.z, m.w};
-#pragma unroll
-        for (int h = 0; h < 4; h++) {
-          uint32_t pw = ww[h] ^ mm[h];
-          opaque(pw);                                       // one xor per pair, then the two halves
-          a[v * 8 + 2 * h] = as_f(pw << 16);
-          a[v * 8 + 2 * h + 1] = as_f(pw & 0xFFFF0000u);
-        }
-      }
-    } else {
-      const uint64_t base = (active ? t : T - 1) * N + (uint64_t)q * kLaneElems;
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + base);
-#pragma unroll
-      for (int v = 0; v < 8; v++) {
-        float4 w = p[v];
-        a[v * 4] = w.x; a[v * 4 + 1] = w.y; a[v * 4 + 2] = w.z; a[v * 4 + 3] = w.w;
-      }
-#pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = as_f(as_u(a[i]) ^ ((sg << (31 - i)) & 0x80000000u));
-    }
-
-    // ---- RHT: the butterfly (exact values in every lane), then y = z fl(1/sqrt(n)).
-    // When 1/sqrt(n) is a power of two and the input is bf16 the scale is
-    // exact: every butterfly value z is a multiple of 2^-133 (the finest bf16
-    // unit; sums round to coarser multiples), so z / sqrt(n) is representable
-    // even below the normal range.  Then the lane keeps z and the scale is
-    // folded into the quantiser's factor (ydom false). ----
-    fwht_tile_signed<LPT>(a, q);
-    constexpr bool ydom = !kPow2Scale<N> || !bf16;
-    if (ydom) {
-#pragma unroll
-      for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * inv_sqrtn;
-    }
-
-    // ---- tile energy and step = bf16(sqrt(ss / n) * c), ss the pinned
-    // pairwise sum of y^2.  An estimate from fused multiply-add chains decides
-    // the step unless it lies within 64 units in the last place of a bf16
-    // rounding tie: the pinned sum and the estimate are each within 9 and 13
-    // roundings of the exact sum of squares, so their two values of
-    // sqrt(ss / n) * c (the estimate's square root by the hardware
-    // instruction, within 1 ulp) differ by less than 16 units in the last
-    // place.  A wave
-    // with such a tile, or with an estimate outside [2^-90, 2^100] (where
-    // subnormal terms, overflow, a flushed or an infinite step could enter),
-    // computes the pinned sum (steps below 2^-124 are stored as 0). ----
-    float e4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < kLaneElems; i++) e4[i & 3] = __builtin_fmaf(a[i], a[i], e4[i & 3]);
-    float est = (e4[0] + e4[1]) + (e4[2] + e4[3]);
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) est = est + lane_xor(est, partner_xor<LPT>(m));
-    if (!ydom) est = est * inv_n;                            // sum of z^2 / n (exact power-of-two scale)
-    const float r_est = __builtin_amdgcn_sqrtf(est * inv_n) * c;   // v_sqrt_f32: within 1 ulp
-    const bool near_tie = ((as_u(r_est) & 0xFFFFu) - 0x7FC0u) <= 0x80u;
-    const bool in_range = est >= 0x1p-90f && est <= 0x1p100f && r_est >= 0x1p-100f && r_est <= 0x1p100f;
-    bool nonfinite = false;
-    uint32_t sbits;
-    if (wave_any(near_tie || !in_range)) {
-      asm volatile("");                                     // (rare: stays a branch)
-      // the pinned tree as a running stack of partial sums: part[l] holds
-      // the sum of the last complete block of 2^l squares
-      float part[6];
-#pragma unroll
-      for (int i = 0; i < kLaneElems; i++) {
-        const float y = ydom ? a[i] : a[i] * inv_sqrtn;
-        float v = y * y;
-        int l = 0;
-#pragma unroll
-        for (; (i >> l) & 1; l++) v = part[l] + v;
-        part[l] = v;
-      }
-      float ss = part[5];
-#pragma unroll
-      for (int m = 1; m < LPT; m <<= 1) ss = ss + lane_xor(ss, partner_xor<LPT>(m));
-      nonfinite = (as_u(ss) & 0x7F800000u) == 0x7F800000u;
-      sbits = 0;
-      if (!nonfinite) {
-        const float rms = sqrtf(ss * inv_n);
-        const float r = rms * c;
-        sbits = bf16_rne_bits(r);
-        if ((sbits & 0x7F80u) == 0x7F80u) { nonfinite = true; sbits = 0; }
-        else if ((sbits & 0x7F80u) < 0x0180u) sbits = 0;    // below 2^-124: stored as 0
-      }
-    } else {
-      sbits = bf16_rne_bits(r_est);
-    }
-    // fl(1 / s) from the hardware reciprocal r0 (within 1 ulp) and one
-    // correction: e = 1 - s r0 is exact (s has 8 significant bits), r0 + r0 e
-    // differs from 1 / s by e^2 / s (below 2^-22 ulp), and 1 / s = 2^-j / M
-    // (s = M 2^j, M < 256 an integer) lies at least 2^-9 ulp from every
-    // rounding midpoint, so the fused multiply-add rounds to fl(1 / s).  s is
-    // in [2^-124, 2^61 c]: r0 and 1 / s are normal.
-    const float s = as_f(sbits << 16);
-    const float r0 = __builtin_amdgcn_rcpf(s);
-    const float e = __builtin_fmaf(-s, r0, 1.0f);
-    const float inv = sbits == 0u ? 0.0f : __builtin_fmaf(e, r0, r0);
-    // t = y / s; with z kept, z * (inv / sqrt(n)) is the same product: both
-    // scalings are exact (a finite tile energy bounds the step by
-    // sqrt(FLT_MAX / n) * c < 2^61 c, far below 2^122 for the table's rate
-    // constants, so inv / sqrt(n) is a normal number)
-    const float qf = ydom ? inv : inv * inv_sqrtn;
-#pragma unroll
-    for (int i = 0; i < kLaneElems; i++) a[i] = a[i] * qf;
-    if (wave_any(nonfinite)) {                                 // rare: a non-finite tile is coded as zero
-      asm volatile("");                                     // (stays a branch, not 32 selects)
-      if (nonfinite) {
-#pragma unroll
-        for (int i = 0; i < kLaneElems; i++) a[i] = 0.0f;
-      }
-    }
-
-
-    // ---- nearest lattice point, strip, zigzag: symbols as 16-bit pairs
-    // (every symbol is below 2^12: |t| <= sqrt(n) / c' for the table's c) ----
-    uint32_t S2[kLaneElems / 2];
-    uint32_t cb = 0;
-#pragma unroll
-    for (int i = 0; i < kLaneElems / 2; i++) S2[i] = 0u;
-#pragma unroll
-    for (int b = 0; b < BPL; b++) {
-      uint32_t p;
-      uint32_t u[D];
-      if constexpr (DITHER) {
-        // KV: add the dither (Methodology 4), block by block
-        float du[D];
-        dither_block<LAT>(key_dither, (uint32_t)(t * N) + (uint32_t)(q * kLaneElems + b * D), du, a2);
-#pragma unroll
-        for (int i = 0; i < D; i++) a[b * D + i] = a[b * D + i] + du[i];
-      }
-      if constexpr (LAT == 8) {
-        if (b > 0) {
-          // one 8-block at a time: its inputs are released together with the
-          // previous block's symbols (keeps four blocks' temporaries from
-          // being live at once)
-          asm volatile("" : "+v"(S2[4 * b - 4]), "+v"(S2[4 * b - 3]), "+v"(S2[4 * b - 2]), "+v"(S2[4 * b - 1]),
-                            "+v"(a[8 * b + 0]), "+v"(a[8 * b + 1]), "+v"(a[8 * b + 2]), "+v"(a[8 * b + 3]),
-                            "+v"(a[8 * b + 4]), "+v"(a[8 * b + 5]), "+v"(a[8 * b + 6]), "+v"(a[8 * b + 7]));
-        }
-        nearest_e8_symbols(&a[b * D], u, p);
-      } else {
-        int32_t d[D];
-        nearest<LAT>(&a[b * D], d, p, a2);
-        block_symbols<LAT>(d, u);
-      }
-#pragma unroll
-      for (int i = 0; i < D; i++) {
-        const int e = b * D + i;
-        S2[e >> 1] |= u[i] << (16 * (e & 1));
-      }
-      cb |= p << b;
-    }
-
-    // ---- Rice parameter: smallest k in 0..7 minimising the tile's length ----
-    // cost(k) = S(k) + n (1 + k) with S(k) = sum of sym >> k is convex in k
-    // (S(k) - S(k+1) = sum ceil((sym >> k) / 2) does not grow with k), so the
-    // smallest minimiser is the first k with S(k) - S(k+1) <= n (7 if none).
-    // Three sums around the tile's previous k settle it when k has not moved;
-    // otherwise the wave computes all eight.  When every symbol of the wave
-    // fits a byte, four symbols share a register and one shift, one mask and
-    // one byte-sum (v_sad_u8) add four terms.
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < kLaneElems / 2; i++) mx |= S2[i];
-    const bool bytes = wave_all((mx & 0xFF00FF00u) == 0u);
-    // R: the byte-packed symbols (R[j], byte m = symbol 4j + m) when every
-    // symbol of the wave fits a byte, else the 16-bit pairs
     uint32_t R[kLaneElems / 2];
-    if (bytes) {
-#pragma unroll
-      for (int j = 0; j < kLaneElems / 4; j++) R[j] = __builtin_amdgcn_perm(S2[2 * j + 1], S2[2 * j], 0x06040200u);
-#pragma unroll
-      for (int j = kLaneElems / 4; j < kLaneElems / 2; j++) R[j] = S2[j];   // (unread: no copies)
-    } else {
-#pragma unroll
-      for (int j = 0; j < kLaneElems / 2; j++) R[j] = S2[j];
-    }
-    uint32_t k = 0, best_c = 0, lane_sum = 0;
-    bool settled = false;
-    if (bytes && k_prev < 8u) {
-      const uint32_t kb = k_prev == 0u ? 0u : (k_prev >= 6u ? 5u : k_prev - 1u);
-      uint32_t L[3], Tt[3];
-#pragma unroll
-      for (int jj = 0; jj < 3; jj++) {
-        // sum of (sym >> k) = (sum of sym with its low k bits cleared) >> k
-        const uint32_t kk = kb + (uint32_t)jj;
-        const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
-        uint32_t acc = 0;
-#pragma unroll
-        for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
-        acc >>= kk;
-        L[jj] = acc;
-        uint32_t tot = acc;
-#pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
-        Tt[jj] = tot;
-      }
-      const bool drop0 = Tt[0] - Tt[1] > (uint32_t)N, drop1 = Tt[1] - Tt[2] > (uint32_t)N;
-      int pick = -1;
-      if (kb == 0u && !drop0) pick = 0;
-      else if (drop0 && !drop1) pick = 1;
-      else if (kb == 5u && drop0 && drop1) pick = 2;
-      if (pick >= 0) {
-        settled = true;
-        k = kb + (uint32_t)pick;
-        const uint32_t tot = pick == 0 ? Tt[0] : (pick == 1 ? Tt[1] : Tt[2]);
-        lane_sum = pick == 0 ? L[0] : (pick == 1 ? L[1] : L[2]);
-        best_c = tot + (uint32_t)N * (1u + k);
-      }
-    }
-    if (wave_any(!settled)) {
-      // rare: all eight sums, one k per (rolled) iteration, running minimum
-      uint32_t bk = 0, bc = 0xFFFFFFFFu, bsum = 0;
-#pragma unroll 1
-      for (uint32_t kk = 0; kk < 8u; kk++) {
-        uint32_t acc = 0;
-        if (bytes) {
-          const uint32_t bmask = 0x01010100u - (0x01010101u << kk);   // bytes 256 - 2^kk
-#pragma unroll
-          for (int j = 0; j < kLaneElems / 4; j++) acc = __builtin_amdgcn_sad_u8(R[j] & bmask, 0u, acc);
-          acc >>= kk;
-        } else {
-          // 16-bit halves: each half's sum stays below 2^16 (16 symbols < 2^12)
-          const uint32_t hmask = 0x00010001u * (0xFFFFu >> kk);
-          uint32_t a2acc = 0;
-#pragma unroll
-          for (int j = 0; j < kLaneElems / 2; j++) a2acc += (R[j] >> kk) & hmask;
-          acc = (a2acc & 0xFFFFu) + (a2acc >> 16);
-        }
-        uint32_t tot = acc;
-#pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) tot += lane_xor(tot, partner_xor<LPT>(m));
-        const uint32_t cost = tot + (uint32_t)N * (1u + kk);
-        if (cost < bc) { bc = cost; bk = kk; bsum = acc; }
-      }
-      if (!settled) {
-        k = bk;
-        best_c = bc;
-        lane_sum = bsum;
-      }
-    }
-    k_prev = k;
+    uint32_t cb, sbits, k, best_c, lane_sum;
+    bool nonfinite, bytes;
+    encode_tile<LAT, N, DITHER, BF16>(x, pre, emask, sgn, T, t, active, q, c, inv_sqrtn, inv_n, key_dither, a2,
+                                      k_prev, R, cb, sbits, nonfinite, bytes, k, best_c, lane_sum);
     // this lane's unary quotients: sum (q_i + 1) bits; exclusive prefix over the tile's lanes
     const uint32_t lane_unary = lane_sum + (uint32_t)kLaneElems;
     uint32_t lane_excl = 0, span = lane_unary;              // exclusive prefix in logical lane order
@@ -759,6 +786,13 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
         const uint32_t i = (uint32_t)(tid - 64), g = gridDim.x;
         const uint32_t want = 32u * i >= g ? 0u : (32u * (i + 1u) <= g ? 0xFFFFFFFFu : (1u << (g & 31u)) - 1u);
         all_started = wave_all((started_copy[i] & want) == want);
+        if (!all_started) {
+          // the copy was taken at the top of this chunk, with one-chunk groups
+          // a few microseconds after the launch, when some starts may not have
+          // landed yet: read the array again before leaving
+          const uint32_t v = __hip_atomic_load(&started[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          all_started = wave_all((v & want) == want);
+        }
         checked = true;
       }
       if (tid == 64) next_ticket = take_ticket(ws, CG, epoch, all_started);
@@ -821,6 +855,76 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     __syncthreads();
     copy_out();
   }
+}
+
+// --------------------------------------------------------------------------
+// Length pass: the payload size, in words, that the encoder would write at
+// rate constant c (each chunk's tile lengths summed and rounded up to a
+// whole word, over every chunk), with nothing packed, placed or stored.  The
+// closed-loop rate search (Methodology 3) runs it as its trial.  Each
+// workgroup takes chunks blockIdx.x, blockIdx.x + grid, ... and adds its
+// total to *words once at the end; no workgroup waits for another.
+// --------------------------------------------------------------------------
+template <int LAT, int N, bool DITHER, bool BF16>
+__global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems)) __attribute__((amdgpu_waves_per_eu(4)))
+length_kernel(const void* __restrict__ x, uint64_t T, uint64_t C, float c, float inv_sqrtn, float inv_n,
+              uint32_t key_sign, uint32_t key_dither, A2Consts a2, unsigned long long* __restrict__ words) {
+  constexpr int LPT = N / kLaneElems;
+  constexpr int D = LatticeTraits<LAT>::dim;
+  constexpr uint32_t B = LatticeTraits<LAT>::coset * (kLaneElems / D) * LPT;   // coset bits per tile
+  __shared__ uint32_t smask[8];                             // [N / 32] sign diagonal bits
+  __shared__ uint32_t emask[16 * LPT];                      // per-pair sign masks of each lane
+  __shared__ uint32_t tile_len[2][kChunkTiles];             // alternate chunks' tile lengths
+
+  const int tid = threadIdx.x;
+  const int tau = tid / LPT;
+  const int q = tile_lane<LPT>(tid % LPT);
+  const uint32_t sgn = sign_mask<N>(smask, key_sign, tid, q) ^ (lane_sign_odd(q) ? 0xFFFFFFFFu : 0u);
+  if (tid < 16 * LPT) {
+    const int qq = tid >> 4;
+    uint32_t W[2];
+    pair_sign_words(smask[qq] ^ (lane_sign_odd(qq) ? 0xFFFFFFFFu : 0u), W);
+    emask[tid] = pair_sign_mask(W, tid & 15);
+  }
+  __syncthreads();
+
+  // the next chunk's bf16 input is loaded during this one's work; a tile
+  // past the end loads the last tile (its length is not counted)
+  uint4 pre[4];
+  auto prefetch = [&](uint64_t ch) {
+    if (BF16) {
+      uint64_t tt = ch * kChunkTiles + (uint64_t)tau;
+      tt = tt < T ? tt : T - 1;
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + tt * N +
+                                                      (uint64_t)q * kLaneElems);
+#pragma unroll
+      for (int v = 0; v < 4; v++) pre[v] = p[v];
+    }
+  };
+  uint32_t k_prev = 0xFFu;
+  unsigned long long total = 0;                             // (lane 63 of wave 0) this workgroup's words
+  uint32_t buf = 0;
+  uint64_t chunk = blockIdx.x;
+  prefetch(chunk);
+  for (; chunk < C; chunk += gridDim.x) {
+    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const bool active = t < T;
+    uint32_t R[kLaneElems / 2];
+    uint32_t cb, sbits, k, best_c, lane_sum;
+    bool nonfinite, bytes;
+    encode_tile<LAT, N, DITHER, BF16>(x, pre, emask, sgn, T, t, active, q, c, inv_sqrtn, inv_n, key_dither, a2,
+                                      k_prev, R, cb, sbits, nonfinite, bytes, k, best_c, lane_sum);
+    if (chunk + gridDim.x < C) prefetch(chunk + gridDim.x);
+    if (q == 0) tile_len[buf][tau] = active ? B + best_c : 0u;
+    // one barrier a chunk: the buffer written next was last read before it
+    __syncthreads();
+    if (tid < kChunkTiles) {
+      const uint32_t inc = wave_incl_scan(tile_len[buf][tid]);
+      if (tid == kChunkTiles - 1) total += (inc + 31u) >> 5;
+    }
+    buf ^= 1u;
+  }
+  if (tid == kChunkTiles - 1 && total) atomicAdd(words, total);
 }
 
 // --------------------------------------------------------------------------
@@ -1403,6 +1507,19 @@ EncFn enc_table(uint32_t n, bool dither, bool bf16) {
   if (n == 128) return enc_table_n<LAT, 128>(dither, bf16);
   return enc_table_n<LAT, 256>(dither, bf16);
 }
+using LenFn = void (*)(const void*, uint64_t, uint64_t, float, float, float, uint32_t, uint32_t, A2Consts,
+                       unsigned long long*);
+template <int LAT, int N>
+LenFn len_table_n(bool dither, bool bf16) {
+  if (dither) return bf16 ? length_kernel<LAT, N, true, true> : length_kernel<LAT, N, true, false>;
+  return bf16 ? length_kernel<LAT, N, false, true> : length_kernel<LAT, N, false, false>;
+}
+template <int LAT>
+LenFn len_table(uint32_t n, bool dither, bool bf16) {
+  if (n == 64) return len_table_n<LAT, 64>(dither, bf16);
+  if (n == 128) return len_table_n<LAT, 128>(dither, bf16);
+  return len_table_n<LAT, 256>(dither, bf16);
+}
 template <int LAT>
 DecFn dec_codes_table(uint32_t n) {
   if (n == 64) return decode_kernel<LAT, 64, false, true>;
@@ -1420,6 +1537,10 @@ EncFn enc_fn_z(uint32_t n, bool dither, bool bf16);
 EncFn enc_fn_a2(uint32_t n, bool dither, bool bf16);
 EncFn enc_fn_d4(uint32_t n, bool dither, bool bf16);
 EncFn enc_fn_e8(uint32_t n, bool dither, bool bf16);
+LenFn len_fn_z(uint32_t n, bool dither, bool bf16);
+LenFn len_fn_a2(uint32_t n, bool dither, bool bf16);
+LenFn len_fn_d4(uint32_t n, bool dither, bool bf16);
+LenFn len_fn_e8(uint32_t n, bool dither, bool bf16);
 DecFn dec_fn_z(uint32_t n, bool dither);
 DecFn dec_fn_a2(uint32_t n, bool dither);
 DecFn dec_fn_d4(uint32_t n, bool dither);

@@ -141,6 +141,14 @@ EncFn enc_fn(uint32_t lat, uint32_t n, bool dither, bool bf16) {
     default: return enc_fn_e8(n, dither, bf16);
   }
 }
+LenFn len_fn(uint32_t lat, uint32_t n, bool dither, bool bf16) {
+  switch (lat) {
+    case HQ_Z: return len_fn_z(n, dither, bf16);
+    case HQ_A2: return len_fn_a2(n, dither, bf16);
+    case HQ_D4: return len_fn_d4(n, dither, bf16);
+    default: return len_fn_e8(n, dither, bf16);
+  }
+}
 DecFn dec_fn(uint32_t lat, uint32_t n, bool dither) {
   switch (lat) {
     case HQ_Z: return dec_fn_z(n, dither);
@@ -212,16 +220,23 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   }
   // Chunks per group, at most the size that fits: a workgroup runs its
   // groups' chunks one after another, so the last to finish has run about
-  // ceil(groups / grid) groups of `group` chunks.  The size that makes that
-  // shortest, the largest such (fewest look-backs) on a tie: 4096 chunks over
-  // 512 workgroups keep groups of 4, while 5504 over 1024 take groups of 3 (2
-  // rounds of 3 chunks rather than 2 of 4) and 2048 over 1024 groups of 2.
+  // ceil(groups / grid) groups of `group` chunks.  Every group past the
+  // grid's first ones is drawn from one atomic counter, whose draws are
+  // served one at a time: 9984 single-chunk draws (11008 chunks over 1024
+  // workgroups) took milliseconds.  So each round of draws (grid draws) is
+  // charged half a chunk, and the size of least cost, the largest (fewest
+  // look-backs) on a tie, is taken: 4096 chunks over 512 workgroups keep
+  // groups of 4, 5504 over 1024 take groups of 3 (2 rounds of 3 chunks
+  // rather than 2 of 4), 2048 over 1024 groups of 2, and 11008 over 1024
+  // groups of 4 (12 chunks a workgroup, 1728 draws) rather than 1 (11 chunks,
+  // 9984 draws).  The cost below is in units of 1 / (2 grid) chunks.
   const uint32_t gmax = group;
   uint64_t best = UINT64_MAX;
   for (uint32_t g = gmax; g >= 1u; g--) {
     const uint64_t groups = (P.C + g - 1) / g;
     const uint64_t span = (groups + (uint64_t)grid_full - 1) / (uint64_t)grid_full * g;
-    if (span < best) { best = span; group = g; }
+    const uint64_t cost = 2 * span * (uint64_t)grid_full + (groups > (uint64_t)grid_full ? groups - grid_full : 0);
+    if (cost < best) { best = cost; group = g; }
   }
   if (const char* e = getenv("HQ_ENCODE_GROUP_CHUNKS")) {   // (tests: a fixed group size)
     const long v = strtol(e, nullptr, 10);
@@ -252,6 +267,26 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, x, (uint32_t)(dtype == HQ_BF16), P.T, P.C, P.c, inv_sqrtn, inv_n,
                      derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, payload, cap, step, meta,
                      chunk_off, status, (uint32_t*)ws, stage_words, grp_words, group, spin_limit);
+  return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
+}
+
+// the length pass: adds to *words (device) the payload words an encode with
+// plan P would write
+int do_length(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint32_t lat, uint64_t seed,
+              uint32_t kv, unsigned long long* words, void* stream) {
+  if (!x || !words) return HQ_EINVAL;
+  if (((uintptr_t)x & 15) || ((uintptr_t)words & 7)) return HQ_EINVAL;
+  if (P.C == 0) return HQ_OK;
+  LenFn fn = len_fn(lat, tile, kv != 0, dtype == HQ_BF16);
+  const int block = kChunkTiles * (int)(tile / kLaneElems);
+  int grid;
+  int rc = grid_for((const void*)fn, block, 0, P.C, &grid);
+  if (rc) return rc;
+  A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
+  const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
+  const float inv_n = 1.0f / (float)tile;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(block), 0, (hipStream_t)stream, x, P.T, P.C, P.c, inv_sqrtn, inv_n,
+                     derive_key(seed, 0x5349474Eu), derive_key(seed, 0x44495448u), a2, words);
   return hipGetLastError() == hipSuccess ? HQ_OK : HQ_EHIP;
 }
 
@@ -462,6 +497,16 @@ int hq_rate_bracket(uint32_t lattice, float target_bps, float* c_lo, float* c_hi
   return HQ_OK;
 }
 
+int hq_encode_length_c(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
+                       uint32_t lattice, float c, uint64_t seed, uint32_t kv, unsigned long long* words,
+                       void* stream) {
+  Plan P;
+  int rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &P);
+  if (rc) return rc;
+  if (kv && cols != tile) return HQ_EINVAL;
+  return do_length(P, x, dtype, tile, lattice, seed, kv, words, stream);
+}
+
 int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, uint32_t tile,
                    uint32_t lattice, float target_bps, uint64_t seed, uint32_t kv, uint32_t* payload,
                    uint64_t payload_cap_words, uint16_t* step, uint16_t* meta, uint32_t* chunk_off,
@@ -475,7 +520,12 @@ int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, 
   Plan P;
   rc = plan_for_c(dtype, rows, cols, tile, lattice, lo, kv, &P);
   if (rc) return rc;
+  if (!x || !payload || !step || !meta || !chunk_off || !status || !workspace) return HQ_EINVAL;
   if (payload_cap_words < P.cap_words || workspace_bytes < P.ws_bytes) return HQ_ENOSPC;
+  if (((uintptr_t)x & 15) || ((uintptr_t)workspace & 7)) return HQ_EINVAL;
+  // each trial is a length pass counting into the workspace's length word
+  // (no encoder reads it); the stream is encoded once, at the chosen constant
+  unsigned long long* count = reinterpret_cast<unsigned long long*>(static_cast<uint32_t*>(workspace) + kLengthWord);
   const double numel = (double)rows * (double)cols;
   float c = lo;
   double r = 0.0;
@@ -485,11 +535,11 @@ int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, 
     Plan Q;
     rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &Q);
     if (rc) return rc;
-    rc = do_encode(Q, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off,
-                   status, workspace, workspace_bytes, stream);
+    if (hipMemsetAsync(count, 0, sizeof(*count), (hipStream_t)stream) != hipSuccess) return HQ_EHIP;
+    rc = do_length(Q, x, dtype, tile, lattice, seed, kv, count, stream);
     if (rc) return rc;
-    uint32_t words = 0;
-    if (hipMemcpyAsync(&words, chunk_off + P.C, 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+    unsigned long long words = 0;
+    if (hipMemcpyAsync(&words, count, sizeof(words), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
         hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
       return HQ_EHIP;
     it++;
@@ -498,6 +548,12 @@ int hq_encode_rate(const void* x, uint32_t dtype, uint64_t rows, uint64_t cols, 
     if (r > (double)target_bps) lo = c;              // too many bits: a larger step
     else hi = c;
   }
+  Plan Q;
+  rc = plan_for_c(dtype, rows, cols, tile, lattice, c, kv, &Q);
+  if (rc) return rc;
+  rc = do_encode(Q, x, dtype, tile, lattice, seed, kv, payload, payload_cap_words, step, meta, chunk_off, status,
+                 workspace, workspace_bytes, stream);
+  if (rc) return rc;
   if (c_out) *c_out = c;
   if (bps_out) *bps_out = r;
   if (encodes_out) *encodes_out = it;

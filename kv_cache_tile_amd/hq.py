@@ -23,7 +23,8 @@ FLAG_NONFINITE, FLAG_CORRUPT, FLAG_NOSPACE, FLAG_RANGE, FLAG_STALL = 1, 2, 4, 8,
 CHUNK_TILES = 64
 
 EXPORTS = ("hq_plan", "hq_encode", "hq_decode", "hq_kv_encode", "hq_kv_decode", "hq_strerror",
-           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate", "hq_rotate", "hq_decode_codes", "hq_act_quant",
+           "hq_version", "hq_plan_c", "hq_encode_c", "hq_decode_c", "hq_rate_bracket", "hq_encode_rate",
+           "hq_encode_length_c", "hq_rotate", "hq_decode_codes", "hq_act_quant",
            "hq_act_quant_blocked", "hq_codes_matmul", "hq_nearest", "hq_encode_c_noalloc", "hq_codes_matmul_fused")
 
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
                                      P(f32), P(ctypes.c_double), P(u32), vp]
         L.hq_encode_rate.restype = ctypes.c_int
+        L.hq_encode_length_c.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, vp]
+        L.hq_encode_length_c.restype = ctypes.c_int
         L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
         L.hq_rotate.restype = ctypes.c_int
         L.hq_decode_codes.argtypes = [vp, u64, vp, vp, vp, u64, u64, u32, u32, f32, u64, vp, vp, vp]
@@ -324,11 +327,25 @@ def encode_c_noalloc(x: torch.Tensor, tile: int, lattice: str, c: float, seed: i
     return out
 
 
+def encode_length_c(x: torch.Tensor, tile: int, lattice: str, c: float, seed: int = 0, kv: bool = False,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """The length pass: the payload word count (chunk_off[C]) that encode_c
+    with these arguments would produce, as a device int64 tensor of one
+    element, without writing a stream.  With `out` (a zeroed device int64
+    scalar), the count is added to it."""
+    x2, rows, cols = _rows_cols(x, tile, kv)
+    words = torch.zeros((), dtype=torch.int64, device=x.device) if out is None else out
+    _check(lib().hq_encode_length_c(x2.data_ptr(), _dtype_code(x2.dtype), rows, cols, tile, LATTICES[lattice],
+                                    float(c), seed, int(kv), words.data_ptr(), _stream(x.device)))
+    return words
+
+
 def encode_rate(x: torch.Tensor, tile: int, lattice: str, target_bps: float, seed: int = 0,
                 kv: bool = False) -> HQTensor:
-    """Closed-loop rate: the library bisects on c until the stored stream is
-    within 0.01 bits per scalar of target_bps (synchronous).  The result
-    records c, the rate reached and the number of encodes in `extra`."""
+    """Closed-loop rate: the library bisects on c, each trial a length pass,
+    until the stream would be within 0.01 bits per scalar of target_bps, and
+    then encodes it once (synchronous).  The result records c, the rate
+    reached and the number of trials (`encodes`) in `extra`."""
     x2, rows, cols = _rows_cols(x, tile, kv)
     dt = _dtype_code(x2.dtype)
     lo, _ = rate_bracket(lattice, target_bps)

@@ -36,6 +36,7 @@ def lib():
     L.hq_rate_bracket.argtypes = [u32, f32, P(f32), P(f32)]
     L.hq_encode_rate.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, u64, vp, vp, vp, vp, vp, u64,
                                  P(f32), P(ctypes.c_double), P(u32), vp]
+    L.hq_encode_length_c.argtypes = [vp, u32, u64, u64, u32, u32, f32, u64, u32, vp, vp]
     L.hq_rotate.argtypes = [vp, u32, u32, vp, u32, u64, vp, u32, vp]
     L.hq_act_quant.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
     L.hq_act_quant_blocked.argtypes = [vp, u32, u64, u64, u32, u64, vp, vp, vp]
@@ -166,16 +167,28 @@ def test_rate_calls_reject_before_device_work(lib):
     c_out, r_out, n_out = ctypes.c_float(), ctypes.c_double(), ctypes.c_uint32()
 
     def rate(**kw):
-        a = dict(x=A, pay=A, cap=cap, ws=ws, R=4.0, kv=0, cols=1024, tile=128)
+        a = dict(x=A, pay=A, cap=cap, wsp=A, ws=ws, R=4.0, kv=0, cols=1024, tile=128)
         a.update(kw)
         return lib.hq_encode_rate(a["x"], BF16, 64, a["cols"], a["tile"], E8, a["R"], 1, a["kv"], a["pay"],
-                                  a["cap"], A, A, A, A, A, a["ws"], ctypes.byref(c_out), ctypes.byref(r_out),
+                                  a["cap"], A, A, A, A, a["wsp"], a["ws"], ctypes.byref(c_out), ctypes.byref(r_out),
                                   ctypes.byref(n_out), None)
 
     assert rate(cap=cap - 1) == ENOSPC and rate(ws=ws - 8) == ENOSPC   # sized at the bracket's low end
     assert rate(R=0.5) == EINVAL and rate(R=9.0) == EINVAL
     assert rate(kv=1) == EINVAL                                        # KV needs cols == tile
-    assert rate(x=None) == EINVAL and rate(pay=None) == EINVAL          # the first trial's checks
+    assert rate(x=None) == EINVAL and rate(pay=None) == EINVAL and rate(wsp=None) == EINVAL
+    assert rate(x=A + 8) == EINVAL and rate(wsp=A + 4) == EINVAL       # 16- and 8-byte alignment
+
+    def length(**kw):
+        a = dict(x=A, words=A, c=0.3, kv=0, cols=1024, tile=128)
+        a.update(kw)
+        return lib.hq_encode_length_c(a["x"], BF16, 64, a["cols"], a["tile"], E8, a["c"], 1, a["kv"], a["words"],
+                                      None)
+
+    assert length(x=None) == EINVAL and length(words=None) == EINVAL
+    assert length(x=A + 8) == EINVAL and length(words=A + 4) == EINVAL
+    assert length(c=0.0) == EINVAL and length(c=float("inf")) == EINVAL
+    assert length(kv=1) == EINVAL and length(cols=1000) == EINVAL and length(tile=96) == EINVAL
     assert lib.hq_encode_c(A, BF16, 64, 1024, 128, E8, 0.0, 1, 0, A, cap, A, A, A, A, A, ws, None) == EINVAL
     assert lib.hq_encode_c(None, BF16, 64, 1024, 128, E8, 0.3, 1, 0, A, cap, A, A, A, A, A, ws, None) == EINVAL
     assert lib.hq_decode_c(A, 100, A, A, A, BF16, 64, 1024, 128, E8, -1.0, 1, 0, A, A, None) == EINVAL

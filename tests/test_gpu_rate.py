@@ -124,3 +124,60 @@ def test_rate_search_degenerate_inputs(kind):
         assert r < 1.2 and n > 5           # 144 bits per 128-scalar tile, far below the target
     else:
         assert h.flags() == hq.FLAG_NONFINITE and e.status == oracle.ENONFINITE
+
+
+# The length pass (hq_encode_length_c): the payload word count the encoder
+# would write, chunk_off[C], without writing a stream.  Ragged last chunks
+# (130 x 768 scalars: 390 tiles at n = 256, 6 in the last chunk), every
+# lattice, both dtypes, KV, off-table constants, and degenerate tiles.
+LENGTH_CASES = [("E8", 256, False, "bf16", 4.0), ("E8", 128, True, "bf16", 2.0), ("D4", 64, False, "f32", 3.0),
+                ("A2", 128, False, "bf16", 5.0), ("Z", 128, False, "bf16", 4.0), ("E8", 64, False, "f32", 6.0),
+                ("A2", 64, True, "f32", 2.5)]
+
+
+@pytest.mark.parametrize("f", [0.37, 1.0, 2.9])
+@pytest.mark.parametrize("lat,tile,kv,dtype,R", LENGTH_CASES)
+def test_length_pass_counts_the_encoders_words(lat, tile, kv, dtype, R, f):
+    xd, xo = _inputs("student", tile, kv, dtype, rows=130, cols=768)
+    c = float(np.float32(rate_c(lat, tile, R, int(kv)) * f))
+    print(f"[case] length pass {lat} n={tile} kv={kv} {dtype} c={c}", flush=True)
+    words = hq.encode_length_c(xd, tile, lat, c, seed=13, kv=kv)
+    h = hq.encode_c(xd, tile, lat, c, seed=13, kv=kv)
+    e = oracle.encode(xo, tile, lat, c, 13, int(kv))
+    torch.cuda.synchronize()
+    assert int(words.item()) == int(e.chunk_off[-1]) == h.payload_words()
+    # a second pass adds to the same counter
+    hq.encode_length_c(xd, tile, lat, c, seed=13, kv=kv, out=words)
+    assert int(words.item()) == 2 * int(e.chunk_off[-1])
+
+
+@pytest.mark.parametrize("kind", ["zeros", "nan_inf", "tiny_huge"])
+def test_length_pass_degenerate_tiles(kind):
+    x = workloads.gaussian(192, 1024, key=4)
+    if kind == "zeros":
+        x[:] = 0.0
+    elif kind == "nan_inf":
+        x[3, 10], x[77, 500], x[150, 0] = np.nan, np.inf, -np.inf     # non-finite tiles count as zero tiles
+    else:
+        x[:64] *= 1e-38
+        x[64:128] *= 1e37
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    xo = workloads.bf16_bits(t)
+    c = rate_c("E8", 128, 4.0, 0)
+    print(f"[case] length pass degenerate {kind}", flush=True)
+    words = hq.encode_length_c(t.to(_dev()), 128, "E8", c, seed=2)
+    e = oracle.encode(xo, 128, "E8", c, 2, 0)
+    torch.cuda.synchronize()
+    assert int(words.item()) == int(e.chunk_off[-1])
+
+
+def test_length_pass_dit_layer():
+    # one 4096 x 16384 bf16 layer at n = 256 (4096 chunks, several a
+    # workgroup): the length pass against the encoder's own chunk_off[C]
+    x = workloads.dit_layer_device(4096, 16384, 0, _dev())
+    c = rate_c("E8", 256, 4.0, 0)
+    print("[case] length pass 4096x16384 E8 n=256", flush=True)
+    words = hq.encode_length_c(x, 256, "E8", c, seed=5)
+    h = hq.encode_c(x, 256, "E8", c, seed=5)
+    torch.cuda.synchronize()
+    assert int(words.item()) == h.payload_words()
