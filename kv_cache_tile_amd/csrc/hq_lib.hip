@@ -310,8 +310,21 @@ int do_decode(const Plan& P, const uint32_t* payload, uint64_t payload_words, co
   // metadata slots (meta, step), the lanes' unary starts, the sign words
   const size_t lds = (size_t)(2 * stage_words + 3 * 3 * kChunkTiles + 12 + 2 * 2 * kChunkTiles + tpw * lpt + 8) * 4;
   int grid;
-  rc = grid_for((const void*)fn, block, lds, P.C * (kChunkTiles / tpw), &grid);
+  const uint64_t units = P.C * (kChunkTiles / tpw);
+  rc = grid_for((const void*)fn, block, lds, units, &grid);
   if (rc) return rc;
+  // between one and two resident grids of units: two units a workgroup (the
+  // second one's words stream in during the first) instead of a second round
+  // of units for some workgroups (4096 x 4096 bf16 at n = 128: 2048 units,
+  // 23.3 -> 22.1 us); more rounds keep the full grid (balancing them with a
+  // smaller one measured slower)
+  if (units > (uint64_t)grid && units <= 2 * (uint64_t)grid) grid = (int)((units + 1) / 2);
+  // a grid of a given size, up to the unit count, on request (for timing
+  // sweeps: units are grid-strided, so any grid decodes the same stream)
+  if (const char* e = getenv("HQ_DECODE_GRID")) {
+    const unsigned long long v = strtoull(e, nullptr, 10);
+    if (v > 0) grid = (int)(v < units ? v : units);
+  }
   A2Consts a2{(float)sqrt(3.0), (float)(1.0 / sqrt(3.0))};
   const float inv_sqrtn = (float)(1.0 / sqrt((double)tile));
   hipLaunchKernelGGL(fn, dim3(grid), dim3(block), lds, (hipStream_t)stream, payload, payload_words, step, meta,
