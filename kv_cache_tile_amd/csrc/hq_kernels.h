@@ -511,15 +511,17 @@ __device__ __forceinline__ void encode_tile(const void* __restrict__ x, const ui
 // --------------------------------------------------------------------------
 // Encode kernel
 // --------------------------------------------------------------------------
-// Occupancy: at n = 256 three 512-thread workgroups a CU (6 waves per SIMD,
-// at most 80 VGPRs): the chunk's input is then loaded at the top of its own
-// iteration (the other workgroups hide the latency) rather than prefetched
-// into 16 registers during the previous chunk; measured 2-4% fewer cycles
-// than two workgroups with the prefetch.  Smaller tiles, the dithered
-// encode and A2 (whose extra registers would spill at 80) keep 4 waves and
-// the prefetch.
+// Occupancy: the E8 encode at n = 128 and 256 runs 6 waves per SIMD (three
+// 512-thread or six 256-thread workgroups a CU, at most 80 VGPRs): the
+// chunk's input is then loaded at the top of its own iteration (the other
+// workgroups hide the latency) rather than prefetched into 16 registers
+// during the previous chunk.  Measured on one box, bit-identical streams:
+// 3.5% fewer cycles for a 4096 x 16384 layer at n = 256, 6.5% less time for
+// 11008 x 4096 at n = 128.  Z and D4 at n = 128 measured no faster (D4 4%
+// slower), A2 would spill at 80 VGPRs, and the dither adds registers: they,
+// and n = 64, keep 4 waves and the prefetch.
 template <int LAT, int N, bool DITHER>
-constexpr bool kEncodePrefetch = !(N == 256 && !DITHER && LAT != 2);
+constexpr bool kEncodePrefetch = !(LAT == 8 && N >= 128 && !DITHER);
 
 template <int LAT, int N, bool DITHER, bool BF16>
 __global__ void __launch_bounds__(kChunkTiles * (N / kLaneElems)) __attribute__((amdgpu_waves_per_eu(kEncodePrefetch<LAT, N, DITHER> ? 4 : 6)))
