@@ -682,10 +682,14 @@ __device__ __forceinline__ uint32_t zero_sign_butterfly(uint32_t z, int q) {
     const uint32_t lo = z & lo_mask[st], hi = (z >> h) & lo_mask[st];
     z = (lo & hi) | ((lo & ~hi) << h);
   }
+  // (q through an opaque copy: its bit masks are formed on this rare path,
+  // not hoisted into registers held across the caller's loop)
+  uint32_t qo = (uint32_t)q;
+  opaque(qo);
 #pragma unroll
   for (int m = 1; m < LPT; m <<= 1) {
     const uint32_t p = lane_xor(z, partner_xor<LPT>(m));
-    z = (q & m) ? (p & ~z) : (z & p);
+    z = (qo & (uint32_t)m) ? (p & ~z) : (z & p);
   }
   return z;
 }
