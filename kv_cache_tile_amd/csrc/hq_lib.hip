@@ -225,17 +225,27 @@ int do_encode(const Plan& P, const void* x, uint32_t dtype, uint32_t tile, uint3
   // served one at a time: 9984 single-chunk draws (11008 chunks over 1024
   // workgroups) took milliseconds.  So each round of draws (grid draws) is
   // charged half a chunk, and the size of least cost, the largest (fewest
-  // look-backs) on a tie, is taken: 4096 chunks over 512 workgroups keep
-  // groups of 4, 5504 over 1024 take groups of 3 (2 rounds of 3 chunks
+  // look-backs) on a tie, is taken: 4096 chunks over 512 workgroups (4 waves a
+  // SIMD) keep groups of 4, 5504 over 1024 take groups of 3 (2 rounds of 3 chunks
   // rather than 2 of 4), 2048 over 1024 groups of 2, and 11008 over 1024
   // groups of 4 (12 chunks a workgroup, 1728 draws) rather than 1 (11 chunks,
   // 9984 draws).  The cost below is in units of 1 / (2 grid) chunks.
+  // A workgroup that runs more than one group places each finished group
+  // while packing the next into the other area; where the two areas overlap
+  // so far that a group's words (taken as 7/8 of its worst case) would reach
+  // the other area, the placement is forced early and its look-back waits
+  // on the critical path, so such sizes are passed over.  The DiT layer at 6
+  // waves a SIMD (4096 chunks over 768 workgroups, 13100 staging words)
+  // takes groups of 2 instead of 3: 82.1 against 84.2 us, interleaved runs.
   const uint32_t gmax = group;
   uint64_t best = UINT64_MAX;
   for (uint32_t g = gmax; g >= 1u; g--) {
     const uint64_t groups = (P.C + g - 1) / g;
     const uint64_t span = (groups + (uint64_t)grid_full - 1) / (uint64_t)grid_full * g;
     const uint64_t cost = 2 * span * (uint64_t)grid_full + (groups > (uint64_t)grid_full ? groups - grid_full : 0);
+    const uint64_t gw_g = ((uint64_t)g * P.chunk_words + 4 + 3) & ~3ull;
+    const bool overlaps = 2 * gw_g * 7 > 8 * (uint64_t)stage_words;
+    if (g > 1u && groups > (uint64_t)grid_full && overlaps) continue;
     if (cost < best) { best = cost; group = g; }
   }
   if (const char* e = getenv("HQ_ENCODE_GROUP_CHUNKS")) {   // (tests: a fixed group size)
