@@ -556,7 +556,10 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   uint64_t* look = reinterpret_cast<uint64_t*>(ws + kLookBase);   // one word per group
 
   // Tickets number groups of group_chunks consecutive chunks (take_ticket).
-  const uint64_t CG = (C + group_chunks - 1) / group_chunks;
+  // Chunk and group numbers are 32-bit (the plan admits fewer than 2^32
+  // scalars, so fewer than 2^20 chunks): scalar registers are scarce here.
+  const uint32_t C32 = (uint32_t)C;
+  const uint32_t CG = (C32 + group_chunks - 1) / group_chunks;
   if (tid == 0)
     misc[2] = __hip_atomic_load(&ws[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kEpochMask;
 
@@ -581,8 +584,8 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   const uint32_t started_copy_lds = __builtin_amdgcn_readfirstlane(lds_addr(started_copy));
   for (uint32_t i = tid; i < stage_words; i += blockDim.x) stage[i] = 0u;
   __syncthreads();
-  uint64_t grp = blockIdx.x;
-  uint64_t chunk = grp * group_chunks;
+  uint32_t grp = blockIdx.x;
+  uint32_t chunk = grp * group_chunks;
   uint32_t gi = 0, gw = 0;                                  // chunk of the group, group words staged so far
   bool gfits = true;
 
@@ -623,7 +626,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
   const uint32_t base1 = stage_words - grp_words;          // the second area's first word
   uint32_t h = 0;                                           // the current group's area
   bool pend = false, pgfits = true;
-  uint64_t pgrp = 0, pchunk = 0;
+  uint32_t pgrp = 0, pchunk = 0;
   uint32_t pgtotal = 0, pgi = 0, ph = 0;
 
   // wave 0: decoupled look-back over groups.  A round loads kLookJ
@@ -691,9 +694,9 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
                            __HIP_MEMORY_SCOPE_AGENT);
       }
       misc[3] = excl;
-      const uint64_t c0 = pgrp * group_chunks;
+      const uint32_t c0 = pgrp * group_chunks;
       for (uint32_t i = 0; i <= pgi; i++) chunk_off[c0 + i] = excl + goff[ph * kMaxGroupChunks + i];
-      if (pchunk == C - 1) chunk_off[C] = excl + pgtotal;
+      if (pchunk == C32 - 1) chunk_off[C32] = excl + pgtotal;
       if (!pgfits || (uint64_t)excl + pgtotal > cap_words) atomicOr(status, HQ_FLAG_NOSPACE);
       if (stalled) atomicOr(status, HQ_FLAG_STALL);
     }
@@ -734,7 +737,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
     if (grp >= CG) break;
     const uint32_t quarters = 4u * done++ / share;
     wave_priority(quarters >= 3u ? 0u : 3u - quarters);
-    const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C);
+    const bool last = (gi + 1 == group_chunks) || (chunk + 1 >= C32);
     if (pend && last && tid < 64) place();
     // before the first draw: wave 1 loads the started array into LDS now
     // (no register held through the compute), to read it after this chunk's
@@ -745,7 +748,7 @@ encode_kernel(const void* __restrict__ x, uint32_t /* input is bf16: BF16 */, ui
       lds_load_u32_coherent(started, so, started_copy_lds);
     }
 
-    const uint64_t t = chunk * kChunkTiles + (uint64_t)tau;
+    const uint64_t t = (uint64_t)chunk * kChunkTiles + (uint64_t)tau;
     const bool active = t < T;
     if (!kEncodePrefetch<LAT, N, DITHER>) prefetch(chunk);
 
